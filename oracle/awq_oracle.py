@@ -1,0 +1,270 @@
+"""CPU oracle for the W4A16 group-wise AWQ linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
+module: only the test-suite, the smoke check in ``__graft_entry__`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, table or
+constant with the HIP library and imports nothing from it.
+
+What it computes, and where that comes from
+-------------------------------------------
+Sources (web pages, cited by title and section):
+
+* [P5] "AI-Research-SKILLs AWQ 高级使用指南" (lshu.cn): section "算法原理"
+  (the reconstruction objective L(s)), section "分组大小与零点量化" with its
+  two sub-parts "分组大小 Group Size" (weights share one scale/zero per group;
+  sizes 32/128/256, 128 the default) and "零点量化 Zero-Point" (a zero point
+  is an offset for asymmetric weight ranges; ``zero_point: False`` is the
+  symmetric case), section "WQLinear 内核全景" (GEMM for batches, GEMV for a
+  single token).
+* [P2] "Optimization Awq" (skillsdirectory.com): section "Quantizar seu
+  próprio modelo" (``quant_config`` = zero_point, q_group_size, w_bit=4,
+  version) and section "Integração vLLM" (activations in half precision).
+* [P4] "AWQ Activation-aware Weight Quantization (Lin 2023年)" (jisaku.com),
+  section "主な特徴・仕組み": 4-bit weight-only, group-wise quantization.
+
+The pages give neither a formula for the quantizer nor a storage layout.  The
+readings taken here (every one is listed with its reason in the design notes
+of the repository):
+
+1. Groups are ``g`` consecutive input channels (K) of one output row of the
+   ``nn.Linear`` weight W[N, K]; Y = X . W'^T.
+2. zero_point=True (asymmetric, min-max):
+   r = max(mx - mn, 1e-5); s = f16(r / 15); z = clamp(rne(-mn / s), 0, 15).
+3. zero_point=False (symmetric):
+   a = max(max|w|, 1e-5); s = f16(a / 7); z = 8 (implicit, not stored).
+4. q = clamp(rne(w / s) + z, 0, 15); decoded weight w' = (q - z) * s.
+   All of 2-4 is IEEE binary32 arithmetic with round-half-to-even, the scale
+   rounded to binary16 before z and q are formed, every division a correctly
+   rounded fp32 division.
+5. Storage (our layout):
+   qweight u32 [N][K/8]: bits 4i..4i+3 of word (n, j) hold the code of
+   k = 8j + PACK_ORDER[i]; scales fp16 [K/g][N]; qzeros u32 [K/g][N/8], bits
+   4i..4i+3 of word (j, c) hold the zero of row 8c + i.
+6. Y_ref = X . W'^T and D = |X| . |W'|^T in fp64.  Products of an fp16 x and
+   an exact w' need at most 27 significant bits, so each product is exact in
+   fp64; only the summation rounds.
+7. L(s) = || (X diag(s)^-1) . Dq(f16(W diag(s)))^T - X . W^T ||_F in fp64.
+
+Parity pins: every function here is pinned by tests that do not re-type its
+formula (hand-worked examples, brute force over every fp16 value of a range,
+closed forms and invariants); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F32 = np.float32
+
+# Nibble slot i of a packed weight word holds the code of k = 8j + PACK_ORDER[i].
+# With this order the low halfword of a word holds k = 0,2,4,6 and the high
+# halfword k = 1,3,5,7 of its 8-channel block (storage reading 5 above).
+PACK_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
+
+SCALE_FLOOR = F32(1e-5)
+QMAX = 15
+
+
+def _check_shape(W16: np.ndarray, g: int) -> tuple[int, int, int]:
+    if W16.dtype != np.float16 or W16.ndim != 2:
+        raise TypeError("W must be a 2-D float16 array [N, K]")
+    N, K = W16.shape
+    if g <= 0 or K % g:
+        raise ValueError(f"group size {g} must divide K={K}")
+    return N, K, K // g
+
+
+def group_params(W16: np.ndarray, g: int, zero_point: bool):
+    """Per-(row, group) scale and zero point (readings 1-3).
+
+    [P5] "分组大小 Group Size": all weights of a group share one scale and one
+    zero point.  [P5] "零点量化 Zero-Point": with a zero point the grid is
+    shifted to cover an asymmetric range; without one it is symmetric.
+
+    Returns ``(s16, z)``: ``s16`` float16 [N, G], ``z`` int64 [N, G].
+    """
+    N, K, G = _check_shape(W16, g)
+    a = W16.astype(F32).reshape(N, G, g)  # fp16 -> fp32 is exact
+    if zero_point:
+        mn = a.min(axis=2)
+        mx = a.max(axis=2)
+        r = (mx - mn).astype(F32)
+        r = np.where(r < SCALE_FLOOR, SCALE_FLOOR, r).astype(F32)
+        s16 = (r / F32(QMAX)).astype(F32).astype(np.float16)
+        s = s16.astype(F32)
+        zf = np.rint((-mn).astype(F32) / s).astype(F32)
+        z = np.clip(zf, F32(0), F32(QMAX)).astype(np.int64)
+    else:
+        amax = np.abs(a).max(axis=2).astype(F32)
+        amax = np.where(amax < SCALE_FLOOR, SCALE_FLOOR, amax).astype(F32)
+        s16 = (amax / F32(7)).astype(F32).astype(np.float16)
+        z = np.full((N, G), 8, dtype=np.int64)
+    return s16, z
+
+
+def codes(W16: np.ndarray, s16: np.ndarray, z: np.ndarray, g: int) -> np.ndarray:
+    """q = clamp(rne(w / s) + z, 0, 15), one code per weight (reading 4).
+
+    The division is a correctly rounded fp32 division and the sum is formed in
+    fp32, exactly as written; the clamp keeps every code a 4-bit value.
+    """
+    N, K, G = _check_shape(W16, g)
+    a = W16.astype(F32).reshape(N, G, g)
+    s = s16.astype(F32)[:, :, None]
+    v = (np.rint((a / s).astype(F32)) + z.astype(F32)[:, :, None]).astype(F32)
+    q = np.clip(v, F32(0), F32(QMAX)).astype(np.uint8)
+    return q.reshape(N, K)
+
+
+def quantize(W16: np.ndarray, g: int, zero_point: bool):
+    """Group-wise 4-bit quantization Q: returns ``(q uint8 [N,K], s16 [N,G], z [N,G])``."""
+    s16, z = group_params(W16, g, zero_point)
+    return codes(W16, s16, z, g), s16, z
+
+
+def dequant(q: np.ndarray, s16: np.ndarray, z: np.ndarray, g: int) -> np.ndarray:
+    """Decoded weight w' = (q - z) * s in fp64 (exact: a 5-bit by 11-bit product)."""
+    N, K = q.shape
+    G = K // g
+    d = q.astype(np.float64).reshape(N, G, g) - z.astype(np.float64)[:, :, None]
+    return (d * s16.astype(np.float64)[:, :, None]).reshape(N, K)
+
+
+def fake_quant(W16: np.ndarray, g: int, zero_point: bool) -> np.ndarray:
+    """Dq(Q(W)): quantize then decode, fp64 [N, K]."""
+    q, s16, z = quantize(W16, g, zero_point)
+    return dequant(q, s16, z, g)
+
+
+# ---------------------------------------------------------------------------
+# Storage layout (reading 5).  Written with explicit per-slot index formulas.
+# ---------------------------------------------------------------------------
+
+def pack_qweight(q: np.ndarray) -> np.ndarray:
+    """qweight u32 [N][K/8]; nibble slot i of word (n, j) = q[n, 8j + PACK_ORDER[i]]."""
+    N, K = q.shape
+    if K % 8:
+        raise ValueError("K must be a multiple of 8")
+    words = np.zeros((N, K // 8), dtype=np.uint32)
+    for i, kk in enumerate(PACK_ORDER):
+        words |= q[:, kk::8].astype(np.uint32) << np.uint32(4 * i)
+    return words
+
+
+def unpack_qweight(qweight: np.ndarray, K: int) -> np.ndarray:
+    N = qweight.shape[0]
+    q = np.zeros((N, K), dtype=np.uint8)
+    for i, kk in enumerate(PACK_ORDER):
+        q[:, kk::8] = ((qweight >> np.uint32(4 * i)) & np.uint32(0xF)).astype(np.uint8)
+    return q
+
+
+def pack_scales(s16: np.ndarray) -> np.ndarray:
+    """scales as raw fp16 bits, group-major: uint16 [G][N] (element (j, n) = s of row n, group j)."""
+    return np.ascontiguousarray(s16.T).view(np.uint16)
+
+
+def unpack_scales(scales_u16: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(scales_u16.view(np.float16).T)
+
+
+def pack_qzeros(z: np.ndarray) -> np.ndarray:
+    """qzeros u32 [G][N/8]; nibble slot i of word (j, c) = z[8c + i, j] (natural order)."""
+    N, G = z.shape
+    if N % 8:
+        raise ValueError("N must be a multiple of 8")
+    zt = z.T.astype(np.uint32)  # [G, N]
+    words = np.zeros((G, N // 8), dtype=np.uint32)
+    for i in range(8):
+        words |= zt[:, i::8] << np.uint32(4 * i)
+    return words
+
+
+def unpack_qzeros(qzeros: np.ndarray, N: int) -> np.ndarray:
+    G = qzeros.shape[0]
+    zt = np.zeros((G, N), dtype=np.int64)
+    for i in range(8):
+        zt[:, i::8] = ((qzeros >> np.uint32(4 * i)) & np.uint32(0xF)).astype(np.int64)
+    return np.ascontiguousarray(zt.T)
+
+
+def pack(W16: np.ndarray, g: int, zero_point: bool):
+    """Quantize and store: ``(qweight u32 [N,K/8], scales u16 [G,N], qzeros u32 [G,N/8] | None)``."""
+    q, s16, z = quantize(W16, g, zero_point)
+    qz = pack_qzeros(z) if zero_point else None
+    return pack_qweight(q), pack_scales(s16), qz
+
+
+def unpack(qweight, scales_u16, qzeros, N: int, K: int, g: int, zero_point: bool):
+    """Inverse of :func:`pack`: ``(q, s16, z)``; the symmetric zero is the implicit 8."""
+    G = K // g
+    q = unpack_qweight(qweight, K)
+    s16 = unpack_scales(scales_u16)
+    if zero_point:
+        z = unpack_qzeros(qzeros, N)
+    else:
+        z = np.full((N, G), 8, dtype=np.int64)
+    return q, s16, z
+
+
+def dequant_packed(qweight, scales_u16, qzeros, N: int, K: int, g: int, zero_point: bool):
+    q, s16, z = unpack(qweight, scales_u16, qzeros, N, K, g, zero_point)
+    return dequant(q, s16, z, g)
+
+
+# ---------------------------------------------------------------------------
+# The linear layer and the acceptance test.
+# ---------------------------------------------------------------------------
+
+def matmul_ref(X16: np.ndarray, Wdq: np.ndarray):
+    """Y_ref = X . W'^T and D = |X| . |W'|^T, both fp64 [M, N] (reading 6).
+
+    [P5] "WQLinear 内核全景": the quantized layer is an ordinary linear map on
+    the decoded weights; GEMM and GEMV differ only in how they are computed.
+    """
+    X = X16.astype(np.float64)
+    W = np.asarray(Wdq, dtype=np.float64)
+    return X @ W.T, np.abs(X) @ np.abs(W).T
+
+
+def matmul_ref_fsum(X16: np.ndarray, Wdq: np.ndarray) -> np.ndarray:
+    """The same Y with every dot product summed by ``math.fsum`` (small inputs only)."""
+    X = X16.astype(np.float64)
+    W = np.asarray(Wdq, dtype=np.float64)
+    M, N = X.shape[0], W.shape[0]
+    Y = np.empty((M, N))
+    for m in range(M):
+        for n in range(N):
+            Y[m, n] = math.fsum((X[m] * W[n]).tolist())
+    return Y
+
+
+def tolerance_ratio(Y_dev: np.ndarray, Y_ref: np.ndarray, D: np.ndarray) -> np.ndarray:
+    """|Y_dev - Y_ref| / D per element; 0 where both the error and D are 0, inf
+    where D = 0 but the error is not."""
+    err = np.abs(np.asarray(Y_dev, dtype=np.float64) - Y_ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(D > 0, err / np.where(D > 0, D, 1.0), np.where(err > 0, np.inf, 0.0))
+    return r
+
+
+def recon_loss(W16: np.ndarray, X: np.ndarray, s: np.ndarray, g: int, zero_point: bool) -> float:
+    """L(s) = ||Q(W*s)(s^-1*X) - W*X|| (reading 7).
+
+    [P5] "算法原理": the per-input-channel scale s multiplies the weight before
+    quantization and its inverse multiplies the activation; AWQ picks s to make
+    this reconstruction error small.  ``s`` is a positive fp32 vector of length
+    K; ``W*s`` is formed in fp32 and rounded to fp16 (Q takes fp16 weights);
+    ``s^-1 * X`` and the norm are fp64.
+    """
+    N, K, _ = _check_shape(W16, g)
+    s = np.asarray(s, dtype=F32)
+    if s.shape != (K,) or not np.all(s > 0):
+        raise ValueError("s must be a positive vector of length K")
+    Ws16 = (W16.astype(F32) * s[None, :]).astype(F32).astype(np.float16)
+    Wq = fake_quant(Ws16, g, zero_point)
+    Xs = np.asarray(X, dtype=np.float64) / s.astype(np.float64)[None, :]
+    ref = np.asarray(X, dtype=np.float64) @ W16.astype(np.float64).T
+    return float(np.linalg.norm(Xs @ Wq.T - ref))
+
