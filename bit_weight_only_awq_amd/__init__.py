@@ -1,0 +1,200 @@
+"""MI355X-native W4A16 group-wise quantized linear layer (AWQ's WQLinear hot path).
+
+A thin binding of the C ABI in ``include/awq.h`` (``libawq_mi355x.so``, built
+by ``python -m bit_weight_only_awq_amd.build``).  PyTorch supplies device
+memory and the current stream only; every step of the layer runs in the
+library's HIP kernels.  There is no fallback: if the library is missing or
+the tensors are not on the GPU, the calls raise.
+
+Entry points (same names and arguments as the C ABI):
+
+* ``awq_pack(w, group_size, zero_point)`` -> ``(qweight, scales, qzeros)``
+* ``awq_dequant(qweight, scales, qzeros, N, K, group_size, zero_point)``
+* ``awq_gemv(x, qweight, scales, qzeros, N, K, group_size, zero_point)``
+* ``awq_gemm(x, qweight, scales, qzeros, N, K, group_size, zero_point)``
+* ``awq_gemm_workspace_bytes(M, N, K, group_size)``, ``awq_strerror(status)``
+
+plus ``pack(W, q_group_size, zero_point)`` / ``linear(x, packed)`` which pick
+GEMV for one token and GEMM otherwise, following ``quant_config``'s
+``version`` ("Optimization Awq", section "Quantizar seu próprio modelo").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+import torch  # noqa: F401  (loaded first: the library then shares torch's HIP runtime)
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libawq_mi355x.so")
+
+AWQ_OK = 0
+AWQ_ERR_NULL = -1
+AWQ_ERR_SHAPE = -2
+AWQ_ERR_GROUP = -3
+AWQ_ERR_ALIGN = -4
+AWQ_ERR_UNSUPPORTED = -5
+AWQ_ERR_WORKSPACE = -6
+AWQ_ERR_HIP = -7
+
+EXPORTED = ("awq_pack", "awq_dequant", "awq_gemv", "awq_gemm", "awq_gemm_workspace_bytes", "awq_strerror")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class AwqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {awq_strerror(status)} (status {status})")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the C ABI library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m bit_weight_only_awq_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.awq_pack.argtypes = [P, I32, I32, I32, I32, P, P, P, P]
+    lib.awq_pack.restype = ctypes.c_int
+    lib.awq_dequant.argtypes = [P, P, P, P, I32, I32, I32, I32, P]
+    lib.awq_dequant.restype = ctypes.c_int
+    lib.awq_gemv.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, P]
+    lib.awq_gemv.restype = ctypes.c_int
+    lib.awq_gemm.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, P, SZ, P]
+    lib.awq_gemm.restype = ctypes.c_int
+    lib.awq_gemm_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.awq_gemm_workspace_bytes.restype = SZ
+    lib.awq_strerror.argtypes = [ctypes.c_int]
+    lib.awq_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the AWQ kernels must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the AWQ kernels must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != AWQ_OK:
+        raise AwqError(status, where)
+
+
+def awq_strerror(status: int) -> str:
+    return load_library().awq_strerror(int(status)).decode()
+
+
+def awq_gemm_workspace_bytes(M: int, N: int, K: int, group_size: int) -> int:
+    return int(load_library().awq_gemm_workspace_bytes(M, N, K, group_size))
+
+
+def awq_pack(w: torch.Tensor, group_size: int = 128, zero_point: bool = True,
+             qweight: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+             qzeros: Optional[torch.Tensor] = None):
+    """Quantize fp16 ``w`` [N, K] and return ``(qweight int32 [N, K/8], scales fp16 [K/g, N],
+    qzeros int32 [K/g, N/8] or None)``; the int32 tensors hold the ABI's uint32 words."""
+    lib = load_library()
+    if w.dtype != torch.float16 or w.dim() != 2:
+        raise ValueError("w must be a 2-D float16 tensor [N, K]")
+    N, K = w.shape
+    G = K // group_size if group_size > 0 else 0
+    dev = w.device
+    if qweight is None:
+        qweight = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    if scales is None:
+        scales = torch.empty((G, N), dtype=torch.float16, device=dev)
+    if zero_point and qzeros is None:
+        qzeros = torch.empty((G, N // 8), dtype=torch.int32, device=dev)
+    st = lib.awq_pack(_ptr(w), N, K, group_size, int(bool(zero_point)), _ptr(qweight), _ptr(scales),
+                      _ptr(qzeros) if zero_point else None, _stream(w))
+    _check(st, "awq_pack")
+    return qweight, scales, (qzeros if zero_point else None)
+
+
+def awq_dequant(qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional[torch.Tensor], N: int, K: int,
+                group_size: int = 128, zero_point: bool = True, w_out: Optional[torch.Tensor] = None):
+    """Decode a packed weight to fp16 [N, K] (test and inspection aid)."""
+    lib = load_library()
+    if w_out is None:
+        w_out = torch.empty((N, K), dtype=torch.float16, device=qweight.device)
+    st = lib.awq_dequant(_ptr(qweight), _ptr(scales), _ptr(qzeros) if zero_point else None, _ptr(w_out), N, K,
+                         group_size, int(bool(zero_point)), _stream(qweight))
+    _check(st, "awq_dequant")
+    return w_out
+
+
+def _xy(x: torch.Tensor, N: int, y: Optional[torch.Tensor]):
+    if x.dtype != torch.float16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D float16 tensor [M, K]")
+    if y is None:
+        y = torch.empty((x.shape[0], N), dtype=torch.float16, device=x.device)
+    return y
+
+
+def awq_gemv(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional[torch.Tensor], N: int,
+             K: int, group_size: int = 128, zero_point: bool = True, y: Optional[torch.Tensor] = None):
+    """Single-token layer y = x . W'^T for x fp16 [1, K]; returns fp16 [1, N]."""
+    lib = load_library()
+    y = _xy(x, N, y)
+    st = lib.awq_gemv(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros) if zero_point else None, _ptr(y),
+                      x.shape[0], N, K, group_size, int(bool(zero_point)), _stream(x))
+    _check(st, "awq_gemv")
+    return y
+
+
+def awq_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional[torch.Tensor], N: int,
+             K: int, group_size: int = 128, zero_point: bool = True, y: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None):
+    """Batched layer Y = X . W'^T for X fp16 [M, K]; returns fp16 [M, N]."""
+    lib = load_library()
+    y = _xy(x, N, y)
+    M = x.shape[0]
+    need = awq_gemm_workspace_bytes(M, N, K, group_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.awq_gemm(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros) if zero_point else None, _ptr(y), M, N, K,
+                      group_size, int(bool(zero_point)), _ptr(workspace), ws_bytes, _stream(x))
+    _check(st, "awq_gemm")
+    return y
+
+
+class PackedWeight(NamedTuple):
+    qweight: torch.Tensor
+    scales: torch.Tensor
+    qzeros: Optional[torch.Tensor]
+    N: int
+    K: int
+    group_size: int
+    zero_point: bool
+
+
+def pack(W: torch.Tensor, q_group_size: int = 128, zero_point: bool = True) -> PackedWeight:
+    """Quantize an ``nn.Linear`` weight [out, in] on the GPU (``quant_config``: w_bit 4)."""
+    qw, sc, qz = awq_pack(W, q_group_size, zero_point)
+    return PackedWeight(qw, sc, qz, W.shape[0], W.shape[1], q_group_size, bool(zero_point))
+
+
+def linear(x: torch.Tensor, pw: PackedWeight, version: str = "auto") -> torch.Tensor:
+    """Y = X . W'^T.  ``version`` "GEMV" (one token), "GEMM" (any batch) or "auto"."""
+    x2 = x.reshape(-1, pw.K)
+    v = version.upper()
+    if v == "AUTO":
+        v = "GEMV" if x2.shape[0] == 1 else "GEMM"
+    fn = awq_gemv if v == "GEMV" else awq_gemm
+    y = fn(x2, pw.qweight, pw.scales, pw.qzeros, pw.N, pw.K, pw.group_size, pw.zero_point)
+    return y.reshape(*x.shape[:-1], pw.N)

@@ -1,0 +1,113 @@
+// C ABI of the W4A16 layer: argument validation, then one launch on the
+// caller's stream.  Declarations and the contract of every entry point are in
+// include/awq.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/awq.h"
+#include "awq_launch.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128 || g == 256; }
+
+// Checks shared by every entry point that reads or writes a packed weight.
+int check_weight_shape(int32_t N, int32_t K, int32_t group_size) {
+  if (!valid_group(group_size)) return AWQ_ERR_GROUP;
+  if (N < 1 || K < 1 || (N & 7) != 0) return AWQ_ERR_SHAPE;
+  if (K % group_size != 0) return AWQ_ERR_GROUP;
+  return AWQ_OK;
+}
+
+int check_packed(const uint32_t* qweight, const void* scales, const uint32_t* qzeros, int32_t zero_point) {
+  if (!qweight || !scales || (zero_point && !qzeros)) return AWQ_ERR_NULL;
+  if (!aligned16(qweight) || !aligned16(scales) || (zero_point && !aligned16(qzeros))) return AWQ_ERR_ALIGN;
+  return AWQ_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? AWQ_OK : AWQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int awq_pack(const void* w, int32_t N, int32_t K, int32_t group_size, int32_t zero_point, uint32_t* qweight,
+             void* scales, uint32_t* qzeros, void* stream) {
+  int st = check_weight_shape(N, K, group_size);
+  if (st != AWQ_OK) return st;
+  if (!w) return AWQ_ERR_NULL;
+  st = check_packed(qweight, scales, qzeros, zero_point);
+  if (st != AWQ_OK) return st;
+  if (!aligned16(w)) return AWQ_ERR_ALIGN;
+  return from_hip(awq::launch_pack(w, N, K, group_size, zero_point != 0, qweight, scales, zero_point ? qzeros : nullptr,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int awq_dequant(const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* w_out, int32_t N, int32_t K,
+                int32_t group_size, int32_t zero_point, void* stream) {
+  int st = check_weight_shape(N, K, group_size);
+  if (st != AWQ_OK) return st;
+  if (!w_out) return AWQ_ERR_NULL;
+  st = check_packed(qweight, scales, qzeros, zero_point);
+  if (st != AWQ_OK) return st;
+  if (!aligned16(w_out)) return AWQ_ERR_ALIGN;
+  return from_hip(awq::launch_dequant(qweight, scales, zero_point ? qzeros : nullptr, w_out, N, K, group_size,
+                                      zero_point != 0, static_cast<hipStream_t>(stream)));
+}
+
+int awq_gemv(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* y, int32_t M,
+             int32_t N, int32_t K, int32_t group_size, int32_t zero_point, void* stream) {
+  int st = check_weight_shape(N, K, group_size);
+  if (st != AWQ_OK) return st;
+  if (M < 1) return AWQ_ERR_SHAPE;
+  if (!x || !y) return AWQ_ERR_NULL;
+  st = check_packed(qweight, scales, qzeros, zero_point);
+  if (st != AWQ_OK) return st;
+  if (!aligned16(x) || !aligned16(y)) return AWQ_ERR_ALIGN;
+  if (M != 1) return AWQ_ERR_UNSUPPORTED;
+  return from_hip(awq::launch_gemv(x, qweight, scales, zero_point ? qzeros : nullptr, y, N, K, group_size,
+                                   zero_point != 0, static_cast<hipStream_t>(stream)));
+}
+
+size_t awq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t group_size) {
+  (void)M;
+  (void)N;
+  (void)K;
+  (void)group_size;
+  return 0;
+}
+
+int awq_gemm(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* y, int32_t M,
+             int32_t N, int32_t K, int32_t group_size, int32_t zero_point, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  int st = check_weight_shape(N, K, group_size);
+  if (st != AWQ_OK) return st;
+  if (M < 1) return AWQ_ERR_SHAPE;
+  if (!x || !y) return AWQ_ERR_NULL;
+  st = check_packed(qweight, scales, qzeros, zero_point);
+  if (st != AWQ_OK) return st;
+  if (!aligned16(x) || !aligned16(y)) return AWQ_ERR_ALIGN;
+  const size_t need = awq_gemm_workspace_bytes(M, N, K, group_size);
+  if (workspace_bytes < need) return AWQ_ERR_WORKSPACE;
+  if (need > 0 && !workspace) return AWQ_ERR_NULL;
+  return from_hip(awq::launch_gemm(x, qweight, scales, zero_point ? qzeros : nullptr, y, M, N, K, group_size,
+                                   zero_point != 0, static_cast<hipStream_t>(stream)));
+}
+
+const char* awq_strerror(int status) {
+  switch (status) {
+    case AWQ_OK: return "ok";
+    case AWQ_ERR_NULL: return "a required pointer is NULL";
+    case AWQ_ERR_SHAPE: return "invalid shape: need M >= 1, N >= 1 with N % 8 == 0, K >= 1";
+    case AWQ_ERR_GROUP: return "invalid group size: need group_size in {32, 64, 128, 256} dividing K";
+    case AWQ_ERR_ALIGN: return "a buffer pointer is not 16-byte aligned";
+    case AWQ_ERR_UNSUPPORTED: return "unsupported argument combination for this entry point (awq_gemv takes M == 1)";
+    case AWQ_ERR_WORKSPACE: return "workspace smaller than awq_gemm_workspace_bytes()";
+    case AWQ_ERR_HIP: return "the HIP runtime reported an error while launching";
+    default: return "unknown awq status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Device-side helpers shared by the gfx950 kernels of the W4A16 layer.
+//
+// Packed weight word (8 input channels of one output row): channel c of the
+// word sits at bit 16*(c & 1) + 4*(c >> 1), so the low halfword holds the even
+// channels 0,2,4,6 and the high halfword the odd channels 1,3,5,7.  That
+// placement lets one AND pick the pair (2t, 2t+1) into the two halves of a
+// 32-bit register, ready to be turned into a half2 without any shuffling.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Bit offset of channel c (0..7) inside its packed word.
+__host__ __device__ constexpr int nibble_shift(int c) { return 16 * (c & 1) + 4 * (c >> 1); }
+
+__device__ __forceinline__ half2_t as_half2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+__device__ __forceinline__ uint32_t as_u32(half2_t v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Subtrahends that turn the biased halves produced by decode_pairs into q - z.
+struct ZeroBias {
+  half2_t hi;  // (1024 + z, 1024 + z): pairs taken from nibble bits 0..3
+  half2_t lo;  // (  64 + z,   64 + z): pairs taken from nibble bits 4..7
+};
+
+__device__ __forceinline__ ZeroBias zero_bias(uint32_t z) {
+  ZeroBias b;
+  b.hi = as_half2((0x6400u + z) * 0x00010001u);
+  b.lo = as_half2((0x5400u + (z << 4)) * 0x00010001u);
+  return b;
+}
+
+// Decode one packed word into four half2 values (q - z), pair t holding
+// channels (2t, 2t+1).  Every step is exact:
+//   * a nibble in bits 0..3 OR-ed under the fp16 pattern 0x6400 (1024.0) reads
+//     as 1024 + q (the fp16 spacing at 1024 is 1);
+//   * a nibble in bits 4..7 OR-ed under 0x5400 (64.0) reads as 64 + q (the
+//     spacing at 64 is 1/16 and the nibble sits 4 bits up);
+//   * subtracting 1024 + z or 64 + z leaves the small integer q - z, which
+//     fp16 represents exactly.
+__device__ __forceinline__ void decode_pairs(uint32_t w, const ZeroBias& b, half2_t d[4]) {
+  const uint32_t w8 = w >> 8;
+  d[0] = as_half2((w & 0x000F000Fu) | 0x64006400u) - b.hi;
+  d[1] = as_half2((w & 0x00F000F0u) | 0x54005400u) - b.lo;
+  d[2] = as_half2((w8 & 0x000F000Fu) | 0x64006400u) - b.hi;
+  d[3] = as_half2((w8 & 0x00F000F0u) | 0x54005400u) - b.lo;
+}
+
+// Decoded weights w' = (q - z) * s of one word as 8 halves in channel order,
+// each rounded once to fp16 (the product q - z times s is formed exactly and
+// rounded by the fp16 multiply).
+__device__ __forceinline__ half8_t decode_word_scaled(uint32_t w, const ZeroBias& b, half2_t s2) {
+  half2_t d[4];
+  decode_pairs(w, b, d);
+  half2_t p0 = d[0] * s2, p1 = d[1] * s2, p2 = d[2] * s2, p3 = d[3] * s2;
+  half8_t r;
+  r[0] = p0[0]; r[1] = p0[1];
+  r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1];
+  r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ half8_t as_half8(u32x4 v) { return __builtin_bit_cast(half8_t, v); }
+
+__device__ __forceinline__ half2_t splat2(_Float16 h) {
+  half2_t r;
+  r[0] = h;
+  r[1] = h;
+  return r;
+}
+
+// The hardware dispatches workgroup b of a 1-D grid to XCD (b mod 8).  This
+// returns a tile index such that each XCD works on one contiguous range of
+// tiles, so tiles that share operands also share that XCD's L2.
+__device__ __forceinline__ int xcd_contiguous_tile(int b, int nblocks) {
+  const int q = nblocks >> 3, r = nblocks & 7;
+  const int x = b & 7, local = b >> 3;
+  return x * q + (x < r ? x : r) + local;
+}
+
+}  // namespace awq

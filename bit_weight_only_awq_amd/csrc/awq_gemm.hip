@@ -1,0 +1,314 @@
+// Batched W4A16 layer (awq_gemm): Y[M][N] = X[M][K] . W'^T, W' = (q - z) * s.
+//
+// The GEMM variant of the quantized linear layer ("AI-Research-SKILLs AWQ 高级
+// 使用指南", section WQLinear 内核全景: general matrix multiplication for
+// batches).  Weights are decoded to fp16 on the fly (exact q - z, one fp16
+// rounding of the product with the group scale) and multiplied on the gfx950
+// fp16 matrix cores with fp32 accumulation.  Two kernels:
+//
+//   * gemm_skinny_kernel (M <= 64): still bound by the weight stream.  A wave
+//     owns NT tiles of 16 output rows and all (<= 4) tiles of 16 tokens; its
+//     lanes load packed weights straight into MFMA B-operand registers (one
+//     128-bit load = 32 channels of one row = four 16x16x32 B fragments), so
+//     no LDS round trip sits on the weight path.  The NW waves of a workgroup
+//     split K and are summed through LDS in a fixed order (deterministic, no
+//     workspace, no atomics).
+//
+//   * gemm_large_kernel (M > 64): compute-bound.  256x256 output tile per
+//     workgroup of 4 waves (2x2, 128x128 each, 4x4 v_mfma_f32_32x32x16_f16
+//     tiles), K in steps of 64.  The next step's X tile and packed weights are
+//     fetched into registers while the current step multiplies out of LDS; the
+//     weights are then decoded and written to LDS as fp16 next to the X tile.
+//     LDS rows are padded to 72 halves so that the 128-bit fragment reads of 8
+//     consecutive rows hit distinct banks.  Workgroups are mapped so that each
+//     XCD (and its L2) works on a contiguous band of tiles.
+//
+// MFMA operand placement: a lane's 8 fp16 values of A and of B cover the same
+// 8 reduction indices, so any assignment of channels to (lane group, element)
+// slots gives the same product as long as A and B use the same one.  Both
+// kernels give a lane whole packed words (8 consecutive channels).
+#include "awq_device.hpp"
+#include "awq_launch.hpp"
+
+namespace awq {
+namespace {
+
+int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 128 ? 7 : 8; }
+
+// --------------------------------------------------------------------------
+// Skinny M: weight-stream bound.
+// --------------------------------------------------------------------------
+template <int MT, int NT, int NW, bool ZP>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const u32x4* __restrict__ X,
+                                                              const u32x4* __restrict__ qweight,
+                                                              const uint16_t* __restrict__ scales,
+                                                              const uint32_t* __restrict__ qzeros,
+                                                              _Float16* __restrict__ Y, int M, int N, int K,
+                                                              int gshift) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int li = lane & 15, lh = lane >> 4;
+  const int n0 = blockIdx.x * (16 * NT);
+  const int chunks = (K + 127) >> 7;  // 128-channel steps
+  const size_t row_u4 = (size_t)(K >> 5);
+  const size_t xrow_u4 = (size_t)(K >> 3);
+
+  float4_t acc[MT][NT];
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[a][b] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int c = wave; c < chunks; c += NW) {
+    const int k0 = (c << 7) + (lh << 5);  // this lane's 32 channels: k0 .. k0+31
+    const bool kin = k0 < K;
+    u32x4 wv[NT];
+    half2_t s2[NT];
+    ZeroBias zb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = n0 + 16 * nt + li;
+      const bool ok = kin && n < N;
+      wv[nt] = ok ? qweight[(size_t)n * row_u4 + (k0 >> 5)] : u32x4{0u, 0u, 0u, 0u};
+      const int grp = k0 >> gshift;
+      _Float16 s = (_Float16)0.0f;
+      uint32_t z = 8;
+      if (ok) {
+        s = __builtin_bit_cast(_Float16, scales[(size_t)grp * N + n]);
+        if (ZP) z = (qzeros[(size_t)grp * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 15u;
+      }
+      s2[nt] = splat2(s);
+      zb[nt] = zero_bias(z);
+    }
+    u32x4 xv[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = 16 * mt + li;
+      const bool ok = kin && m < M;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        xv[mt][e] = ok ? X[(size_t)m * xrow_u4 + (k0 >> 3) + e] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      half8_t bfrag[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) bfrag[nt] = decode_word_scaled(wv[nt][e], zb[nt], s2[nt]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const half8_t afrag = as_half8(xv[mt][e]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag, bfrag[nt], acc[mt][nt], 0, 0, 0);
+      }
+    }
+  }
+
+  // 16x16 accumulator layout: lane (li, lh) holds column li, rows 4*lh + r.
+  if constexpr (NW == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = 16 * mt + 4 * lh + r, n = n0 + 16 * nt + li;
+          if (m < M && n < N) Y[(size_t)m * N + n] = (_Float16)acc[mt][nt][r];
+        }
+  } else {
+    constexpr int kVals = MT * NT * 4;
+    __shared__ float red[NW][kVals][64];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][(mt * NT + nt) * 4 + r][lane] = acc[mt][nt][r];
+    __syncthreads();
+    for (int o = t; o < kVals * 64; o += NW * 64) {
+      const int idx = o >> 6, ln = o & 63;
+      float sum = red[0][idx][ln];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) sum += red[w][idx][ln];
+      const int mt = idx / (NT * 4), nt = (idx >> 2) % NT, r = idx & 3;
+      const int m = 16 * mt + 4 * (ln >> 4) + r, n = n0 + 16 * nt + (ln & 15);
+      if (m < M && n < N) Y[(size_t)m * N + n] = (_Float16)sum;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Large M: matrix-core bound.
+// --------------------------------------------------------------------------
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int LDS_STRIDE = BK + 8;  // halves per LDS row (padding breaks bank conflicts)
+constexpr int TILE_HALVES = BM * LDS_STRIDE;
+
+template <bool ZP>
+__global__ __launch_bounds__(256) void gemm_large_kernel(const u32x4* __restrict__ X,
+                                                         const uint32_t* __restrict__ qweight,
+                                                         const uint16_t* __restrict__ scales,
+                                                         const uint32_t* __restrict__ qzeros,
+                                                         _Float16* __restrict__ Y, int M, int N, int K, int gshift,
+                                                         int tiles_m) {
+  __shared__ __attribute__((aligned(16))) _Float16 lds[2][2][TILE_HALVES];  // [buffer][X | W'][row * 72 + k]
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int wm = (wave & 1) * 128, wn = (wave >> 1) * 128;
+  const int kw = K >> 3;
+  const size_t xrow_u4 = (size_t)(K >> 3);
+  const int nsteps = (K + BK - 1) / BK;
+
+  // Global -> register staging.  X: thread t loads 8 x 16 B: rows (t >> 3) + 32 i,
+  // channels 8 * (t & 7) .. +8 of the step.  W: thread t loads the 8 packed
+  // words (64 channels) of row n0 + t for the step.
+  const int xr = t >> 3, xc = t & 7;
+  u32x4 xreg[8];
+  uint32_t wreg[8];
+  _Float16 sreg[2];
+  uint32_t zreg[2];
+
+  auto fetch = [&](int step) {
+    const int k0 = step * BK;
+    const bool kin = k0 + 8 * xc < K;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = m0 + xr + 32 * i;
+      xreg[i] = (kin && m < M) ? X[(size_t)m * xrow_u4 + (k0 >> 3) + xc] : u32x4{0u, 0u, 0u, 0u};
+    }
+    const int n = n0 + t;
+    const bool nin = n < N;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = (k0 >> 3) + i;
+      wreg[i] = (nin && j < kw) ? qweight[(size_t)n * kw + j] : 0u;
+    }
+#pragma unroll
+    for (int hgrp = 0; hgrp < 2; ++hgrp) {
+      const int kk = k0 + 32 * hgrp;
+      _Float16 s = (_Float16)0.0f;
+      uint32_t z = 8;
+      if (nin && kk < K) {
+        const int grp = kk >> gshift;
+        s = __builtin_bit_cast(_Float16, scales[(size_t)grp * N + n]);
+        if (ZP) z = (qzeros[(size_t)grp * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 15u;
+      }
+      sreg[hgrp] = s;
+      zreg[hgrp] = z;
+    }
+  };
+
+  auto stash = [&](int buf) {
+    _Float16* xa = lds[buf][0];
+    _Float16* wb = lds[buf][1];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(xa + (xr + 32 * i) * LDS_STRIDE + 8 * xc) = xreg[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int hgrp = i >> 2;  // words 0-3 and 4-7 may sit in different groups when g = 32
+      const half8_t v = decode_word_scaled(wreg[i], zero_bias(zreg[hgrp]), splat2(sreg[hgrp]));
+      *reinterpret_cast<half8_t*>(wb + t * LDS_STRIDE + 8 * i) = v;
+    }
+  };
+
+  float16_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+
+  const int fi = lane & 31, fh = lane >> 5;  // fragment row and k-half of this lane
+  for (int step = 0; step < nsteps; ++step) {
+    const int buf = step & 1;
+    const bool more = step + 1 < nsteps;
+    if (more) fetch(step + 1);
+
+    const _Float16* xa = lds[buf][0];
+    const _Float16* wb = lds[buf][1];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      half8_t af[4], bf[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        af[a] = *reinterpret_cast<const half8_t*>(xa + (wm + 32 * a + fi) * LDS_STRIDE + 16 * ks + 8 * fh);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        bf[b] = *reinterpret_cast<const half8_t*>(wb + (wn + 32 * b + fi) * LDS_STRIDE + 16 * ks + 8 * fh);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+    }
+
+    if (more) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // 32x32 accumulator layout: lane l holds column l % 32 and, in register r,
+  // row 8 * (r / 4) + 4 * (l / 32) + r % 4.
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int n = n0 + wn + 32 * b + fi;
+      if (n >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm + 32 * a + 8 * (r >> 2) + 4 * fh + (r & 3);
+        if (m < M) Y[(size_t)m * N + n] = (_Float16)acc[a][b][r];
+      }
+    }
+}
+
+template <int MT, bool ZP>
+hipError_t launch_skinny(const u32x4* X, const u32x4* qw, const uint16_t* sc, const uint32_t* qz, _Float16* Y, int M,
+                         int N, int K, int gs, hipStream_t stream) {
+  constexpr int NT = MT >= 3 ? 1 : 2;
+  constexpr int NW = 4;
+  const dim3 grid((N + 16 * NT - 1) / (16 * NT));
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, NW, ZP>), grid, dim3(NW * 64), 0, stream, X, qw, sc, qz, Y, M, N, K,
+                     gs);
+  return hipGetLastError();
+}
+
+template <bool ZP>
+hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* y,
+                     int M, int N, int K, int group_size, hipStream_t stream) {
+  const u32x4* X = static_cast<const u32x4*>(x);
+  const uint16_t* sc = static_cast<const uint16_t*>(scales);
+  _Float16* Y = static_cast<_Float16*>(y);
+  const int gs = log2_group(group_size);
+  if (M <= 64) {
+    const u32x4* qw = reinterpret_cast<const u32x4*>(qweight);
+    switch ((M + 15) / 16) {
+      case 1: return launch_skinny<1, ZP>(X, qw, sc, qzeros, Y, M, N, K, gs, stream);
+      case 2: return launch_skinny<2, ZP>(X, qw, sc, qzeros, Y, M, N, K, gs, stream);
+      case 3: return launch_skinny<3, ZP>(X, qw, sc, qzeros, Y, M, N, K, gs, stream);
+      default: return launch_skinny<4, ZP>(X, qw, sc, qzeros, Y, M, N, K, gs, stream);
+    }
+  }
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_large_kernel<ZP>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, X, qweight, sc, qzeros, Y,
+                     M, N, K, gs, tiles_m);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* y,
+                       int M, int N, int K, int group_size, bool zero_point, hipStream_t stream) {
+  return zero_point ? launch_zp<true>(x, qweight, scales, qzeros, y, M, N, K, group_size, stream)
+                    : launch_zp<false>(x, qweight, scales, qzeros, y, M, N, K, group_size, stream);
+}
+
+}  // namespace awq

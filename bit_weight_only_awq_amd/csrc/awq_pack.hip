@@ -1,0 +1,186 @@
+// Group-wise 4-bit quantization and packing (awq_pack) and the fp16 decoder
+// used to inspect packed weights (awq_dequant).
+//
+// The quantizer follows "AI-Research-SKILLs AWQ 高级使用指南", section
+// 分组大小与零点量化: every group of g consecutive input channels of one
+// output row shares one scale and one zero point; with zero_point the grid is
+// shifted to cover an asymmetric range, without it the grid is symmetric.
+// The codes are q = clamp(round(w/s) + z, 0, 15).  The arithmetic is IEEE
+// fp32 in one fixed order, with round-half-to-even and correctly rounded
+// division, so the output is bit-reproducible:
+//   zero_point:  r = max(max - min, 1e-5); s = fp16(r / 15); z = clamp(rne(-min / s), 0, 15)
+//   symmetric:   a = max(max|w|, 1e-5);    s = fp16(a / 7);  z = 8
+//   q = clamp(rne(w / s) + z, 0, 15)
+#include "awq_device.hpp"
+#include "awq_launch.hpp"
+
+#pragma clang fp contract(off)
+
+namespace awq {
+namespace {
+
+constexpr int kPackThreads = 256;  // 8 rows x 32 lanes
+constexpr float kRangeFloor = 1e-5f;
+
+// One block quantizes one octet of rows (n0 .. n0+7).  Thread t works on row
+// n0 + (t >> 5); its lane l = t & 31 owns one packed word (8 channels) of each
+// 256-channel pass over the row.  A group of g channels is GW = g/8
+// consecutive lanes of the same row, reduced with butterfly shuffles (GW
+// divides 32, so a group never leaves its half-wave).  Scales and zero points
+// of the octet are staged in LDS and written 8 rows at a time.
+template <int GW, bool ZP>
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restrict__ w, int N, int K,
+                                                            uint32_t* __restrict__ qweight,
+                                                            uint16_t* __restrict__ scales,
+                                                            uint32_t* __restrict__ qzeros) {
+  constexpr int kGroupsPerPass = 32 / GW;
+  __shared__ uint16_t s_lds[kGroupsPerPass][8];
+  __shared__ uint8_t z_lds[kGroupsPerPass][8];
+
+  const int t = threadIdx.x;
+  const int r = t >> 5, l = t & 31;
+  const int n0 = blockIdx.x * 8;
+  const int n = n0 + r;
+  const int kw = K >> 3;            // packed words per row
+  const int ngroups = kw / GW;      // groups per row
+
+  for (int w0 = 0; w0 < kw; w0 += 32) {
+    const int j = w0 + l;
+    const bool active = j < kw;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (active) raw = w[(size_t)n * kw + j];
+    const half8_t h = as_half8(raw);
+
+    float a[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a[c] = (float)h[c];
+
+    float s, zf;
+    _Float16 s16;
+    if constexpr (ZP) {
+      float mn = a[0], mx = a[0];
+#pragma unroll
+      for (int c = 1; c < 8; ++c) {
+        mn = fminf(mn, a[c]);
+        mx = fmaxf(mx, a[c]);
+      }
+#pragma unroll
+      for (int off = 1; off < GW; off <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off));
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+      }
+      float rng = mx - mn;
+      if (rng < kRangeFloor) rng = kRangeFloor;
+      s16 = (_Float16)(rng / 15.0f);
+      s = (float)s16;
+      zf = rintf(-mn / s);
+      zf = fminf(fmaxf(zf, 0.0f), 15.0f);
+    } else {
+      float amax = fabsf(a[0]);
+#pragma unroll
+      for (int c = 1; c < 8; ++c) amax = fmaxf(amax, fabsf(a[c]));
+#pragma unroll
+      for (int off = 1; off < GW; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+      if (amax < kRangeFloor) amax = kRangeFloor;
+      s16 = (_Float16)(amax / 7.0f);
+      s = (float)s16;
+      zf = 8.0f;
+    }
+
+    uint32_t word = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float v = rintf(a[c] / s) + zf;
+      v = fminf(fmaxf(v, 0.0f), 15.0f);
+      word |= (uint32_t)v << nibble_shift(c);
+    }
+    if (active) qweight[(size_t)n * kw + j] = word;
+
+    if (active && (l % GW) == 0) {
+      s_lds[l / GW][r] = __builtin_bit_cast(uint16_t, s16);
+      z_lds[l / GW][r] = (uint8_t)zf;
+    }
+    __syncthreads();
+    const int gbase = w0 / GW;
+    if (t < kGroupsPerPass * 8) {
+      const int gi = t >> 3, rr = t & 7;
+      if (gbase + gi < ngroups) scales[(size_t)(gbase + gi) * N + n0 + rr] = s_lds[gi][rr];
+    }
+    if constexpr (ZP) {
+      if (t < kGroupsPerPass && gbase + t < ngroups) {
+        uint32_t zw = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) zw |= (uint32_t)z_lds[t][i] << (4 * i);
+        qzeros[(size_t)(gbase + t) * (N >> 3) + (n0 >> 3)] = zw;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// One thread per packed word: w_out[n][8j .. 8j+7] = fp16((q - z) * s).
+// (q - z) * s is exact in fp32 (a 5-bit by 11-bit product), so the single
+// conversion to fp16 is the only rounding.
+__global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ qweight,
+                                                      const uint16_t* __restrict__ scales,
+                                                      const uint32_t* __restrict__ qzeros,
+                                                      u32x4* __restrict__ w_out, int N, int K, int gshift,
+                                                      int zero_point) {
+  const int kw = K >> 3;
+  const size_t total = (size_t)N * kw;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int n = (int)(idx / kw), j = (int)(idx % kw);
+    const int grp = (j << 3) >> gshift;
+    const float s = (float)__builtin_bit_cast(_Float16, scales[(size_t)grp * N + n]);
+    int z = 8;
+    if (zero_point) z = (int)((qzeros[(size_t)grp * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 15u);
+    const uint32_t word = qweight[idx];
+    half8_t out;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int q = (int)((word >> nibble_shift(c)) & 15u);
+      out[c] = (_Float16)((float)(q - z) * s);
+    }
+    w_out[idx] = __builtin_bit_cast(u32x4, out);
+  }
+}
+
+template <bool ZP>
+hipError_t launch_pack_zp(const void* w, int N, int K, int group_size, uint32_t* qweight, void* scales,
+                          uint32_t* qzeros, hipStream_t stream) {
+  const dim3 grid(N / 8), block(kPackThreads);
+  const u32x4* wv = static_cast<const u32x4*>(w);
+  uint16_t* sc = static_cast<uint16_t*>(scales);
+  switch (group_size) {
+    case 32: hipLaunchKernelGGL((pack_kernel<4, ZP>), grid, block, 0, stream, wv, N, K, qweight, sc, qzeros); break;
+    case 64: hipLaunchKernelGGL((pack_kernel<8, ZP>), grid, block, 0, stream, wv, N, K, qweight, sc, qzeros); break;
+    case 128: hipLaunchKernelGGL((pack_kernel<16, ZP>), grid, block, 0, stream, wv, N, K, qweight, sc, qzeros); break;
+    case 256: hipLaunchKernelGGL((pack_kernel<32, ZP>), grid, block, 0, stream, wv, N, K, qweight, sc, qzeros); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 128 ? 7 : 8; }
+
+}  // namespace
+
+hipError_t launch_pack(const void* w, int N, int K, int group_size, bool zero_point, uint32_t* qweight,
+                       void* scales, uint32_t* qzeros, hipStream_t stream) {
+  return zero_point ? launch_pack_zp<true>(w, N, K, group_size, qweight, scales, qzeros, stream)
+                    : launch_pack_zp<false>(w, N, K, group_size, qweight, scales, qzeros, stream);
+}
+
+hipError_t launch_dequant(const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* w_out,
+                          int N, int K, int group_size, bool zero_point, hipStream_t stream) {
+  const size_t words = (size_t)N * (K >> 3);
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, qweight,
+                     static_cast<const uint16_t*>(scales), qzeros, static_cast<u32x4*>(w_out), N, K,
+                     log2_group(group_size), zero_point ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace awq

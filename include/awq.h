@@ -1,0 +1,132 @@
+/*
+ * awq.h - C ABI of the MI355X (gfx950) W4A16 group-wise quantized linear layer.
+ *
+ * The layer is AWQ's 4-bit weight-only linear layer: weights are stored as
+ * 4-bit codes with one fp16 scale and one 4-bit zero point per group of
+ * consecutive input channels, activations stay fp16, and the layer computes
+ * Y = X . W'^T with W' = (q - z) * s.  Sources (web pages, by title and section):
+ *   - "AI-Research-SKILLs AWQ 高级使用指南", section 分组大小与零点量化
+ *     ("Group Size": a group shares one scale and zero point; 32/128/256,
+ *     128 recommended; "Zero-Point": an offset for asymmetric ranges,
+ *     zero_point False = symmetric), section WQLinear 内核全景 (GEMM kernel
+ *     for batches, GEMV kernel for a single token).
+ *   - "Optimization Awq", section "Quantizar seu próprio modelo" (quant_config
+ *     = zero_point, q_group_size, w_bit = 4, version GEMM | GEMV) and section
+ *     "Integração vLLM" (half-precision activations).
+ *
+ * Conventions for every entry point
+ *   - All buffer pointers are DEVICE pointers on the current HIP device; the
+ *     caller allocates and owns them.  The library never allocates, frees or
+ *     keeps mutable state between calls, and never synchronizes the device.
+ *   - fp16 buffers are passed as void* and hold IEEE binary16 values.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; the return value reports argument
+ *     validation and launch errors only.  On any error nothing is launched.
+ *   - Every pointer must be 16-byte aligned.  Buffers must not overlap.
+ *   - Shapes: N (output features) >= 1 and a multiple of 8; K (input
+ *     features) >= 1 and a multiple of group_size; group_size in
+ *     {32, 64, 128, 256}; M (tokens) >= 1.  G = K / group_size.
+ *   - Weights must be finite; results for NaN/Inf weights are unspecified.
+ *
+ * Storage layout of a packed weight (the pages fix none; this one is ours):
+ *   qweight  uint32 [N][K/8]  word (n, j) holds the 4-bit codes of channels
+ *            k = 8j .. 8j+7 of row n: channel 8j+c sits at bit
+ *            16*(c & 1) + 4*(c >> 1), i.e. the low halfword holds the even
+ *            channels 0,2,4,6 and the high halfword the odd ones 1,3,5,7.
+ *   scales   fp16   [G][N]    scale of row n, group j at (j, n).
+ *   qzeros   uint32 [G][N/8]  zero point of row 8c+i, group j in bits
+ *            4i..4i+3 of word (j, c).  Only with zero_point != 0; the
+ *            symmetric format has the implicit zero point 8 and no qzeros.
+ */
+#ifndef AWQ_MI355X_AWQ_H
+#define AWQ_MI355X_AWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum awq_status {
+  AWQ_OK = 0,
+  AWQ_ERR_NULL = -1,        /* a required pointer is NULL                      */
+  AWQ_ERR_SHAPE = -2,       /* M, N or K out of range / not a multiple         */
+  AWQ_ERR_GROUP = -3,       /* group_size not in {32,64,128,256} or K % g != 0  */
+  AWQ_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                */
+  AWQ_ERR_UNSUPPORTED = -5, /* valid arguments this entry point does not take  */
+  AWQ_ERR_WORKSPACE = -6,   /* workspace smaller than awq_gemm_workspace_bytes */
+  AWQ_ERR_HIP = -7          /* the HIP runtime reported an error at launch     */
+};
+
+/*
+ * awq_pack - quantize fp16 weights group-wise to 4 bits and store them.
+ *
+ * Defines the quantizer Q ("AI-Research-SKILLs AWQ 高级使用指南", section
+ * 分组大小与零点量化; codes q = clamp(round(w/s) + z, 0, 15)).  For each row n
+ * and group j (channels j*g .. j*g+g-1), all in IEEE fp32 with
+ * round-half-to-even:
+ *   zero_point != 0:  r = max(max - min, 1e-5);  s = fp16(r / 15);
+ *                     z = clamp(rne(-min / s), 0, 15)
+ *   zero_point == 0:  a = max(max |w|, 1e-5);    s = fp16(a / 7);  z = 8
+ *   q = clamp(rne(w / s) + z, 0, 15)   (correctly rounded fp32 division by
+ *                                       the fp16-rounded scale s)
+ *
+ * w        in   fp16  [N][K], row-major.
+ * qweight  out  uint32 [N][K/8]; scales out fp16 [G][N];
+ * qzeros   out  uint32 [G][N/8] when zero_point != 0 (may be NULL otherwise).
+ * Deterministic: the output is bit-identical for identical input.
+ */
+int awq_pack(const void* w, int32_t N, int32_t K, int32_t group_size, int32_t zero_point,
+             uint32_t* qweight, void* scales, uint32_t* qzeros, void* stream);
+
+/*
+ * awq_dequant - decode a packed weight to fp16: w_out[n][k] = fp16((q - z) * s),
+ * rounded once to nearest-even.  A test and inspection aid; not on the hot path.
+ * w_out out fp16 [N][K].
+ */
+int awq_dequant(const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* w_out,
+                int32_t N, int32_t K, int32_t group_size, int32_t zero_point, void* stream);
+
+/*
+ * awq_gemv - single-token quantized linear layer, y = x . W'^T.
+ *
+ * The GEMV variant ("AI-Research-SKILLs AWQ 高级使用指南", section WQLinear 内核全景,
+ * WQLinear_GEMV: single-token generation, batch size 1 only).
+ * x in fp16 [M][K] with M == 1 (AWQ_ERR_UNSUPPORTED otherwise);
+ * y out fp16 [M][N].  Accumulation is fp32, the output rounded once to fp16.
+ * Each output meets |y - y_ref| <= 1e-3 * sum_k |x_k w'_k| against the exact
+ * product, and is bit-reproducible run to run.
+ */
+int awq_gemv(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros,
+             void* y, int32_t M, int32_t N, int32_t K, int32_t group_size, int32_t zero_point,
+             void* stream);
+
+/*
+ * awq_gemm - batched quantized linear layer, Y = X . W'^T, any M >= 1.
+ *
+ * The GEMM variant ("AI-Research-SKILLs AWQ 高级使用指南", section WQLinear 内核全景,
+ * WQLinear_GEMM: general matrix multiplication for batches).  Weights are
+ * decoded to fp16 in registers and multiplied on the fp16 matrix cores with
+ * fp32 accumulation; the output is rounded once to fp16.
+ * X in fp16 [M][K]; Y out fp16 [M][N].  Same accuracy contract as awq_gemv.
+ * workspace: device scratch of at least awq_gemm_workspace_bytes(M, N, K,
+ * group_size) bytes (may be NULL when that is 0), owned by the caller and
+ * not read before it is written.  Deterministic run to run.
+ */
+int awq_gemm(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros,
+             void* y, int32_t M, int32_t N, int32_t K, int32_t group_size, int32_t zero_point,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace awq_gemm needs for this shape (0 when it needs none). */
+size_t awq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t group_size);
+
+/* Static, NUL-terminated description of a status code. */
+const char* awq_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_MI355X_AWQ_H */

@@ -1,0 +1,109 @@
+"""The C ABI library loads, exports every entry point declared in
+include/awq.h, and rejects invalid arguments on the host, before any launch.
+
+These tests run without a GPU: every call below fails validation, so no
+pointer is ever dereferenced and nothing reaches the HIP runtime."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq.h")
+
+awq = pytest.importorskip("bit_weight_only_awq_amd")
+
+
+def declared_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(awq_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(awq.LIB_PATH):
+        pytest.fail(f"{awq.LIB_PATH} not built; run python -m bit_weight_only_awq_amd.build")
+    return awq.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(awq.EXPORTED), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_strerror_and_workspace(lib):
+    for code in range(-7, 1):
+        assert awq.awq_strerror(code) and awq.awq_strerror(code) != "unknown awq status"
+    assert awq.awq_strerror(42) == "unknown awq status"
+    assert awq.awq_gemm_workspace_bytes(2048, 28672, 8192, 128) == 0
+
+
+# Fake, 16-byte aligned device addresses: validation must reject every call
+# below before anything could touch them.
+A = 0x7F0000000000
+B = A + 0x100000
+C = A + 0x200000
+D = A + 0x300000
+E = A + 0x400000
+
+
+@pytest.mark.parametrize(
+    "args,expect",
+    [
+        # (N, K, g, zp, w, qweight, scales, qzeros)
+        ((8, 128, 48, 1, A, B, C, D), awq.AWQ_ERR_GROUP),
+        ((8, 96, 64, 1, A, B, C, D), awq.AWQ_ERR_GROUP),
+        ((12, 128, 32, 1, A, B, C, D), awq.AWQ_ERR_SHAPE),
+        ((0, 128, 32, 1, A, B, C, D), awq.AWQ_ERR_SHAPE),
+        ((8, 0, 32, 1, A, B, C, D), awq.AWQ_ERR_SHAPE),
+        ((8, 128, 32, 1, 0, B, C, D), awq.AWQ_ERR_NULL),
+        ((8, 128, 32, 1, A, 0, C, D), awq.AWQ_ERR_NULL),
+        ((8, 128, 32, 1, A, B, C, 0), awq.AWQ_ERR_NULL),
+        ((8, 128, 32, 1, A + 4, B, C, D), awq.AWQ_ERR_ALIGN),
+        ((8, 128, 32, 1, A, B + 8, C, D), awq.AWQ_ERR_ALIGN),
+    ],
+)
+def test_pack_validation(lib, args, expect):
+    N, K, g, zp, w, qw, sc, qz = args
+    assert lib.awq_pack(w or None, N, K, g, zp, qw or None, sc or None, qz or None, None) == expect
+
+
+def test_gemv_gemm_validation(lib):
+    ok = dict(x=A, qw=B, sc=C, qz=D, y=E)
+    gemv = lambda M, N, K, g, zp, **kw: lib.awq_gemv(  # noqa: E731
+        kw.get("x", A) or None, kw.get("qw", B) or None, kw.get("sc", C) or None, kw.get("qz", D) or None,
+        kw.get("y", E) or None, M, N, K, g, zp, None)
+    assert gemv(2, 8, 128, 32, 1) == awq.AWQ_ERR_UNSUPPORTED
+    assert gemv(0, 8, 128, 32, 1) == awq.AWQ_ERR_SHAPE
+    assert gemv(1, 8, 128, 100, 1) == awq.AWQ_ERR_GROUP
+    assert gemv(1, 8, 128, 32, 1, y=0) == awq.AWQ_ERR_NULL
+    assert gemv(1, 8, 128, 32, 1, x=A + 2) == awq.AWQ_ERR_ALIGN
+    assert gemv(1, 8, 128, 32, 1, qz=0) == awq.AWQ_ERR_NULL
+    gemm = lambda M, N, K, g, zp, ws=0, wsb=0, **kw: lib.awq_gemm(  # noqa: E731
+        kw.get("x", A) or None, kw.get("qw", B) or None, kw.get("sc", C) or None, kw.get("qz", D) or None,
+        kw.get("y", E) or None, M, N, K, g, zp, ws or None, wsb, None)
+    assert gemm(0, 8, 128, 32, 1) == awq.AWQ_ERR_SHAPE
+    assert gemm(4, 10, 128, 32, 1) == awq.AWQ_ERR_SHAPE
+    assert gemm(4, 8, 160, 64, 1) == awq.AWQ_ERR_GROUP
+    assert gemm(4, 8, 128, 32, 1, sc=0) == awq.AWQ_ERR_NULL
+    assert gemm(4, 8, 128, 32, 1, y=E + 6) == awq.AWQ_ERR_ALIGN
+    assert ok  # silence unused
+
+
+def test_dequant_validation(lib):
+    assert lib.awq_dequant(B, C, D, None, 8, 128, 32, 1, None) == awq.AWQ_ERR_NULL
+    assert lib.awq_dequant(B, C, None, A, 8, 128, 32, 1, None) == awq.AWQ_ERR_NULL
+    assert lib.awq_dequant(B, C, D, A, 8, 100, 32, 1, None) == awq.AWQ_ERR_GROUP
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    w = torch.zeros((8, 128), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        awq.awq_pack(w, 32, True)

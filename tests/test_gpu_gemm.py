@@ -1,0 +1,128 @@
+"""awq_gemm (any M) on the GPU against the oracle: per-element tolerance
+1e-3 * sum_k |x_k w'_k| on the skinny (M <= 64) and the matrix-core (M > 64)
+kernels, ragged tiles, one-hot bit-exactness, the batched-decode and prefill
+shapes at full size (prefill on sampled outputs), determinism."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import awq_oracle as O
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def run_gemm(X16, packed, N, K, g, zp, stream=None):
+    awq = G.lib()
+    dqw, dsc, dqz = G.upload_packed(*packed)
+    x = G.dev_f16(X16)
+    if stream is None:
+        y = awq.awq_gemm(x, dqw, dsc, dqz, N, K, g, zp)
+    else:
+        with torch.cuda.stream(stream):
+            y = awq.awq_gemm(x, dqw, dsc, dqz, N, K, g, zp)
+        stream.synchronize()
+    torch.cuda.synchronize()
+    return G.host_f16(y)
+
+
+def check(M, N, K, g, zp, W=None, X=None, what=""):
+    if W is None:
+        W = workloads.weight(N, K, cfg=3, layer=N + K)
+    if X is None:
+        X = workloads.activations(M, K, cfg=3, layer=N + K)
+    packed = O.pack(W, g, zp)
+    y = run_gemm(X, packed, N, K, g, zp)
+    y_ref, d = O.matmul_ref(X, O.dequant_packed(*packed, N, K, g, zp))
+    return G.assert_within_tolerance(y, y_ref, d, what or f"gemm M={M} N={N} K={K} g={g} zp={zp}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 15, 16, 17, 31, 33, 48, 64])
+def test_gemm_skinny_m(M):
+    check(M, 512, 512, 128, True)
+
+
+@pytest.mark.parametrize("M", [65, 128, 256, 300, 512])
+def test_gemm_large_m(M):
+    check(M, 512, 1024, 128, True)
+
+
+@pytest.mark.parametrize("zp", [True, False])
+@pytest.mark.parametrize("g", [32, 64, 128, 256])
+@pytest.mark.parametrize("M", [8, 96])
+def test_gemm_group_sizes_and_symmetry(M, g, zp):
+    W = workloads.weight(512, 2048, cfg=5, layer=g, row_offset=True)
+    check(M, 512, 2048, g, zp, W=W)
+
+
+@pytest.mark.parametrize("M,N,K,g", [(1, 8, 32, 32), (5, 8, 96, 32), (70, 8, 96, 32), (3, 24, 160, 32),
+                                     (200, 264, 2080, 32), (64, 40, 4128, 32), (257, 520, 544, 32),
+                                     (33, 4104, 256, 256)])
+def test_gemm_ragged_tiles(M, N, K, g):
+    check(M, N, K, g, True)
+    check(M, N, K, g, False)
+
+
+@pytest.mark.parametrize("M", [4, 200])
+@pytest.mark.parametrize("zp", [True, False])
+def test_gemm_one_hot_reproduces_decoded_weights(M, zp):
+    N, K, g = 264, 512, 32
+    W = workloads.adversarial_weight(N, K, g, seed=11)
+    packed = O.pack(W, g, zp)
+    wdq = O.dequant_packed(*packed, N, K, g, zp).astype(np.float16)
+    ks = np.random.default_rng(M).integers(0, K, size=M)
+    X = np.zeros((M, K), np.float16)
+    X[np.arange(M), ks] = 1
+    y = run_gemm(X, packed, N, K, g, zp)
+    assert np.array_equal(y.astype(np.float64), wdq[:, ks].T.astype(np.float64))
+
+
+@pytest.mark.parametrize("M", [4, 16, 64])
+@pytest.mark.parametrize("name,K,N", [workloads.LLAMA7B_BLOCK[0], workloads.LLAMA7B_BLOCK[4],
+                                      workloads.LLAMA7B_BLOCK[6]])
+def test_gemm_batched_decode_full_size(M, name, K, N):
+    layer = [n for n, _, _ in workloads.LLAMA7B_BLOCK].index(name)
+    W = workloads.weight(N, K, cfg=3, layer=layer)
+    X = workloads.activations(M, K, cfg=3, layer=layer)
+    check(M, N, K, 128, True, W, X, f"gemm {name} M={M}")
+
+
+@pytest.mark.parametrize("name,K,N", workloads.LLAMA70B_MLP)
+def test_gemm_prefill_70b_sampled(name, K, N):
+    """Full-size prefill GEMM (M=2048) launched as in the benchmark; the oracle
+    checks a random sample of output rows and columns."""
+    awq = G.lib()
+    M, g = 2048, 128
+    layer = 0 if K == 8192 else 1
+    W = workloads.weight(N, K, cfg=4, layer=layer)
+    X = workloads.activations(M, K, cfg=4, layer=layer)
+    w = G.dev_f16(W)
+    qw, sc, qz = awq.awq_pack(w, g, True)
+    del w
+    y = G.host_f16(awq.awq_gemm(G.dev_f16(X), qw, sc, qz, N, K, g, True))
+    rng = np.random.default_rng(4)
+    octets = rng.choice(N // 8, size=8, replace=False)
+    cols = (octets[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+    rows = np.sort(rng.choice(M, size=64, replace=False))
+    # the GPU-packed sample must equal the oracle's packing of the same rows
+    oq, os_, oz = O.pack(W[cols], g, True)
+    assert np.array_equal(G.host_u32(qw)[cols], oq)
+    assert np.array_equal(G.host_f16_bits(sc)[:, cols], os_)
+    y_ref, d = O.matmul_ref(X[rows], O.dequant_packed(oq, os_, oz, len(cols), K, g, True))
+    G.assert_within_tolerance(y[np.ix_(rows, cols)], y_ref, d, f"prefill {name}")
+
+
+def test_gemm_deterministic_and_stream():
+    M, N, K, g = 300, 1024, 2048, 128
+    W = workloads.weight(N, K, cfg=3, layer=99)
+    X = workloads.activations(M, K, cfg=3, layer=99)
+    packed = O.pack(W, g, True)
+    a = run_gemm(X, packed, N, K, g, True)
+    b = run_gemm(X, packed, N, K, g, True, stream=torch.cuda.Stream())
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    a = run_gemm(X[:16], packed, N, K, g, True)
+    b = run_gemm(X[:16], packed, N, K, g, True, stream=torch.cuda.Stream())
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
