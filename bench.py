@@ -1,0 +1,393 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 AWQ linear layer on one MI355X.
+
+Headline: single-token decode through the seven quantized linears (q, k, v, o
+projections 4096->4096, gate/up 4096->11008, down 11008->4096; group size
+128, zero points) of BLOCKS distinct Llama-7B-shaped decoder blocks.  One
+step = one token through all blocks = 7 * BLOCKS awq_gemv launches, replayed
+from a HIP graph.  Every block has its own copy of the packed weights, so a
+step streams ~3.3 GB and no launch is served from the 256 MB Infinity Cache.
+
+value  = algorithmic bytes of a step / step time, GB/s (whole job, one GPU)
+roofline = the GEMV kernel against 8 TB/s HBM; its average launch time comes
+         from HIP events around back-to-back launches on the launch stream.
+legs   = awq_pack, batched-decode awq_gemm (M = 4/16/64), prefill awq_gemm
+         (M = 2048, 70B-shaped MLP), GEMV vs GEMM at M = 1.
+cpu_baseline = the CPU oracle (decode + fp64 product) on one block, timed on
+         the host; a reported reference, not a target.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--blocks 32]
+                       [--legs all|none|<comma list>] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 matrix throughput (256 CU x 2.4 GHz x 4096 flop/clk)
+METRIC = "W4A16 GEMV achieved GB/s + GEMM TFLOPS (fraction of MI355X roofline)"
+
+
+def algorithmic_bytes(M, N, K, g, zp):
+    """Minimum HBM bytes of one layer call: 4-bit codes, fp16 scales, 4-bit
+    zero points, fp16 X in and fp16 Y out."""
+    G = K // g
+    return K * N // 2 + G * N * 2 + (G * N // 2 if zp else 0) + 2 * M * K + 2 * M * N
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--blocks", type=int, default=32)
+    ap.add_argument("--legs", default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def start(self):
+        self.a.record()
+
+    def stop_ms(self):
+        self.b.record()
+        self.b.synchronize()
+        return self.a.elapsed_time(self.b)
+
+
+def build_decode_block(torch, awq, workloads, blocks, g=128, zp=True):
+    """Pack one Llama-7B block on the GPU and replicate the packed buffers."""
+    layers = []
+    for li, (name, K, N) in enumerate(workloads.LLAMA7B_BLOCK):
+        W = workloads.weight(N, K, cfg=2, layer=li)
+        X = workloads.activations(1, K, cfg=2, layer=li)
+        w = torch.from_numpy(W).cuda()
+        qw, sc, qz = awq.awq_pack(w, g, zp)
+        layers.append(dict(name=name, K=K, N=N, W=W, X=X, w_dev=w, qw=qw, sc=sc, qz=qz,
+                           x=torch.from_numpy(X).cuda()))
+    torch.cuda.synchronize()
+    reps = []
+    for b in range(blocks):
+        rep = []
+        for L in layers:
+            rep.append(dict(qw=L["qw"].clone(), sc=L["sc"].clone(),
+                            qz=L["qz"].clone() if L["qz"] is not None else None,
+                            y=torch.empty((1, L["N"]), dtype=torch.float16, device="cuda")))
+        reps.append(rep)
+    torch.cuda.synchronize()
+    return layers, reps
+
+
+def decode_step(awq, layers, reps, g, zp):
+    for rep in reps:
+        for L, R in zip(layers, rep):
+            awq.awq_gemv(L["x"], R["qw"], R["sc"], R["qz"], L["N"], L["K"], g, zp, y=R["y"])
+
+
+def kernel_launch_times(torch, awq, layers, reps, g, zp, rounds=3):
+    """Average duration of one awq_gemv launch, from HIP events recorded on
+    the launch stream around every launch.  A long device-side sleep is queued
+    first so that all packets are enqueued before the GPU reaches them and the
+    events measure device time, not host enqueue gaps."""
+    per_layer = {L["name"]: [] for L in layers}
+    for _ in range(rounds):
+        evs = []
+        torch.cuda._sleep(50_000_000)
+        for rep in reps:
+            for L, R in zip(layers, rep):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                awq.awq_gemv(L["x"], R["qw"], R["sc"], R["qz"], L["N"], L["K"], g, zp, y=R["y"])
+                b.record()
+                evs.append((L["name"], a, b))
+        torch.cuda.synchronize()
+        for name, a, b in evs:
+            per_layer[name].append(a.elapsed_time(b) * 1e3)  # us
+    return per_layer
+
+
+def leg_pack(torch, awq, layers, g, zp, reps=5):
+    tm = Timer(torch)
+    total_w = sum(L["N"] * L["K"] for L in layers)
+    out_bytes = sum(algorithmic_bytes(0, L["N"], L["K"], g, zp) for L in layers)
+    in_bytes = 2 * total_w
+    for L in layers:  # warm
+        awq.awq_pack(L["w_dev"], g, zp, qweight=L["qw"], scales=L["sc"], qzeros=L["qz"])
+    torch.cuda.synchronize()
+    tm.start()
+    for _ in range(reps):
+        for L in layers:
+            awq.awq_pack(L["w_dev"], g, zp, qweight=L["qw"], scales=L["sc"], qzeros=L["qz"])
+    ms = tm.stop_ms() / reps
+    return {"what": "awq_pack of the 7 Llama-7B block linears (g=128, zero_point)", "us": round(ms * 1e3, 2),
+            "GB/s": round((in_bytes + out_bytes) / (ms * 1e-3) / 1e9, 1),
+            "bytes": in_bytes + out_bytes,
+            "frac_hbm": round((in_bytes + out_bytes) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+
+
+def time_graph(torch, fn, iters, warm=3):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    for _ in range(warm):
+        graph.replay()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    tm.start()
+    for _ in range(iters):
+        graph.replay()
+    return tm.stop_ms() / iters, graph
+
+
+def leg_batched_decode(torch, awq, workloads, g=128, zp=True, blocks=16, iters=20):
+    """M = 4 / 16 / 64 tokens through the 7 linears of `blocks` distinct blocks."""
+    out = {}
+    base = []
+    for li, (name, K, N) in enumerate(workloads.LLAMA7B_BLOCK):
+        W = torch.from_numpy(workloads.weight(N, K, cfg=3, layer=li)).cuda()
+        qw, sc, qz = awq.awq_pack(W, g, zp)
+        base.append((K, N, qw, sc, qz))
+    torch.cuda.synchronize()
+    reps = [[(K, N, qw.clone(), sc.clone(), qz.clone()) for (K, N, qw, sc, qz) in base] for _ in range(blocks)]
+    for M in (1, 4, 16, 64):
+        xs = [torch.from_numpy(workloads.activations(M, K, cfg=3, layer=li)).cuda()
+              for li, (_, K, _) in enumerate(workloads.LLAMA7B_BLOCK)]
+        ys = [torch.empty((M, N), dtype=torch.float16, device="cuda") for (_, _, N) in workloads.LLAMA7B_BLOCK]
+
+        def step():
+            for rep in reps:
+                for i, (K, N, qw, sc, qz) in enumerate(rep):
+                    awq.awq_gemm(xs[i], qw, sc, qz, N, K, g, zp, y=ys[i])
+
+        ms, _ = time_graph(torch, step, iters)
+        nbytes = blocks * sum(algorithmic_bytes(M, N, K, g, zp) for (_, K, N) in workloads.LLAMA7B_BLOCK)
+        flops = blocks * sum(2 * M * N * K for (_, K, N) in workloads.LLAMA7B_BLOCK)
+        out[f"M{M}"] = {"us_per_block": round(ms * 1e3 / blocks, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+                        "TFLOPS": round(flops / (ms * 1e-3) / 1e12, 2)}
+        if M == 1:
+            def step_gemv():
+                for rep in reps:
+                    for i, (K, N, qw, sc, qz) in enumerate(rep):
+                        awq.awq_gemv(xs[i], qw, sc, qz, N, K, g, zp, y=ys[i])
+
+            ms_v, _ = time_graph(torch, step_gemv, iters)
+            out["M1_gemv_vs_gemm"] = {"gemv_us_per_block": round(ms_v * 1e3 / blocks, 2),
+                                      "gemm_us_per_block": round(ms * 1e3 / blocks, 2),
+                                      "gemv_speedup": round(ms / ms_v, 3)}
+    return out
+
+
+def leg_prefill(torch, awq, workloads, g=128, zp=True, iters=5):
+    """M = 2048 prefill through the two 70B-shaped MLP linears (matrix-core bound)."""
+    out = {}
+    M = 2048
+    for li, (name, K, N) in enumerate(workloads.LLAMA70B_MLP):
+        W = torch.from_numpy(workloads.weight(N, K, cfg=4, layer=li)).cuda()
+        qw, sc, qz = awq.awq_pack(W, g, zp)
+        del W
+        X = torch.from_numpy(workloads.activations(M, K, cfg=4, layer=li)).cuda()
+        Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        for _ in range(2):
+            awq.awq_gemm(X, qw, sc, qz, N, K, g, zp, y=Y)
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        tm.start()
+        for _ in range(iters):
+            awq.awq_gemm(X, qw, sc, qz, N, K, g, zp, y=Y)
+        ms = tm.stop_ms() / iters
+        tf = 2 * M * N * K / (ms * 1e-3) / 1e12
+        out[name] = {"M": M, "K": K, "N": N, "us": round(ms * 1e3, 1), "TFLOPS": round(tf, 1),
+                     "frac_mfma_fp16": round(tf / FP16_MFMA_PEAK_TFLOPS, 3)}
+        del qw, sc, qz, X, Y
+        torch.cuda.empty_cache()
+    tot_f = sum(2 * M * N * K for (_, K, N) in workloads.LLAMA70B_MLP)
+    tot_us = sum(v["us"] for v in out.values())
+    out["both"] = {"TFLOPS": round(tot_f / (tot_us * 1e-6) / 1e12, 1),
+                   "frac_mfma_fp16": round(tot_f / (tot_us * 1e-6) / 1e12 / FP16_MFMA_PEAK_TFLOPS, 3)}
+    return out
+
+
+def cpu_baseline(layers, g, zp):
+    """The CPU oracle as it stands (unpack + fp64 decode + fp64 product) on the
+    seven linears of one block, M = 1."""
+    from oracle import awq_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        blas_threads = 1
+    packed = [O.pack(L["W"], g, zp) for L in layers]
+    t0 = time.perf_counter()
+    nbytes = 0
+    for L, (qw, sc, qz) in zip(layers, packed):
+        wdq = O.dequant_packed(qw, sc, qz, L["N"], L["K"], g, zp)
+        O.matmul_ref(L["X"], wdq)
+        nbytes += algorithmic_bytes(1, L["N"], L["K"], g, zp)
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": "one Llama-7B block (7 linears, M=1, g=128, zero_point): oracle unpack + fp64 decode + "
+                      "fp64 matmul (numpy; the product uses the BLAS threads, the decode one core)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        log("bench.py: the W4A16 layer benchmark is single-GPU; run with --gpus 1")
+        return 2
+
+    import torch
+
+    import bit_weight_only_awq_amd as awq
+    import workloads
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        return 1
+    awq.load_library()
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}))
+        return 0
+
+    g, zp = 128, True
+    log(f"building {args.blocks} decode blocks")
+    layers, reps = build_decode_block(torch, awq, workloads, args.blocks, g, zp)
+    step_bytes = args.blocks * sum(algorithmic_bytes(1, L["N"], L["K"], g, zp) for L in layers)
+    launches = args.blocks * len(layers)
+
+    def step():
+        decode_step(awq, layers, reps, g, zp)
+
+    log("capturing decode step")
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t_wall = time.perf_counter()
+    tm = Timer(torch)
+    tm.start()
+    for _ in range(args.steps):
+        graph.replay()
+    total_ms = tm.stop_ms()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    ms_per_step = total_ms / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    log("timing individual launches")
+    per_layer = kernel_launch_times(torch, awq, layers, reps, g, zp)
+    all_us = [u for v in per_layer.values() for u in v]
+    avg_us = sum(all_us) / len(all_us)
+    bytes_per_launch = step_bytes / launches
+    achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    layer_stats = {}
+    for L in layers:
+        us = per_layer[L["name"]]
+        mu = sum(us) / len(us)
+        b = algorithmic_bytes(1, L["N"], L["K"], g, zp)
+        layer_stats[L["name"]] = {"K": L["K"], "N": L["N"], "us": round(mu, 3),
+                                  "GB/s": round(b / (mu * 1e-6) / 1e9, 1)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": "llama7b_decode_gemv", "M": 1, "blocks": args.blocks,
+                   "layers": "q,k,v,o 4096->4096; gate,up 4096->11008; down 11008->4096",
+                   "group_size": g, "zero_point": zp, "launches_per_step": launches,
+                   "bytes_per_step": step_bytes, "timed_wall_s": round(wall_s, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_kernel", "avg_launch_us": round(avg_us, 3),
+                     "bytes_per_launch": int(bytes_per_launch), "per_layer": layer_stats},
+    }
+
+    legs = set(args.legs.split(",")) if args.legs not in ("all", "none") else (
+        {"pack", "batched", "prefill"} if args.legs == "all" else set())
+    out_legs = {}
+    if "pack" in legs:
+        log("leg: pack")
+        out_legs["pack"] = leg_pack(torch, awq, layers, g, zp)
+    del reps, graph
+    torch.cuda.empty_cache()
+    if "batched" in legs:
+        log("leg: batched decode")
+        out_legs["batched_decode_gemm"] = leg_batched_decode(torch, awq, workloads, g, zp)
+    if "prefill" in legs:
+        log("leg: prefill")
+        out_legs["prefill_gemm_70b"] = leg_prefill(torch, awq, workloads, g, zp)
+    if out_legs:
+        result["legs"] = out_legs
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cb = cpu_baseline(layers, g, zp)
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -105,8 +105,8 @@ def awq_gemm_workspace_bytes(M: int, N: int, K: int, group_size: int) -> int:
 def awq_pack(w: torch.Tensor, group_size: int = 128, zero_point: bool = True,
              qweight: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
              qzeros: Optional[torch.Tensor] = None):
-    """Quantize fp16 ``w`` [N, K] and return ``(qweight int32 [N, K/8], scales fp16 [K/g, N],
-    qzeros int32 [K/g, N/8] or None)``; the int32 tensors hold the ABI's uint32 words."""
+    """Quantize fp16 ``w`` [N, K] and return ``(qweight int32 [N, K/8], scales fp16 [N/8, K/g, 8],
+    qzeros int32 [N/8, K/g] or None)``; the int32 tensors hold the ABI's uint32 words."""
     lib = load_library()
     if w.dtype != torch.float16 or w.dim() != 2:
         raise ValueError("w must be a 2-D float16 tensor [N, K]")
@@ -116,9 +116,9 @@ def awq_pack(w: torch.Tensor, group_size: int = 128, zero_point: bool = True,
     if qweight is None:
         qweight = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
     if scales is None:
-        scales = torch.empty((G, N), dtype=torch.float16, device=dev)
+        scales = torch.empty((N // 8, G, 8), dtype=torch.float16, device=dev)
     if zero_point and qzeros is None:
-        qzeros = torch.empty((G, N // 8), dtype=torch.int32, device=dev)
+        qzeros = torch.empty((N // 8, G), dtype=torch.int32, device=dev)
     st = lib.awq_pack(_ptr(w), N, K, group_size, int(bool(zero_point)), _ptr(qweight), _ptr(scales),
                       _ptr(qzeros) if zero_point else None, _stream(w))
     _check(st, "awq_pack")

@@ -37,6 +37,22 @@ __device__ __forceinline__ ZeroBias zero_bias(uint32_t z) {
   return b;
 }
 
+// v_and_or_b32 (a & m) | o with both constants in VGPRs: a VOP3 instruction on
+// gfx9 cannot encode literal operands and reads at most one SGPR, so left to
+// itself the compiler splits the pattern into v_and_b32 + v_or_b32.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
+// Masks and fp16 bias patterns of decode_pairs, kept in registers.
+struct DecodeConsts {
+  uint32_t mask_lo, mask_hi, bias_1024, bias_64;
+  __device__ __forceinline__ DecodeConsts()
+      : mask_lo(0x000F000Fu), mask_hi(0x00F000F0u), bias_1024(0x64006400u), bias_64(0x54005400u) {}
+};
+
 // Decode one packed word into four half2 values (q - z), pair t holding
 // channels (2t, 2t+1).  Every step is exact:
 //   * a nibble in bits 0..3 OR-ed under the fp16 pattern 0x6400 (1024.0) reads
@@ -45,20 +61,21 @@ __device__ __forceinline__ ZeroBias zero_bias(uint32_t z) {
 //     spacing at 64 is 1/16 and the nibble sits 4 bits up);
 //   * subtracting 1024 + z or 64 + z leaves the small integer q - z, which
 //     fp16 represents exactly.
-__device__ __forceinline__ void decode_pairs(uint32_t w, const ZeroBias& b, half2_t d[4]) {
+__device__ __forceinline__ void decode_pairs(uint32_t w, const ZeroBias& b, const DecodeConsts& k, half2_t d[4]) {
   const uint32_t w8 = w >> 8;
-  d[0] = as_half2((w & 0x000F000Fu) | 0x64006400u) - b.hi;
-  d[1] = as_half2((w & 0x00F000F0u) | 0x54005400u) - b.lo;
-  d[2] = as_half2((w8 & 0x000F000Fu) | 0x64006400u) - b.hi;
-  d[3] = as_half2((w8 & 0x00F000F0u) | 0x54005400u) - b.lo;
+  d[0] = as_half2(and_or(w, k.mask_lo, k.bias_1024)) - b.hi;
+  d[1] = as_half2(and_or(w, k.mask_hi, k.bias_64)) - b.lo;
+  d[2] = as_half2(and_or(w8, k.mask_lo, k.bias_1024)) - b.hi;
+  d[3] = as_half2(and_or(w8, k.mask_hi, k.bias_64)) - b.lo;
 }
 
 // Decoded weights w' = (q - z) * s of one word as 8 halves in channel order,
 // each rounded once to fp16 (the product q - z times s is formed exactly and
 // rounded by the fp16 multiply).
-__device__ __forceinline__ half8_t decode_word_scaled(uint32_t w, const ZeroBias& b, half2_t s2) {
+__device__ __forceinline__ half8_t decode_word_scaled(uint32_t w, const ZeroBias& b, const DecodeConsts& k,
+                                                      half2_t s2) {
   half2_t d[4];
-  decode_pairs(w, b, d);
+  decode_pairs(w, b, k, d);
   half2_t p0 = d[0] * s2, p1 = d[1] * s2, p2 = d[2] * s2, p3 = d[3] * s2;
   half8_t r;
   r[0] = p0[0]; r[1] = p0[1];
@@ -75,6 +92,41 @@ __device__ __forceinline__ half2_t splat2(_Float16 h) {
   r[0] = h;
   r[1] = h;
   return r;
+}
+
+// Index of the scale of row n, group j in the row-octet-major scale array
+// [N/8][G][8], and of the zero-point word of that octet and group in [N/8][G].
+__host__ __device__ __forceinline__ size_t scale_index(int n, int j, int G) {
+  return ((size_t)(n >> 3) * G + j) * 8 + (n & 7);
+}
+__host__ __device__ __forceinline__ size_t zero_word_index(int n, int j, int G) { return (size_t)(n >> 3) * G + j; }
+
+// Sum R per-lane row partials over the 64 lanes of a wave.  Each halving step
+// exchanges half of the rows a lane still carries with the partner lane
+// (xor 32, 16, ...), so after log2(R) steps lane l carries one row,
+// l / (64 / R), summed over a group of lanes that the remaining xor steps
+// complete.  Returns that row's total; it is valid in every lane of the group.
+template <int R>
+__device__ __forceinline__ float wave_reduce_rows(float (&v)[R], int lane) {
+  int cnt = R;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    if (cnt > 1) {
+      const bool hi = lane & off;
+#pragma unroll
+      for (int i = 0; i < R / 2; ++i) {
+        if (i < cnt / 2) {
+          const float give = hi ? v[i] : v[i + cnt / 2];
+          const float keep = hi ? v[i + cnt / 2] : v[i];
+          v[i] = keep + __shfl_xor(give, off);
+        }
+      }
+      cnt >>= 1;
+    } else {
+      v[0] += __shfl_xor(v[0], off);
+    }
+  }
+  return v[0];
 }
 
 // The hardware dispatches workgroup b of a 1-D grid to XCD (b mod 8).  This

@@ -51,6 +51,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const u32x4* __res
   const int chunks = (K + 127) >> 7;  // 128-channel steps
   const size_t row_u4 = (size_t)(K >> 5);
   const size_t xrow_u4 = (size_t)(K >> 3);
+  const int G = K >> gshift;
+  const DecodeConsts kc;
 
   float4_t acc[MT][NT];
 #pragma unroll
@@ -73,8 +75,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const u32x4* __res
       _Float16 s = (_Float16)0.0f;
       uint32_t z = 8;
       if (ok) {
-        s = __builtin_bit_cast(_Float16, scales[(size_t)grp * N + n]);
-        if (ZP) z = (qzeros[(size_t)grp * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 15u;
+        s = __builtin_bit_cast(_Float16, scales[scale_index(n, grp, G)]);
+        if (ZP) z = (qzeros[zero_word_index(n, grp, G)] >> (4 * (n & 7))) & 15u;
       }
       s2[nt] = splat2(s);
       zb[nt] = zero_bias(z);
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const u32x4* __res
     for (int e = 0; e < 4; ++e) {
       half8_t bfrag[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) bfrag[nt] = decode_word_scaled(wv[nt][e], zb[nt], s2[nt]);
+      for (int nt = 0; nt < NT; ++nt) bfrag[nt] = decode_word_scaled(wv[nt][e], zb[nt], kc, s2[nt]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const half8_t afrag = as_half8(xv[mt][e]);
@@ -160,6 +162,8 @@ __global__ __launch_bounds__(256) void gemm_large_kernel(const u32x4* __restrict
   const int kw = K >> 3;
   const size_t xrow_u4 = (size_t)(K >> 3);
   const int nsteps = (K + BK - 1) / BK;
+  const int G = K >> gshift;
+  const DecodeConsts kc;
 
   // Global -> register staging.  X: thread t loads 8 x 16 B: rows (t >> 3) + 32 i,
   // channels 8 * (t & 7) .. +8 of the step.  W: thread t loads the 8 packed
@@ -192,8 +196,8 @@ __global__ __launch_bounds__(256) void gemm_large_kernel(const u32x4* __restrict
       uint32_t z = 8;
       if (nin && kk < K) {
         const int grp = kk >> gshift;
-        s = __builtin_bit_cast(_Float16, scales[(size_t)grp * N + n]);
-        if (ZP) z = (qzeros[(size_t)grp * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 15u;
+        s = __builtin_bit_cast(_Float16, scales[scale_index(n, grp, G)]);
+        if (ZP) z = (qzeros[zero_word_index(n, grp, G)] >> (4 * (n & 7))) & 15u;
       }
       sreg[hgrp] = s;
       zreg[hgrp] = z;
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(256) void gemm_large_kernel(const u32x4* __restrict
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int hgrp = i >> 2;  // words 0-3 and 4-7 may sit in different groups when g = 32
-      const half8_t v = decode_word_scaled(wreg[i], zero_bias(zreg[hgrp]), splat2(sreg[hgrp]));
+      const half8_t v = decode_word_scaled(wreg[i], zero_bias(zreg[hgrp]), kc, splat2(sreg[hgrp]));
       *reinterpret_cast<half8_t*>(wb + t * LDS_STRIDE + 8 * i) = v;
     }
   };

@@ -26,15 +26,16 @@ constexpr float kRangeFloor = 1e-5f;
 // n0 + (t >> 5); its lane l = t & 31 owns one packed word (8 channels) of each
 // 256-channel pass over the row.  A group of g channels is GW = g/8
 // consecutive lanes of the same row, reduced with butterfly shuffles (GW
-// divides 32, so a group never leaves its half-wave).  Scales and zero points
-// of the octet are staged in LDS and written 8 rows at a time.
+// divides 32, so a group never leaves its half-wave).  The octet's scales and
+// zero points are staged in LDS and stored as one 16-byte scale vector and one
+// zero-point word per group (row-octet-major layout).
 template <int GW, bool ZP>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restrict__ w, int N, int K,
                                                             uint32_t* __restrict__ qweight,
                                                             uint16_t* __restrict__ scales,
                                                             uint32_t* __restrict__ qzeros) {
   constexpr int kGroupsPerPass = 32 / GW;
-  __shared__ uint16_t s_lds[kGroupsPerPass][8];
+  __shared__ __attribute__((aligned(16))) uint16_t s_lds[kGroupsPerPass][8];
   __shared__ uint8_t z_lds[kGroupsPerPass][8];
 
   const int t = threadIdx.x;
@@ -102,16 +103,14 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restr
     }
     __syncthreads();
     const int gbase = w0 / GW;
-    if (t < kGroupsPerPass * 8) {
-      const int gi = t >> 3, rr = t & 7;
-      if (gbase + gi < ngroups) scales[(size_t)(gbase + gi) * N + n0 + rr] = s_lds[gi][rr];
-    }
-    if constexpr (ZP) {
-      if (t < kGroupsPerPass && gbase + t < ngroups) {
+    if (t < kGroupsPerPass && gbase + t < ngroups) {
+      const size_t octet_group = (size_t)blockIdx.x * ngroups + gbase + t;
+      *reinterpret_cast<u32x4*>(scales + octet_group * 8) = *reinterpret_cast<const u32x4*>(&s_lds[t][0]);
+      if constexpr (ZP) {
         uint32_t zw = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) zw |= (uint32_t)z_lds[t][i] << (4 * i);
-        qzeros[(size_t)(gbase + t) * (N >> 3) + (n0 >> 3)] = zw;
+        qzeros[octet_group] = zw;
       }
     }
     __syncthreads();
@@ -131,10 +130,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
        idx += (size_t)gridDim.x * blockDim.x) {
     const int n = (int)(idx / kw), j = (int)(idx % kw);
+    const int G = K >> gshift;
     const int grp = (j << 3) >> gshift;
-    const float s = (float)__builtin_bit_cast(_Float16, scales[(size_t)grp * N + n]);
+    const float s = (float)__builtin_bit_cast(_Float16, scales[scale_index(n, grp, G)]);
     int z = 8;
-    if (zero_point) z = (int)((qzeros[(size_t)grp * (N >> 3) + (n >> 3)] >> (4 * (n & 7))) & 15u);
+    if (zero_point) z = (int)((qzeros[zero_word_index(n, grp, G)] >> (4 * (n & 7))) & 15u);
     const uint32_t word = qweight[idx];
     half8_t out;
 #pragma unroll

@@ -33,9 +33,10 @@
  *            k = 8j .. 8j+7 of row n: channel 8j+c sits at bit
  *            16*(c & 1) + 4*(c >> 1), i.e. the low halfword holds the even
  *            channels 0,2,4,6 and the high halfword the odd ones 1,3,5,7.
- *   scales   fp16   [G][N]    scale of row n, group j at (j, n).
- *   qzeros   uint32 [G][N/8]  zero point of row 8c+i, group j in bits
- *            4i..4i+3 of word (j, c).  Only with zero_point != 0; the
+ *   scales   fp16   [N/8][G][8]  scale of row 8o+i, group j at (o, j, i):
+ *            the scales of one octet of rows are contiguous, 8 per group.
+ *   qzeros   uint32 [N/8][G]     zero point of row 8o+i, group j in bits
+ *            4i..4i+3 of word (o, j).  Only with zero_point != 0; the
  *            symmetric format has the implicit zero point 8 and no qzeros.
  */
 #ifndef AWQ_MI355X_AWQ_H
@@ -74,8 +75,8 @@ enum awq_status {
  *                                       the fp16-rounded scale s)
  *
  * w        in   fp16  [N][K], row-major.
- * qweight  out  uint32 [N][K/8]; scales out fp16 [G][N];
- * qzeros   out  uint32 [G][N/8] when zero_point != 0 (may be NULL otherwise).
+ * qweight  out  uint32 [N][K/8]; scales out fp16 [N/8][G][8];
+ * qzeros   out  uint32 [N/8][G] when zero_point != 0 (may be NULL otherwise).
  * Deterministic: the output is bit-identical for identical input.
  */
 int awq_pack(const void* w, int32_t N, int32_t K, int32_t group_size, int32_t zero_point,

@@ -38,8 +38,9 @@ of the repository):
    rounded fp32 division.
 5. Storage (our layout):
    qweight u32 [N][K/8]: bits 4i..4i+3 of word (n, j) hold the code of
-   k = 8j + PACK_ORDER[i]; scales fp16 [K/g][N]; qzeros u32 [K/g][N/8], bits
-   4i..4i+3 of word (j, c) hold the zero of row 8c + i.
+   k = 8j + PACK_ORDER[i]; scales fp16 [N/8][G][8]: element (o, j, i) is the
+   scale of row 8o + i, group j; qzeros u32 [N/8][G]: bits 4i..4i+3 of word
+   (o, j) hold the zero point of row 8o + i, group j.
 6. Y_ref = X . W'^T and D = |X| . |W'|^T in fp64.  Products of an fp16 x and
    an exact w' need at most 27 significant bits, so each product is exact in
    fp64; only the summation rounds.
@@ -161,36 +162,47 @@ def unpack_qweight(qweight: np.ndarray, K: int) -> np.ndarray:
 
 
 def pack_scales(s16: np.ndarray) -> np.ndarray:
-    """scales as raw fp16 bits, group-major: uint16 [G][N] (element (j, n) = s of row n, group j)."""
-    return np.ascontiguousarray(s16.T).view(np.uint16)
+    """scales as raw fp16 bits, row-octet major: uint16 [N/8][G][8]; element
+    (o, j, i) = scale of row 8o + i in group j."""
+    N, G = s16.shape
+    if N % 8:
+        raise ValueError("N must be a multiple of 8")
+    out = np.zeros((N // 8, G, 8), dtype=np.uint16)
+    bits = s16.view(np.uint16)
+    for i in range(8):
+        out[:, :, i] = bits[i::8, :]
+    return out
 
 
 def unpack_scales(scales_u16: np.ndarray) -> np.ndarray:
-    return np.ascontiguousarray(scales_u16.view(np.float16).T)
+    O8, G, _ = scales_u16.shape
+    s = np.zeros((O8 * 8, G), dtype=np.uint16)
+    for i in range(8):
+        s[i::8, :] = scales_u16[:, :, i]
+    return s.view(np.float16)
 
 
 def pack_qzeros(z: np.ndarray) -> np.ndarray:
-    """qzeros u32 [G][N/8]; nibble slot i of word (j, c) = z[8c + i, j] (natural order)."""
+    """qzeros u32 [N/8][G]; nibble slot i of word (o, j) = zero point of row 8o + i, group j."""
     N, G = z.shape
     if N % 8:
         raise ValueError("N must be a multiple of 8")
-    zt = z.T.astype(np.uint32)  # [G, N]
-    words = np.zeros((G, N // 8), dtype=np.uint32)
+    words = np.zeros((N // 8, G), dtype=np.uint32)
     for i in range(8):
-        words |= zt[:, i::8] << np.uint32(4 * i)
+        words |= z[i::8, :].astype(np.uint32) << np.uint32(4 * i)
     return words
 
 
 def unpack_qzeros(qzeros: np.ndarray, N: int) -> np.ndarray:
-    G = qzeros.shape[0]
-    zt = np.zeros((G, N), dtype=np.int64)
+    O8, G = qzeros.shape
+    z = np.zeros((O8 * 8, G), dtype=np.int64)
     for i in range(8):
-        zt[:, i::8] = ((qzeros >> np.uint32(4 * i)) & np.uint32(0xF)).astype(np.int64)
-    return np.ascontiguousarray(zt.T)
+        z[i::8, :] = ((qzeros >> np.uint32(4 * i)) & np.uint32(0xF)).astype(np.int64)
+    return z
 
 
 def pack(W16: np.ndarray, g: int, zero_point: bool):
-    """Quantize and store: ``(qweight u32 [N,K/8], scales u16 [G,N], qzeros u32 [G,N/8] | None)``."""
+    """Quantize and store: ``(qweight u32 [N,K/8], scales u16 [N/8,G,8], qzeros u32 [N/8,G] | None)``."""
     q, s16, z = quantize(W16, g, zero_point)
     qz = pack_qzeros(z) if zero_point else None
     return pack_qweight(q), pack_scales(s16), qz

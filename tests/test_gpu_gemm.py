@@ -110,7 +110,8 @@ def test_gemm_prefill_70b_sampled(name, K, N):
     # the GPU-packed sample must equal the oracle's packing of the same rows
     oq, os_, oz = O.pack(W[cols], g, True)
     assert np.array_equal(G.host_u32(qw)[cols], oq)
-    assert np.array_equal(G.host_f16_bits(sc)[:, cols], os_)
+    assert np.array_equal(G.host_f16_bits(sc)[octets], os_)
+    assert np.array_equal(G.host_u32(qz)[octets], oz)
     y_ref, d = O.matmul_ref(X[rows], O.dequant_packed(oq, os_, oz, len(cols), K, g, True))
     G.assert_within_tolerance(y[np.ix_(rows, cols)], y_ref, d, f"prefill {name}")
 

@@ -287,15 +287,18 @@ def check_layout(seed=6):
         assert np.array_equal(lo, q[:, 2 * t::8]) and np.array_equal(hi, q[:, 2 * t + 1::8])
     z = rng.integers(0, 16, size=(N, K // g))
     qz = O.pack_qzeros(z)
+    assert qz.shape == (N // 8, K // g)
     for n in range(N):
         for j in range(K // g):
-            assert (int(qz[j, n // 8]) >> (4 * (n % 8))) & 0xF == z[n, j]
+            assert (int(qz[n // 8, j]) >> (4 * (n % 8))) & 0xF == z[n, j]
     s = rng.standard_normal((N, K // g)).astype(np.float16)
     sc = O.pack_scales(s)
-    assert sc.shape == (K // g, N) and sc.dtype == np.uint16
+    assert sc.shape == (N // 8, K // g, 8) and sc.dtype == np.uint16
+    flat = sc.reshape(-1)
+    G = K // g
     for n in range(N):
-        for j in range(K // g):
-            assert sc[j, n] == s.view(np.uint16)[n, j]
+        for j in range(G):
+            assert flat[((n // 8) * G + j) * 8 + n % 8] == s.view(np.uint16)[n, j]
     q2, s2, z2 = O.unpack(words, sc, qz, N, K, g, True)
     assert np.array_equal(q2, q) and np.array_equal(z2, z)
     assert np.array_equal(s2.view(np.uint16), s.view(np.uint16))
