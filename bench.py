@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--summarize", nargs="+", metavar="DB",
+                    help="print a per-kernel summary of rocprofv3 result databases and exit")
+    ap.add_argument("--kernel-filter", default=None, help="with --summarize: only kernels whose name contains this")
     return ap.parse_args()
 
 
@@ -106,27 +109,44 @@ def decode_step(awq, layers, reps, g, zp):
             awq.awq_gemv(L["x"], R["qw"], R["sc"], R["qz"], L["N"], L["K"], g, zp, y=R["y"])
 
 
-def kernel_launch_times(torch, awq, layers, reps, g, zp, rounds=3):
-    """Average duration of one awq_gemv launch, from HIP events recorded on
-    the launch stream around every launch.  A long device-side sleep is queued
-    first so that all packets are enqueued before the GPU reaches them and the
-    events measure device time, not host enqueue gaps."""
-    per_layer = {L["name"]: [] for L in layers}
-    for _ in range(rounds):
-        evs = []
-        torch.cuda._sleep(50_000_000)
-        for rep in reps:
-            for L, R in zip(layers, rep):
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record()
+def per_layer_launch_times(torch, awq, layers, reps, g, zp, replays=20):
+    """Average device time of one awq_gemv launch per layer shape: a HIP graph
+    holds that layer's launches over all blocks back to back (distinct weight
+    copies), and HIP events on the launching stream bracket its replays."""
+    out = {}
+    for li, L in enumerate(layers):
+        def fn(li=li, L=L):
+            for rep in reps:
+                R = rep[li]
                 awq.awq_gemv(L["x"], R["qw"], R["sc"], R["qz"], L["N"], L["K"], g, zp, y=R["y"])
-                b.record()
-                evs.append((L["name"], a, b))
-        torch.cuda.synchronize()
-        for name, a, b in evs:
-            per_layer[name].append(a.elapsed_time(b) * 1e3)  # us
-    return per_layer
+
+        ms, _ = time_graph(torch, fn, replays)
+        out[L["name"]] = ms * 1e3 / len(reps)  # us per launch
+    return out
+
+
+def hbm_traffic(step_launches):
+    """Measured HBM bytes per GEMV launch from the committed counter summary,
+    if it was taken on the current kernel source; else None."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "gemv_llama7b_decode_traffic.txt")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for rel in rec["sources"].split():
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None, "kernel source changed since the counters were taken"
+    return int(rec["hbm_bytes_per_launch"]), rec["note"]
 
 
 def leg_pack(torch, awq, layers, g, zp, reps=5):
@@ -239,7 +259,7 @@ def leg_prefill(torch, awq, workloads, g=128, zp=True, iters=5):
     return out
 
 
-def cpu_baseline(layers, g, zp):
+def cpu_baseline(layers, g, zp, min_seconds=10.0, max_passes=40):
     """The CPU oracle as it stands (unpack + fp64 decode + fp64 product) on the
     seven linears of one block, M = 1."""
     from oracle import awq_oracle as O
@@ -253,19 +273,64 @@ def cpu_baseline(layers, g, zp):
     packed = [O.pack(L["W"], g, zp) for L in layers]
     t0 = time.perf_counter()
     nbytes = 0
-    for L, (qw, sc, qz) in zip(layers, packed):
-        wdq = O.dequant_packed(qw, sc, qz, L["N"], L["K"], g, zp)
-        O.matmul_ref(L["X"], wdq)
-        nbytes += algorithmic_bytes(1, L["N"], L["K"], g, zp)
+    passes = 0
+    while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
+        for L, (qw, sc, qz) in zip(layers, packed):
+            wdq = O.dequant_packed(qw, sc, qz, L["N"], L["K"], g, zp)
+            O.matmul_ref(L["X"], wdq)
+            nbytes += algorithmic_bytes(1, L["N"], L["K"], g, zp)
+        passes += 1
     dt = time.perf_counter() - t0
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": "one Llama-7B block (7 linears, M=1, g=128, zero_point): oracle unpack + fp64 decode + "
-                      "fp64 matmul (numpy; the product uses the BLAS threads, the decode one core)"}
+            "sample": f"{passes} passes over one Llama-7B block (7 linears, M=1, g=128, zero_point): oracle unpack + "
+                      "fp64 decode + fp64 matmul (numpy; the product runs on the BLAS threads, the decode on one core)"}
+
+
+def summarize(db_paths, name_filter=None):
+    """Per-kernel summary of rocprofv3 SQLite databases (kernel-trace and/or
+    --pmc runs): dispatch count, duration statistics and, when present, the
+    per-dispatch average of each collected counter.  Prints text."""
+    import sqlite3
+    import statistics
+
+    lines = []
+    for db in db_paths:
+        con = sqlite3.connect(db)
+        lines.append(f"# {db}")
+        rows = list(con.execute("select dispatch_id, name, duration, grid_x, workgroup_x from kernels"))
+        by = {}
+        for kid, name, dur, grid, wg in rows:
+            if name_filter and name_filter not in name:
+                continue
+            by.setdefault((name, grid, wg), []).append((kid, dur))
+        pmc = {}
+        try:
+            for kid, cname, val in con.execute("select dispatch_id, counter_name, counter_value from pmc_events"):
+                pmc.setdefault(kid, {}).setdefault(cname, 0.0)
+                pmc[kid][cname] += val
+        except sqlite3.Error:
+            pass
+        for (name, grid, wg), ds in sorted(by.items(), key=lambda kv: -sum(d for _, d in kv[1])):
+            durs = [d for _, d in ds]
+            line = (f"{name[:90]:90s} grid={grid:8d} wg={wg:4d} n={len(durs):5d} "
+                    f"avg_us={statistics.mean(durs) / 1e3:9.3f} med_us={statistics.median(durs) / 1e3:9.3f} "
+                    f"min_us={min(durs) / 1e3:9.3f}")
+            cnt = {}
+            for kid, _ in ds:
+                for c, v in pmc.get(kid, {}).items():
+                    cnt.setdefault(c, []).append(v)
+            for c, vs in sorted(cnt.items()):
+                line += f" {c}_avg={statistics.mean(vs):.1f}"
+            lines.append(line)
+    return "\n".join(lines)
 
 
 def main():
     args = parse()
+    if args.summarize:
+        print(summarize(args.summarize, args.kernel_filter))
+        return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -328,19 +393,20 @@ def main():
     ms_per_step = total_ms / args.steps
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    log("timing individual launches")
-    per_layer = kernel_launch_times(torch, awq, layers, reps, g, zp)
-    all_us = [u for v in per_layer.values() for u in v]
-    avg_us = sum(all_us) / len(all_us)
+    # the timed graph holds nothing but back-to-back GEMV launches, so its
+    # event-timed length per launch is the kernel's average launch duration
+    avg_us = ms_per_step * 1e3 / launches
     bytes_per_launch = step_bytes / launches
     achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    log("timing each layer shape")
+    per_layer = per_layer_launch_times(torch, awq, layers, reps, g, zp)
     layer_stats = {}
     for L in layers:
-        us = per_layer[L["name"]]
-        mu = sum(us) / len(us)
+        mu = per_layer[L["name"]]
         b = algorithmic_bytes(1, L["N"], L["K"], g, zp)
         layer_stats[L["name"]] = {"K": L["K"], "N": L["N"], "us": round(mu, 3),
                                   "GB/s": round(b / (mu * 1e-6) / 1e9, 1)}
+    traffic, traffic_note = hbm_traffic(launches)
 
     result = {
         "metric": METRIC,
@@ -360,7 +426,7 @@ def main():
                    "group_size": g, "zero_point": zp, "launches_per_step": launches,
                    "bytes_per_step": step_bytes, "timed_wall_s": round(wall_s, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_note": traffic_note,
                      "kernel": "gemv_kernel", "avg_launch_us": round(avg_us, 3),
                      "bytes_per_launch": int(bytes_per_launch), "per_layer": layer_stats},
     }
