@@ -145,89 +145,107 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int LDS_STRIDE = BK + 8;  // halves per LDS row (padding breaks bank conflicts)
 constexpr int TILE_HALVES = BM * LDS_STRIDE;
 
+// Buffer resource over `bytes` bytes at `base`: loads past the end return 0
+// and stores past the end are dropped, which masks the M and N edges of a tile.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// 2 x 4 waves of 128 x 64 outputs (two waves per SIMD, so one wave's decode and
+// LDS work overlaps the other's MFMAs).  Every global access goes through a
+// buffer resource based at the tile: a thread's 32-bit offsets are fixed for
+// the whole K loop and the step advances an SGPR offset, so the loop carries
+// no 64-bit address arithmetic, and rows past M or N read as zero.
 template <bool ZP>
-__global__ __launch_bounds__(256) void gemm_large_kernel(const u32x4* __restrict__ X,
+__global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restrict__ X,
                                                          const uint32_t* __restrict__ qweight,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint32_t* __restrict__ qzeros,
                                                          _Float16* __restrict__ Y, int M, int N, int K, int gshift,
                                                          int tiles_m) {
+  constexpr int THREADS = 512;
+  constexpr int WN = 64;                      // wave tile width (N)
+  constexpr int NB = WN / 32;                 // 32x32 MFMA tiles per wave along N
+  constexpr int XL = BM * (BK / 8) / THREADS; // 16-byte X loads per thread per step (4)
+  constexpr int XROWS = THREADS / (BK / 8);   // X rows covered by one load round (64)
   __shared__ __attribute__((aligned(16))) _Float16 lds[2][2][TILE_HALVES];  // [buffer][X | W'][row * 72 + k]
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
   const int tm = tile % tiles_m, tn = tile / tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int wm = (wave & 1) * 128, wn = (wave >> 1) * 128;
-  const int kw = K >> 3;
-  const size_t xrow_u4 = (size_t)(K >> 3);
+  const int rows_m = min(BM, M - m0), rows_n = min(BN, N - n0);  // rows_n is a multiple of 8
+  const int wm = (wave & 1) * 128, wn = (wave >> 1) * WN;
   const int nsteps = (K + BK - 1) / BK;
   const int G = K >> gshift;
   const DecodeConsts kc;
 
-  // Global -> register staging.  X: thread t loads 8 x 16 B: rows (t >> 3) + 32 i,
-  // channels 8 * (t & 7) .. +8 of the step.  W: thread t loads the 8 packed
-  // words (64 channels) of row n0 + t for the step.
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X + (size_t)m0 * K, (uint32_t)rows_m * K * 2);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(qweight + (size_t)n0 * (K >> 3), (uint32_t)rows_n * (K >> 1));
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(scales + scale_index(n0, 0, G), (uint32_t)(rows_n >> 3) * G * 16);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(ZP ? qzeros + zero_word_index(n0, 0, G) : qzeros,
+                                              ZP ? (uint32_t)(rows_n >> 3) * G * 4 : 0u);
+
+  // X: thread t loads XL x 16 B: rows (t >> 3) + XROWS i, channels 8 (t & 7) .. +8.
+  // W: thread t loads one 16-byte piece (32 channels) of row t >> 1, plus the
+  // scale and zero-point word of the piece's group.
   const int xr = t >> 3, xc = t & 7;
-  u32x4 xreg[8];
-  uint32_t wreg[8];
-  _Float16 sreg[2];
-  uint32_t zreg[2];
+  const int wr = t >> 1, piece = t & 1;
+  uint32_t xoff[XL];
+#pragma unroll
+  for (int i = 0; i < XL; ++i) xoff[i] = (uint32_t)(xr + XROWS * i) * K * 2 + xc * 16;
+  const uint32_t woff = (uint32_t)wr * (K >> 1) + piece * 16;
+  const bool g32 = gshift == 5;  // with g = 32 the two pieces of a step are two groups
+  const uint32_t soff = (uint32_t)(((wr >> 3) * G * 8 + (wr & 7)) * 2) + (g32 ? piece * 16 : 0);
+  const uint32_t zoff = (uint32_t)((wr >> 3) * G * 4) + (g32 ? piece * 4 : 0);
+  const int zshift = 4 * (wr & 7);
+
+  u32x4 xreg[XL];
+  u32x4 wreg;
+  uint32_t sraw, zraw;
 
   auto fetch = [&](int step) {
-    const int k0 = step * BK;
-    const bool kin = k0 + 8 * xc < K;
+    const int grp = (step * BK) >> gshift;  // group of piece 0
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int m = m0 + xr + 32 * i;
-      xreg[i] = (kin && m < M) ? X[(size_t)m * xrow_u4 + (k0 >> 3) + xc] : u32x4{0u, 0u, 0u, 0u};
-    }
-    const int n = n0 + t;
-    const bool nin = n < N;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = (k0 >> 3) + i;
-      wreg[i] = (nin && j < kw) ? qweight[(size_t)n * kw + j] : 0u;
-    }
-#pragma unroll
-    for (int hgrp = 0; hgrp < 2; ++hgrp) {
-      const int kk = k0 + 32 * hgrp;
-      _Float16 s = (_Float16)0.0f;
-      uint32_t z = 8;
-      if (nin && kk < K) {
-        const int grp = kk >> gshift;
-        s = __builtin_bit_cast(_Float16, scales[scale_index(n, grp, G)]);
-        if (ZP) z = (qzeros[zero_word_index(n, grp, G)] >> (4 * (n & 7))) & 15u;
-      }
-      sreg[hgrp] = s;
-      zreg[hgrp] = z;
-    }
+    for (int i = 0; i < XL; ++i) xreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], step * BK * 2, 0));
+    wreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, step * (BK / 2), 0));
+    sraw = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, grp * 16, 0);
+    zraw = ZP ? __builtin_amdgcn_raw_buffer_load_b32(rz, zoff, grp * 4, 0) : 0u;
   };
 
-  auto stash = [&](int buf) {
+  auto stash = [&](int buf, int step) {
     _Float16* xa = lds[buf][0];
     _Float16* wb = lds[buf][1];
+    const int k0 = step * BK;
+    if (k0 + BK <= K) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(xa + (xr + 32 * i) * LDS_STRIDE + 8 * xc) = xreg[i];
+      for (int i = 0; i < XL; ++i) *reinterpret_cast<u32x4*>(xa + (xr + XROWS * i) * LDS_STRIDE + 8 * xc) = xreg[i];
+    } else {  // the last step of a K that is not a multiple of 64: zero the channels past K
+      const bool ok = k0 + 8 * xc < K;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int hgrp = i >> 2;  // words 0-3 and 4-7 may sit in different groups when g = 32
-      const half8_t v = decode_word_scaled(wreg[i], zero_bias(zreg[hgrp]), kc, splat2(sreg[hgrp]));
-      *reinterpret_cast<half8_t*>(wb + t * LDS_STRIDE + 8 * i) = v;
+      for (int i = 0; i < XL; ++i)
+        *reinterpret_cast<u32x4*>(xa + (xr + XROWS * i) * LDS_STRIDE + 8 * xc) = ok ? xreg[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+    const uint32_t z = ZP ? ((zraw >> zshift) & 15u) : 8u;
+    const ZeroBias zb = zero_bias(z);
+    const half2_t s2 = splat2(__builtin_bit_cast(_Float16, (uint16_t)sraw));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const half8_t v = decode_word_scaled(wreg[e], zb, kc, s2);
+      *reinterpret_cast<half8_t*>(wb + wr * LDS_STRIDE + 32 * piece + 8 * e) = v;
     }
   };
 
-  float16_t acc[4][4];
+  float16_t acc[4][NB];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
   fetch(0);
-  stash(0);
+  stash(0, 0);
   __syncthreads();
 
   const int fi = lane & 31, fh = lane >> 5;  // fragment row and k-half of this lane
@@ -236,40 +254,50 @@ __global__ __launch_bounds__(256) void gemm_large_kernel(const u32x4* __restrict
     const bool more = step + 1 < nsteps;
     if (more) fetch(step + 1);
 
-    const _Float16* xa = lds[buf][0];
-    const _Float16* wb = lds[buf][1];
+    const _Float16* xa = lds[buf][0] + (wm + fi) * LDS_STRIDE + 8 * fh;
+    const _Float16* wb = lds[buf][1] + (wn + fi) * LDS_STRIDE + 8 * fh;
+    half8_t af[2][4], bf[2][NB];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) af[0][a] = *reinterpret_cast<const half8_t*>(xa + 32 * a * LDS_STRIDE);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) bf[0][b] = *reinterpret_cast<const half8_t*>(wb + 32 * b * LDS_STRIDE);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      half8_t af[4], bf[4];
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks + 1 < BK / 16) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          af[nxt][a] = *reinterpret_cast<const half8_t*>(xa + 32 * a * LDS_STRIDE + 16 * (ks + 1));
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          bf[nxt][b] = *reinterpret_cast<const half8_t*>(wb + 32 * b * LDS_STRIDE + 16 * (ks + 1));
+      }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
-        af[a] = *reinterpret_cast<const half8_t*>(xa + (wm + 32 * a + fi) * LDS_STRIDE + 16 * ks + 8 * fh);
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        bf[b] = *reinterpret_cast<const half8_t*>(wb + (wn + 32 * b + fi) * LDS_STRIDE + 16 * ks + 8 * fh);
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+        for (int b = 0; b < NB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][a], bf[cur][b], acc[a][b], 0, 0, 0);
     }
 
-    if (more) stash(buf ^ 1);
+    if (more) stash(buf ^ 1, step + 1);
     __syncthreads();
   }
 
   // 32x32 accumulator layout: lane l holds column l % 32 and, in register r,
-  // row 8 * (r / 4) + 4 * (l / 32) + r % 4.
+  // row 8 * (r / 4) + 4 * (l / 32) + r % 4.  Rows past M fall outside the
+  // buffer and are dropped; columns past N are skipped.
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y + (size_t)m0 * N, (uint32_t)rows_m * N * 2);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int n = n0 + wn + 32 * b + fi;
-      if (n >= N) continue;
+    for (int b = 0; b < NB; ++b) {
+      const int col = wn + 32 * b + fi;
+      if (col >= rows_n) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm + 32 * a + 8 * (r >> 2) + 4 * fh + (r & 3);
-        if (m < M) Y[(size_t)m * N + n] = (_Float16)acc[a][b][r];
+        const int row = wm + 32 * a + 8 * (r >> 2) + 4 * fh + (r & 3);
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)acc[a][b][r]), ry,
+                                              (uint32_t)(row * N + n0 + col) * 2, 0, 0);
       }
     }
 }
@@ -302,8 +330,8 @@ hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales,
     }
   }
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_large_kernel<ZP>), dim3(tiles_m * tiles_n), dim3(256), 0, stream, X, qweight, sc, qzeros, Y,
-                     M, N, K, gs, tiles_m);
+  hipLaunchKernelGGL((gemm_large_kernel<ZP>), dim3(tiles_m * tiles_n), dim3(512), 0, stream,
+                     static_cast<const _Float16*>(x), qweight, sc, qzeros, Y, M, N, K, gs, tiles_m);
   return hipGetLastError();
 }
 
