@@ -151,23 +151,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
-// 2 x 4 waves of 128 x 64 outputs (two waves per SIMD, so one wave's decode and
-// LDS work overlaps the other's MFMAs).  Every global access goes through a
-// buffer resource based at the tile: a thread's 32-bit offsets are fixed for
-// the whole K loop and the step advances an SGPR offset, so the loop carries
-// no 64-bit address arithmetic, and rows past M or N read as zero.
-template <bool ZP>
+// Registers holding one K step of global data on its way to LDS.
+struct StepRegs {
+  u32x4 x[4];    // X: 4 x 16 B
+  u32x4 w;       // 32 channels of packed weights
+  uint32_t s;    // raw fp16 scale (low half)
+  uint32_t z;    // zero-point word
+};
+
+// 2 x 4 waves of 128 x 64 outputs (two waves per SIMD).  Every global access
+// goes through a buffer resource based at the tile: a thread's 32-bit offsets
+// are fixed for the whole K loop and the step advances an SGPR offset, rows
+// past M or N read as zero and loads past the end of a tile return zero.
+// Software pipeline, one barrier per K step:
+//   iteration s: issue the global loads of step s + 2 (register set s & 1),
+//   multiply step s out of LDS buffer s & 1, and, interleaved with those
+//   MFMAs, decode step s + 1 (register set (s + 1) & 1) into LDS buffer
+//   (s + 1) & 1.
+// The loop has no branches: loads for steps past the end stay inside the
+// buffers (or return zero) and land in an LDS buffer no one reads again.
+template <bool ZP, bool KTAIL>
 __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restrict__ X,
                                                          const uint32_t* __restrict__ qweight,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint32_t* __restrict__ qzeros,
                                                          _Float16* __restrict__ Y, int M, int N, int K, int gshift,
                                                          int tiles_m) {
-  constexpr int THREADS = 512;
   constexpr int WN = 64;                      // wave tile width (N)
   constexpr int NB = WN / 32;                 // 32x32 MFMA tiles per wave along N
-  constexpr int XL = BM * (BK / 8) / THREADS; // 16-byte X loads per thread per step (4)
-  constexpr int XROWS = THREADS / (BK / 8);   // X rows covered by one load round (64)
+  constexpr int XROWS = 512 / (BK / 8);       // X rows covered by one load round (64)
   __shared__ __attribute__((aligned(16))) _Float16 lds[2][2][TILE_HALVES];  // [buffer][X | W'][row * 72 + k]
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -186,54 +198,43 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(ZP ? qzeros + zero_word_index(n0, 0, G) : qzeros,
                                               ZP ? (uint32_t)(rows_n >> 3) * G * 4 : 0u);
 
-  // X: thread t loads XL x 16 B: rows (t >> 3) + XROWS i, channels 8 (t & 7) .. +8.
+  // X: thread t loads 4 x 16 B: rows (t >> 3) + 64 i, channels 8 (t & 7) .. +8.
   // W: thread t loads one 16-byte piece (32 channels) of row t >> 1, plus the
   // scale and zero-point word of the piece's group.
   const int xr = t >> 3, xc = t & 7;
   const int wr = t >> 1, piece = t & 1;
-  uint32_t xoff[XL];
+  uint32_t xoff[4];
 #pragma unroll
-  for (int i = 0; i < XL; ++i) xoff[i] = (uint32_t)(xr + XROWS * i) * K * 2 + xc * 16;
+  for (int i = 0; i < 4; ++i) xoff[i] = (uint32_t)(xr + XROWS * i) * K * 2 + xc * 16;
   const uint32_t woff = (uint32_t)wr * (K >> 1) + piece * 16;
   const bool g32 = gshift == 5;  // with g = 32 the two pieces of a step are two groups
   const uint32_t soff = (uint32_t)(((wr >> 3) * G * 8 + (wr & 7)) * 2) + (g32 ? piece * 16 : 0);
   const uint32_t zoff = (uint32_t)((wr >> 3) * G * 4) + (g32 ? piece * 4 : 0);
   const int zshift = 4 * (wr & 7);
 
-  u32x4 xreg[XL];
-  u32x4 wreg;
-  uint32_t sraw, zraw;
-
-  auto fetch = [&](int step) {
+  auto fetch = [&](StepRegs& r, int step) {
     const int grp = (step * BK) >> gshift;  // group of piece 0
 #pragma unroll
-    for (int i = 0; i < XL; ++i) xreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], step * BK * 2, 0));
-    wreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, step * (BK / 2), 0));
-    sraw = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, grp * 16, 0);
-    zraw = ZP ? __builtin_amdgcn_raw_buffer_load_b32(rz, zoff, grp * 4, 0) : 0u;
+    for (int i = 0; i < 4; ++i)
+      r.x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], step * BK * 2, 0));
+    r.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, step * (BK / 2), 0));
+    r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, grp * 16, 0);
+    r.z = ZP ? __builtin_amdgcn_raw_buffer_load_b32(rz, zoff, grp * 4, 0) : 0u;
   };
 
-  auto stash = [&](int buf, int step) {
+  // One quarter (q = 0..3) of the LDS stash of a step: one X vector and one
+  // decoded packed word per thread.
+  auto stash_part = [&](const StepRegs& r, int buf, int step, int q) {
     _Float16* xa = lds[buf][0];
     _Float16* wb = lds[buf][1];
-    const int k0 = step * BK;
-    if (k0 + BK <= K) {
-#pragma unroll
-      for (int i = 0; i < XL; ++i) *reinterpret_cast<u32x4*>(xa + (xr + XROWS * i) * LDS_STRIDE + 8 * xc) = xreg[i];
-    } else {  // the last step of a K that is not a multiple of 64: zero the channels past K
-      const bool ok = k0 + 8 * xc < K;
-#pragma unroll
-      for (int i = 0; i < XL; ++i)
-        *reinterpret_cast<u32x4*>(xa + (xr + XROWS * i) * LDS_STRIDE + 8 * xc) = ok ? xreg[i] : u32x4{0u, 0u, 0u, 0u};
+    u32x4 xv = r.x[q];
+    if constexpr (KTAIL) {  // zero the channels past K of the last step
+      if (step * BK + 8 * xc >= K) xv = u32x4{0u, 0u, 0u, 0u};
     }
-    const uint32_t z = ZP ? ((zraw >> zshift) & 15u) : 8u;
-    const ZeroBias zb = zero_bias(z);
-    const half2_t s2 = splat2(__builtin_bit_cast(_Float16, (uint16_t)sraw));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const half8_t v = decode_word_scaled(wreg[e], zb, kc, s2);
-      *reinterpret_cast<half8_t*>(wb + wr * LDS_STRIDE + 32 * piece + 8 * e) = v;
-    }
+    *reinterpret_cast<u32x4*>(xa + (xr + XROWS * q) * LDS_STRIDE + 8 * xc) = xv;
+    const uint32_t z = ZP ? ((r.z >> zshift) & 15u) : 8u;
+    const half8_t v = decode_word_scaled(r.w[q], zero_bias(z), kc, splat2(__builtin_bit_cast(_Float16, (uint16_t)r.s)));
+    *reinterpret_cast<half8_t*>(wb + wr * LDS_STRIDE + 32 * piece + 8 * q) = v;
   };
 
   float16_t acc[4][NB];
@@ -244,16 +245,12 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  fetch(0);
-  stash(0, 0);
-  __syncthreads();
-
   const int fi = lane & 31, fh = lane >> 5;  // fragment row and k-half of this lane
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) fetch(step + 1);
 
+  // Multiply step `step` out of LDS buffer `buf`, and stash `nxt` (the data of
+  // step + 1) into the other buffer, a quarter after each 16-channel slice.
+  auto compute = [&](int step, const StepRegs& nxt) {
+    const int buf = step & 1;
     const _Float16* xa = lds[buf][0] + (wm + fi) * LDS_STRIDE + 8 * fh;
     const _Float16* wb = lds[buf][1] + (wn + fi) * LDS_STRIDE + 8 * fh;
     half8_t af[2][4], bf[2][NB];
@@ -263,25 +260,42 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
     for (int b = 0; b < NB; ++b) bf[0][b] = *reinterpret_cast<const half8_t*>(wb + 32 * b * LDS_STRIDE);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const int cur = ks & 1, nxt = cur ^ 1;
+      const int cur = ks & 1, nx = cur ^ 1;
       if (ks + 1 < BK / 16) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
-          af[nxt][a] = *reinterpret_cast<const half8_t*>(xa + 32 * a * LDS_STRIDE + 16 * (ks + 1));
+          af[nx][a] = *reinterpret_cast<const half8_t*>(xa + 32 * a * LDS_STRIDE + 16 * (ks + 1));
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-          bf[nxt][b] = *reinterpret_cast<const half8_t*>(wb + 32 * b * LDS_STRIDE + 16 * (ks + 1));
+          bf[nx][b] = *reinterpret_cast<const half8_t*>(wb + 32 * b * LDS_STRIDE + 16 * (ks + 1));
       }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < NB; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][a], bf[cur][b], acc[a][b], 0, 0, 0);
+      stash_part(nxt, buf ^ 1, step + 1, ks);
     }
+  };
 
-    if (more) stash(buf ^ 1, step + 1);
+  StepRegs ra, rb;
+  fetch(ra, 0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) stash_part(ra, 0, 0, q);
+  fetch(rb, 1);
+  __syncthreads();
+
+  // two steps per trip so that the register sets keep static names
+  int step = 0;
+  for (; step + 1 < nsteps; step += 2) {
+    fetch(ra, step + 2);
+    compute(step, rb);
+    __syncthreads();
+    fetch(rb, step + 3);
+    compute(step + 1, ra);
     __syncthreads();
   }
+  if (step < nsteps) compute(step, rb);
 
   // 32x32 accumulator layout: lane l holds column l % 32 and, in register r,
   // row 8 * (r / 4) + 4 * (l / 32) + r % 4.  Rows past M fall outside the
@@ -330,8 +344,12 @@ hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales,
     }
   }
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_large_kernel<ZP>), dim3(tiles_m * tiles_n), dim3(512), 0, stream,
-                     static_cast<const _Float16*>(x), qweight, sc, qzeros, Y, M, N, K, gs, tiles_m);
+  if (K % BK == 0)
+    hipLaunchKernelGGL((gemm_large_kernel<ZP, false>), dim3(tiles_m * tiles_n), dim3(512), 0, stream,
+                       static_cast<const _Float16*>(x), qweight, sc, qzeros, Y, M, N, K, gs, tiles_m);
+  else
+    hipLaunchKernelGGL((gemm_large_kernel<ZP, true>), dim3(tiles_m * tiles_n), dim3(512), 0, stream,
+                       static_cast<const _Float16*>(x), qweight, sc, qzeros, Y, M, N, K, gs, tiles_m);
   return hipGetLastError();
 }
 
