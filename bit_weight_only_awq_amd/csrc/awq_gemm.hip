@@ -38,103 +38,128 @@ int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 128 ? 7 : 8; }
 // --------------------------------------------------------------------------
 // Skinny M: weight-stream bound.
 // --------------------------------------------------------------------------
-template <int MT, int NT, int NW, bool ZP>
-__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const u32x4* __restrict__ X,
-                                                              const u32x4* __restrict__ qweight,
+// Buffer resource over `bytes` bytes at `base`: loads past the end return 0
+// and stores past the end are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past every resource: loads return 0
+
+// Global data of one 128-channel step for one lane: its 32 channels of one
+// weight row (4 packed words), the matching activations of its MT token rows,
+// and the row's raw scale and zero-point word for the lane's group.
+template <int MT>
+struct SkinnyStep {
+  u32x4 w;
+  u32x4 x[MT][4];
+  uint32_t s, z;
+};
+
+// One workgroup per 16 output rows, KS waves splitting K.  Wave w handles the
+// 128-channel steps w, w + KS, ... in rounds of SPW steps; the loads of round
+// r + 1 are in flight while round r is multiplied.  A lane (i, h) = (lane % 16,
+// lane / 16) loads the 32 channels 128 c + 32 h .. +32 of row n0 + i as one
+// 16-byte word, which is exactly its B operand for four 16x16x32 MFMAs, and
+// the same channels of token rows 16 mt + i as the A operands.  The waves'
+// partial sums meet in LDS and are added in wave order (deterministic).
+template <int MT, int KS, int SPW, bool ZP>
+__global__ __launch_bounds__(KS * 64) void gemm_skinny_kernel(const _Float16* __restrict__ X,
+                                                              const uint32_t* __restrict__ qweight,
                                                               const uint16_t* __restrict__ scales,
                                                               const uint32_t* __restrict__ qzeros,
                                                               _Float16* __restrict__ Y, int M, int N, int K,
                                                               int gshift) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int li = lane & 15, lh = lane >> 4;
-  const int n0 = blockIdx.x * (16 * NT);
-  const int chunks = (K + 127) >> 7;  // 128-channel steps
-  const size_t row_u4 = (size_t)(K >> 5);
-  const size_t xrow_u4 = (size_t)(K >> 3);
+  const int n0 = blockIdx.x * 16;
+  const int nrows = min(16, N - n0);  // 16, or 8 at the end of an N that is not a multiple of 16
+  const int steps = (K + 127) >> 7;
   const int G = K >> gshift;
   const DecodeConsts kc;
 
-  float4_t acc[MT][NT];
-#pragma unroll
-  for (int a = 0; a < MT; ++a)
-#pragma unroll
-    for (int b = 0; b < NT; ++b) acc[a][b] = float4_t{0.f, 0.f, 0.f, 0.f};
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(qweight + (size_t)n0 * (K >> 3), (uint32_t)nrows * (K >> 1));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (uint32_t)M * K * 2);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(scales + scale_index(n0, 0, G), (uint32_t)(nrows >> 3) * G * 16);
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(ZP ? qzeros + zero_word_index(n0, 0, G) : qzeros,
+                                              ZP ? (uint32_t)(nrows >> 3) * G * 4 : 0u);
+  const uint32_t wbase = (uint32_t)li * (K >> 1) + lh * 16;
+  const uint32_t sbase = (uint32_t)(((li >> 3) * G * 8 + (li & 7)) * 2);
+  const uint32_t zbase = (uint32_t)((li >> 3) * G * 4);
+  const int zshift = 4 * (li & 7);
 
-  for (int c = wave; c < chunks; c += NW) {
-    const int k0 = (c << 7) + (lh << 5);  // this lane's 32 channels: k0 .. k0+31
-    const bool kin = k0 < K;
-    u32x4 wv[NT];
-    half2_t s2[NT];
-    ZeroBias zb[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = n0 + 16 * nt + li;
-      const bool ok = kin && n < N;
-      wv[nt] = ok ? qweight[(size_t)n * row_u4 + (k0 >> 5)] : u32x4{0u, 0u, 0u, 0u};
-      const int grp = k0 >> gshift;
-      _Float16 s = (_Float16)0.0f;
-      uint32_t z = 8;
-      if (ok) {
-        s = __builtin_bit_cast(_Float16, scales[scale_index(n, grp, G)]);
-        if (ZP) z = (qzeros[zero_word_index(n, grp, G)] >> (4 * (n & 7))) & 15u;
-      }
-      s2[nt] = splat2(s);
-      zb[nt] = zero_bias(z);
-    }
-    u32x4 xv[MT][4];
+  auto fetch = [&](SkinnyStep<MT>& r, int c) {
+    const int k0 = (c << 7) + (lh << 5);  // first channel of the lane's 32
+    const bool kin = c < steps && k0 < K;
+    const int grp = k0 >> gshift;
+    r.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, kin ? wbase + c * 64 : kOutOfRange, 0, 0));
+    r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, kin ? sbase + grp * 16 : kOutOfRange, 0, 0);
+    r.z = ZP ? __builtin_amdgcn_raw_buffer_load_b32(rz, kin ? zbase + grp * 4 : kOutOfRange, 0, 0) : 0u;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int m = 16 * mt + li;
-      const bool ok = kin && m < M;
+      // token rows past M lie past the end of the X resource and read as 0
+      const uint32_t xo = kin ? ((uint32_t)(16 * mt + li) * K + k0) * 2 : kOutOfRange;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        xv[mt][e] = ok ? X[(size_t)m * xrow_u4 + (k0 >> 3) + e] : u32x4{0u, 0u, 0u, 0u};
+        r.x[mt][e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xo, e * 16, 0));
     }
+  };
+
+  float4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const SkinnyStep<MT>& r) {
+    const uint32_t z = ZP ? ((r.z >> zshift) & 15u) : 8u;
+    const ZeroBias zb = zero_bias(z);
+    const half2_t s2 = splat2(__builtin_bit_cast(_Float16, (uint16_t)r.s));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      half8_t bfrag[NT];
+      const half8_t b = decode_word_scaled(r.w[e], zb, kc, s2);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) bfrag[nt] = decode_word_scaled(wv[nt][e], zb[nt], kc, s2[nt]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const half8_t afrag = as_half8(xv[mt][e]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(afrag, bfrag[nt], acc[mt][nt], 0, 0, 0);
-      }
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(r.x[mt][e]), b, acc[mt], 0, 0, 0);
     }
+  };
+
+  // rounds of SPW steps, double-buffered
+  const int per_round = KS * SPW;
+  const int rounds = (steps + per_round - 1) / per_round;
+  SkinnyStep<MT> ra[SPW], rb[SPW];
+#pragma unroll
+  for (int u = 0; u < SPW; ++u) fetch(ra[u], wave + KS * u);
+  int r = 0;
+  for (; r + 1 < rounds; r += 2) {
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) fetch(rb[u], wave + KS * (SPW * (r + 1) + u));
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) compute(ra[u]);
+    if (r + 2 < rounds) {
+#pragma unroll
+      for (int u = 0; u < SPW; ++u) fetch(ra[u], wave + KS * (SPW * (r + 2) + u));
+    }
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) compute(rb[u]);
+  }
+  if (r < rounds) {
+#pragma unroll
+    for (int u = 0; u < SPW; ++u) compute(ra[u]);
   }
 
-  // 16x16 accumulator layout: lane (li, lh) holds column li, rows 4*lh + r.
-  if constexpr (NW == 1) {
+  // 16x16 accumulator layout: lane (li, lh) holds column li, rows 4 lh + j.
+  __shared__ float red[KS][MT * 4][64];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+    for (int j = 0; j < 4; ++j) red[wave][mt * 4 + j][lane] = acc[mt][j];
+  __syncthreads();
+  for (int o = t; o < MT * 4 * 64; o += KS * 64) {
+    const int idx = o >> 6, ln = o & 63;
+    float sum = red[0][idx][ln];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = 16 * mt + 4 * lh + r, n = n0 + 16 * nt + li;
-          if (m < M && n < N) Y[(size_t)m * N + n] = (_Float16)acc[mt][nt][r];
-        }
-  } else {
-    constexpr int kVals = MT * NT * 4;
-    __shared__ float red[NW][kVals][64];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][(mt * NT + nt) * 4 + r][lane] = acc[mt][nt][r];
-    __syncthreads();
-    for (int o = t; o < kVals * 64; o += NW * 64) {
-      const int idx = o >> 6, ln = o & 63;
-      float sum = red[0][idx][ln];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) sum += red[w][idx][ln];
-      const int mt = idx / (NT * 4), nt = (idx >> 2) % NT, r = idx & 3;
-      const int m = 16 * mt + 4 * (ln >> 4) + r, n = n0 + 16 * nt + (ln & 15);
-      if (m < M && n < N) Y[(size_t)m * N + n] = (_Float16)sum;
-    }
+    for (int w = 1; w < KS; ++w) sum += red[w][idx][ln];
+    const int m = 16 * (idx >> 2) + 4 * (ln >> 4) + (idx & 3), n = n0 + (ln & 15);
+    if (m < M && n < N) Y[(size_t)m * N + n] = (_Float16)sum;
   }
 }
 
@@ -144,12 +169,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(const u32x4* __res
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int LDS_STRIDE = BK + 8;  // halves per LDS row (padding breaks bank conflicts)
 constexpr int TILE_HALVES = BM * LDS_STRIDE;
-
-// Buffer resource over `bytes` bytes at `base`: loads past the end return 0
-// and stores past the end are dropped, which masks the M and N edges of a tile.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
 
 // Registers holding one K step of global data on its way to LDS.
 struct StepRegs {
@@ -316,31 +335,27 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
     }
 }
 
-template <int MT, bool ZP>
-hipError_t launch_skinny(const u32x4* X, const u32x4* qw, const uint16_t* sc, const uint32_t* qz, _Float16* Y, int M,
+template <int MT, int KS, int SPW, bool ZP>
+hipError_t launch_skinny(const void* x, const uint32_t* qw, const uint16_t* sc, const uint32_t* qz, _Float16* Y, int M,
                          int N, int K, int gs, hipStream_t stream) {
-  constexpr int NT = MT >= 3 ? 1 : 2;
-  constexpr int NW = 4;
-  const dim3 grid((N + 16 * NT - 1) / (16 * NT));
-  hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, NW, ZP>), grid, dim3(NW * 64), 0, stream, X, qw, sc, qz, Y, M, N, K,
-                     gs);
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT, KS, SPW, ZP>), dim3((N + 15) / 16), dim3(KS * 64), 0, stream,
+                     static_cast<const _Float16*>(x), qw, sc, qz, Y, M, N, K, gs);
   return hipGetLastError();
 }
 
 template <bool ZP>
 hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* y,
                      int M, int N, int K, int group_size, hipStream_t stream) {
-  const u32x4* X = static_cast<const u32x4*>(x);
   const uint16_t* sc = static_cast<const uint16_t*>(scales);
   _Float16* Y = static_cast<_Float16*>(y);
   const int gs = log2_group(group_size);
   if (M <= 64) {
-    const u32x4* qw = reinterpret_cast<const u32x4*>(qweight);
+    // up to 32 tokens: 8 waves of 2 steps per round; more tokens: 8 waves of 1 step
     switch ((M + 15) / 16) {
-      case 1: return launch_skinny<1, ZP>(X, qw, sc, qzeros, Y, M, N, K, gs, stream);
-      case 2: return launch_skinny<2, ZP>(X, qw, sc, qzeros, Y, M, N, K, gs, stream);
-      case 3: return launch_skinny<3, ZP>(X, qw, sc, qzeros, Y, M, N, K, gs, stream);
-      default: return launch_skinny<4, ZP>(X, qw, sc, qzeros, Y, M, N, K, gs, stream);
+      case 1: return launch_skinny<1, 8, 2, ZP>(x, qweight, sc, qzeros, Y, M, N, K, gs, stream);
+      case 2: return launch_skinny<2, 8, 2, ZP>(x, qweight, sc, qzeros, Y, M, N, K, gs, stream);
+      case 3: return launch_skinny<3, 8, 1, ZP>(x, qweight, sc, qzeros, Y, M, N, K, gs, stream);
+      default: return launch_skinny<4, 8, 1, ZP>(x, qweight, sc, qzeros, Y, M, N, K, gs, stream);
     }
   }
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
