@@ -167,45 +167,53 @@ __global__ __launch_bounds__(KS * 64) void gemm_skinny_kernel(const _Float16* __
 // Large M: matrix-core bound.
 // --------------------------------------------------------------------------
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LDS_STRIDE = BK + 8;  // halves per LDS row (padding breaks bank conflicts)
-constexpr int TILE_HALVES = BM * LDS_STRIDE;
+constexpr int TILE_BYTES = BM * BK * 2;  // one 256 x 64 fp16 tile in LDS (32 KiB)
 
-// Registers holding one K step of global data on its way to LDS.
+// LDS layout of a 256 x 64 fp16 tile: row r occupies bytes 128 r .. 128 r + 127,
+// and its 16-byte chunk c (channels 8 c .. 8 c + 7) sits in slot
+// c ^ ((r >> 1) & 7).  The LDS serves 16 lanes x 16 bytes (all 64 banks) per
+// cycle; 16 consecutive rows read at the same logical chunk land in 16
+// different bank groups (even and odd rows fill the two 128-byte halves), so
+// the MFMA fragment reads are conflict-free without padding, and a 1 KiB run
+// of slots is exactly what one buffer-to-LDS load of 64 lanes x 16 bytes writes.
+__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+__device__ __forceinline__ uint32_t swz(int row, int chunk) { return (uint32_t)(row * 128 + 16 * swz_chunk(row, chunk)); }
+
+// Registers holding one K step of packed weights on their way to LDS.
 struct StepRegs {
-  u32x4 x[4];    // X: 4 x 16 B
   u32x4 w;       // 32 channels of packed weights
   uint32_t s;    // raw fp16 scale (low half)
   uint32_t z;    // zero-point word
 };
 
-// 2 x 4 waves of 128 x 64 outputs (two waves per SIMD).  Every global access
-// goes through a buffer resource based at the tile: a thread's 32-bit offsets
-// are fixed for the whole K loop and the step advances an SGPR offset, rows
-// past M or N read as zero and loads past the end of a tile return zero.
+// 2 x 4 waves of 128 x (32 NB) outputs (two waves per SIMD); tile width
+// 128 NB.  Every global access goes through a buffer resource based at the
+// tile: a thread's 32-bit offsets are fixed for the whole K loop and the step
+// advances an SGPR offset; rows past M or N read as zero.
 // Software pipeline, one barrier per K step:
-//   iteration s: issue the global loads of step s + 2 (register set s & 1),
-//   multiply step s out of LDS buffer s & 1, and, interleaved with those
-//   MFMAs, decode step s + 1 (register set (s + 1) & 1) into LDS buffer
-//   (s + 1) & 1.
+//   iteration s: load the X tile of step s + 1 straight into LDS buffer
+//   (s + 1) & 1 (buffer-to-LDS DMA, no registers), issue the packed-weight
+//   loads of step s + 2 into registers, multiply step s out of buffer s & 1
+//   and, interleaved with those MFMAs, decode step s + 1's weights into
+//   buffer (s + 1) & 1.
 // The loop has no branches: loads for steps past the end stay inside the
 // buffers (or return zero) and land in an LDS buffer no one reads again.
-template <bool ZP, bool KTAIL>
+template <bool ZP, bool KTAIL, int NB>
 __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restrict__ X,
                                                          const uint32_t* __restrict__ qweight,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint32_t* __restrict__ qzeros,
                                                          _Float16* __restrict__ Y, int M, int N, int K, int gshift,
-                                                         int tiles_m) {
-  constexpr int WN = 64;                      // wave tile width (N)
-  constexpr int NB = WN / 32;                 // 32x32 MFMA tiles per wave along N
-  constexpr int XROWS = 512 / (BK / 8);       // X rows covered by one load round (64)
-  __shared__ __attribute__((aligned(16))) _Float16 lds[2][2][TILE_HALVES];  // [buffer][X | W'][row * 72 + k]
+                                                         int tiles_m, int ldy) {
+  constexpr int WN = 32 * NB;                 // wave tile width (N): 64, or 32 for half-width tiles
+  constexpr int TBN = 4 * WN;                 // workgroup tile width: 256 or 128
+  __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE_BYTES];  // [buffer][X | W']
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
   const int tm = tile % tiles_m, tn = tile / tiles_m;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int rows_m = min(BM, M - m0), rows_n = min(BN, N - n0);  // rows_n is a multiple of 8
+  const int m0 = tm * BM, n0 = tn * TBN;
+  const int rows_m = min(BM, M - m0), rows_n = min(TBN, N - n0);  // rows_n is a multiple of 8
   const int wm = (wave & 1) * 128, wn = (wave >> 1) * WN;
   const int nsteps = (K + BK - 1) / BK;
   const int G = K >> gshift;
@@ -217,43 +225,54 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(ZP ? qzeros + zero_word_index(n0, 0, G) : qzeros,
                                               ZP ? (uint32_t)(rows_n >> 3) * G * 4 : 0u);
 
-  // X: thread t loads 4 x 16 B: rows (t >> 3) + 64 i, channels 8 (t & 7) .. +8.
-  // W: thread t loads one 16-byte piece (32 channels) of row t >> 1, plus the
-  // scale and zero-point word of the piece's group.
-  const int xr = t >> 3, xc = t & 7;
-  const int wr = t >> 1, piece = t & 1;
+  // X: wave w fills LDS rows 32 w .. 32 w + 31 with 4 loads of 8 rows x 128 B;
+  // lane l of load j writes slot l of that 1 KiB run: row 32 w + 8 j + l / 8,
+  // physical chunk l % 8, which holds the logical chunk that swizzles there
+  // (the swizzle is an involution).
+  int xchunk[4];
   uint32_t xoff[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) xoff[i] = (uint32_t)(xr + XROWS * i) * K * 2 + xc * 16;
+  for (int j = 0; j < 4; ++j) {
+    const int row = 32 * wave + 8 * j + (lane >> 3);
+    xchunk[j] = swz_chunk(row, lane & 7);
+    xoff[j] = (uint32_t)row * K * 2 + xchunk[j] * 16;
+  }
+
+  // W: thread t loads one 16-byte piece (32 channels) of row t >> 1, plus the
+  // scale and zero-point word of the piece's group (threads past the tile's
+  // 2 * TBN pieces of a half-width tile read rows past its end: zeros, unused).
+  const int wr = t >> 1, piece = t & 1;
   const uint32_t woff = (uint32_t)wr * (K >> 1) + piece * 16;
   const bool g32 = gshift == 5;  // with g = 32 the two pieces of a step are two groups
   const uint32_t soff = (uint32_t)(((wr >> 3) * G * 8 + (wr & 7)) * 2) + (g32 ? piece * 16 : 0);
   const uint32_t zoff = (uint32_t)((wr >> 3) * G * 4) + (g32 ? piece * 4 : 0);
   const int zshift = 4 * (wr & 7);
 
-  auto fetch = [&](StepRegs& r, int step) {
-    const int grp = (step * BK) >> gshift;  // group of piece 0
+  auto load_x = [&](int step) {
+    char* dst = lds[step & 1][0] + wave * 4096;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      r.x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], step * BK * 2, 0));
+    for (int j = 0; j < 4; ++j) {
+      uint32_t off = xoff[j];
+      if constexpr (KTAIL) {  // channels past K of the last step load as zero
+        if (step * BK + 8 * xchunk[j] >= K) off = kOutOfRange;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16, off,
+                                               step * BK * 2, 0, 0);
+    }
+  };
+
+  auto fetch_w = [&](StepRegs& r, int step) {
+    const int grp = (step * BK) >> gshift;  // group of piece 0
     r.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, step * (BK / 2), 0));
     r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, grp * 16, 0);
     r.z = ZP ? __builtin_amdgcn_raw_buffer_load_b32(rz, zoff, grp * 4, 0) : 0u;
   };
 
-  // One quarter (q = 0..3) of the LDS stash of a step: one X vector and one
-  // decoded packed word per thread.
-  auto stash_part = [&](const StepRegs& r, int buf, int step, int q) {
-    _Float16* xa = lds[buf][0];
-    _Float16* wb = lds[buf][1];
-    u32x4 xv = r.x[q];
-    if constexpr (KTAIL) {  // zero the channels past K of the last step
-      if (step * BK + 8 * xc >= K) xv = u32x4{0u, 0u, 0u, 0u};
-    }
-    *reinterpret_cast<u32x4*>(xa + (xr + XROWS * q) * LDS_STRIDE + 8 * xc) = xv;
+  // One quarter (q = 0..3) of a step's W' stash: one decoded word per thread.
+  auto stash_part = [&](const StepRegs& r, int buf, int q) {
     const uint32_t z = ZP ? ((r.z >> zshift) & 15u) : 8u;
     const half8_t v = decode_word_scaled(r.w[q], zero_bias(z), kc, splat2(__builtin_bit_cast(_Float16, (uint16_t)r.s)));
-    *reinterpret_cast<half8_t*>(wb + wr * LDS_STRIDE + 32 * piece + 8 * q) = v;
+    if (TBN == BN || wr < TBN) *reinterpret_cast<half8_t*>(lds[buf][1] + swz(wr, 4 * piece + q)) = v;
   };
 
   float16_t acc[4][NB];
@@ -265,52 +284,55 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
   const int fi = lane & 31, fh = lane >> 5;  // fragment row and k-half of this lane
+  const int fsw = (fi >> 1) & 7;             // swizzle of the fragment rows (tile row bases are multiples of 32)
 
-  // Multiply step `step` out of LDS buffer `buf`, and stash `nxt` (the data of
-  // step + 1) into the other buffer, a quarter after each 16-channel slice.
+  // Multiply step `step` out of LDS buffer step & 1 and stash `nxt` (packed
+  // weights of step + 1) into the other buffer, a quarter per 16-channel slice.
   auto compute = [&](int step, const StepRegs& nxt) {
     const int buf = step & 1;
-    const _Float16* xa = lds[buf][0] + (wm + fi) * LDS_STRIDE + 8 * fh;
-    const _Float16* wb = lds[buf][1] + (wn + fi) * LDS_STRIDE + 8 * fh;
+    const char* xa = lds[buf][0] + (wm + fi) * 128;
+    const char* wb = lds[buf][1] + (wn + fi) * 128;
     half8_t af[2][4], bf[2][NB];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) af[0][a] = *reinterpret_cast<const half8_t*>(xa + 32 * a * LDS_STRIDE);
+    for (int a = 0; a < 4; ++a) af[0][a] = *reinterpret_cast<const half8_t*>(xa + 32 * 128 * a + 16 * (fh ^ fsw));
 #pragma unroll
-    for (int b = 0; b < NB; ++b) bf[0][b] = *reinterpret_cast<const half8_t*>(wb + 32 * b * LDS_STRIDE);
+    for (int b = 0; b < NB; ++b) bf[0][b] = *reinterpret_cast<const half8_t*>(wb + 32 * 128 * b + 16 * (fh ^ fsw));
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int cur = ks & 1, nx = cur ^ 1;
       if (ks + 1 < BK / 16) {
+        const int slot = 16 * ((2 * (ks + 1) + fh) ^ fsw);
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-          af[nx][a] = *reinterpret_cast<const half8_t*>(xa + 32 * a * LDS_STRIDE + 16 * (ks + 1));
+        for (int a = 0; a < 4; ++a) af[nx][a] = *reinterpret_cast<const half8_t*>(xa + 32 * 128 * a + slot);
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-          bf[nx][b] = *reinterpret_cast<const half8_t*>(wb + 32 * b * LDS_STRIDE + 16 * (ks + 1));
+        for (int b = 0; b < NB; ++b) bf[nx][b] = *reinterpret_cast<const half8_t*>(wb + 32 * 128 * b + slot);
       }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < NB; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][a], bf[cur][b], acc[a][b], 0, 0, 0);
-      stash_part(nxt, buf ^ 1, step + 1, ks);
+      stash_part(nxt, buf ^ 1, ks);
     }
   };
 
   StepRegs ra, rb;
-  fetch(ra, 0);
+  load_x(0);
+  fetch_w(ra, 0);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) stash_part(ra, 0, 0, q);
-  fetch(rb, 1);
+  for (int q = 0; q < 4; ++q) stash_part(ra, 0, q);
+  fetch_w(rb, 1);
   __syncthreads();
 
   // two steps per trip so that the register sets keep static names
   int step = 0;
   for (; step + 1 < nsteps; step += 2) {
-    fetch(ra, step + 2);
+    load_x(step + 1);
+    fetch_w(ra, step + 2);
     compute(step, rb);
     __syncthreads();
-    fetch(rb, step + 3);
+    load_x(step + 2);
+    fetch_w(rb, step + 3);
     compute(step + 1, ra);
     __syncthreads();
   }
@@ -319,7 +341,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
   // 32x32 accumulator layout: lane l holds column l % 32 and, in register r,
   // row 8 * (r / 4) + 4 * (l / 32) + r % 4.  Rows past M fall outside the
   // buffer and are dropped; columns past N are skipped.
-  const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y + (size_t)m0 * N, (uint32_t)rows_m * N * 2);
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y + (size_t)m0 * ldy, (uint32_t)rows_m * ldy * 2);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -330,7 +352,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
       for (int r = 0; r < 16; ++r) {
         const int row = wm + 32 * a + 8 * (r >> 2) + 4 * fh + (r & 3);
         __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)acc[a][b][r]), ry,
-                                              (uint32_t)(row * N + n0 + col) * 2, 0, 0);
+                                              (uint32_t)(row * ldy + n0 + col) * 2, 0, 0);
       }
     }
 }
@@ -340,6 +362,53 @@ hipError_t launch_skinny(const void* x, const uint32_t* qw, const uint16_t* sc, 
                          int N, int K, int gs, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_skinny_kernel<MT, KS, SPW, ZP>), dim3((N + 15) / 16), dim3(KS * 64), 0, stream,
                      static_cast<const _Float16*>(x), qw, sc, qz, Y, M, N, K, gs);
+  return hipGetLastError();
+}
+
+int compute_units() {
+  static int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    return n;
+  }();
+  return cus;
+}
+
+template <bool ZP, int NB>
+void launch_large_part(const _Float16* X, const uint32_t* qw, const uint16_t* sc, const uint32_t* qz, _Float16* Y, int M,
+                       int N, int K, int gs, int n_base, int ldy, hipStream_t stream) {
+  constexpr int TBN = 128 * NB;
+  const int G = K >> gs;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + TBN - 1) / TBN;
+  const uint32_t* qwp = qw + (size_t)n_base * (K >> 3);
+  const uint16_t* scp = sc + scale_index(n_base, 0, G);
+  const uint32_t* qzp = ZP ? qz + zero_word_index(n_base, 0, G) : qz;
+  if (K % BK == 0)
+    hipLaunchKernelGGL((gemm_large_kernel<ZP, false, NB>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, X, qwp, scp,
+                       qzp, Y + n_base, M, N, K, gs, tiles_m, ldy);
+  else
+    hipLaunchKernelGGL((gemm_large_kernel<ZP, true, NB>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, X, qwp, scp,
+                       qzp, Y + n_base, M, N, K, gs, tiles_m, ldy);
+}
+
+// 256x256 tiles; when the last wave of tiles over the compute units would run
+// at most half full, the N columns of that wave are computed instead as
+// 256x128 tiles in a second launch, so the tail takes half a tile time.
+template <bool ZP>
+hipError_t launch_large(const _Float16* X, const uint32_t* qw, const uint16_t* sc, const uint32_t* qz, _Float16* Y,
+                        int M, int N, int K, int gs, hipStream_t stream) {
+  const int cus = compute_units();
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int tiles = tiles_m * tiles_n, rem = tiles % cus;
+  int tail_n = 0;  // 256-wide N tiles moved to the half-width launch
+  if (tiles > cus && rem > 0 && 2 * rem <= cus) {
+    tail_n = (rem + tiles_m - 1) / tiles_m;
+    if (tail_n >= tiles_n) tail_n = 0;
+  }
+  const int n_main = (tiles_n - tail_n) * BN;
+  if (n_main > 0) launch_large_part<ZP, 2>(X, qw, sc, qz, Y, M, tail_n ? n_main : N, K, gs, 0, N, stream);
+  if (tail_n) launch_large_part<ZP, 1>(X, qw, sc, qz, Y, M, N - n_main, K, gs, n_main, N, stream);
   return hipGetLastError();
 }
 
@@ -358,13 +427,7 @@ hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales,
       default: return launch_skinny<4, 8, 1, ZP>(x, qweight, sc, qzeros, Y, M, N, K, gs, stream);
     }
   }
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  if (K % BK == 0)
-    hipLaunchKernelGGL((gemm_large_kernel<ZP, false>), dim3(tiles_m * tiles_n), dim3(512), 0, stream,
-                       static_cast<const _Float16*>(x), qweight, sc, qzeros, Y, M, N, K, gs, tiles_m);
-  else
-    hipLaunchKernelGGL((gemm_large_kernel<ZP, true>), dim3(tiles_m * tiles_n), dim3(512), 0, stream,
-                       static_cast<const _Float16*>(x), qweight, sc, qzeros, Y, M, N, K, gs, tiles_m);
+  return launch_large<ZP>(static_cast<const _Float16*>(x), qweight, sc, qzeros, Y, M, N, K, gs, stream);
   return hipGetLastError();
 }
 
