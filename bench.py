@@ -190,6 +190,52 @@ def time_graph(torch, fn, iters, warm=3):
     return tm.stop_ms() / iters, graph
 
 
+def leg_fused_decode(torch, awq, workloads, g=128, zp=True, blocks=32, replays=20):
+    """Single-token decode with the pages' fused projections: q/k/v as one
+    4096 -> 12288 layer and gate/up as one 4096 -> 22016 layer, so a block is 4
+    awq_gemv launches (qkv, o, gate_up, down) instead of 7.  Same weights and
+    bytes as the unfused step; outputs are the concatenations."""
+    names = [n for n, _, _ in workloads.LLAMA7B_BLOCK]
+    Ws = {}
+    for li, (name, K, N) in enumerate(workloads.LLAMA7B_BLOCK):
+        Ws[name] = torch.from_numpy(workloads.weight(N, K, cfg=2, layer=li)).cuda()
+    groups = [("qkv", ["q_proj", "k_proj", "v_proj"]), ("o", ["o_proj"]), ("gate_up", ["gate_proj", "up_proj"]),
+              ("down", ["down_proj"])]
+    fused = [(gname, awq.pack_fused([Ws[n] for n in parts], g, zp)) for gname, parts in groups]
+    del Ws
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(blocks):
+        reps.append([awq.PackedWeight(pw.qweight.clone(), pw.scales.clone(), pw.qzeros.clone() if zp else None, pw.N,
+                                      pw.K, pw.group_size, pw.zero_point) for _, pw in fused])
+    xs = [torch.from_numpy(workloads.activations(1, pw.K, cfg=2, layer=i)).cuda() for i, (_, pw) in enumerate(fused)]
+    ys = [torch.empty((1, pw.N), dtype=torch.float16, device="cuda") for _, pw in fused]
+
+    def step():
+        for rep in reps:
+            for i, pw in enumerate(rep):
+                awq.awq_gemv(xs[i], pw.qweight, pw.scales, pw.qzeros, pw.N, pw.K, g, zp, y=ys[i])
+
+    ms, _ = time_graph(torch, step, replays)
+    nbytes = blocks * sum(algorithmic_bytes(1, pw.N, pw.K, g, zp) for _, pw in fused)
+    per = {}
+    for i, (gname, pw) in enumerate(fused):
+        def one(i=i):
+            for rep in reps:
+                pwr = rep[i]
+                awq.awq_gemv(xs[i], pwr.qweight, pwr.scales, pwr.qzeros, pwr.N, pwr.K, g, zp, y=ys[i])
+
+        ms_i, _ = time_graph(torch, one, replays)
+        us = ms_i * 1e3 / blocks
+        b = algorithmic_bytes(1, pw.N, pw.K, g, zp)
+        per[gname] = {"K": pw.K, "N": pw.N, "us": round(us, 3), "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
+    del reps
+    torch.cuda.empty_cache()
+    return {"what": "decode through %d Llama-7B blocks with fused qkv and gate_up (4 awq_gemv per block)" % blocks,
+            "ms_per_step": round(ms, 4), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "per_layer": per}
+
+
 def leg_batched_decode(torch, awq, workloads, g=128, zp=True, blocks=16, iters=20):
     """M = 4 / 16 / 64 tokens through the 7 linears of `blocks` distinct blocks."""
     out = {}
@@ -432,13 +478,16 @@ def main():
     }
 
     legs = set(args.legs.split(",")) if args.legs not in ("all", "none") else (
-        {"pack", "batched", "prefill"} if args.legs == "all" else set())
+        {"pack", "fused", "batched", "prefill"} if args.legs == "all" else set())
     out_legs = {}
     if "pack" in legs:
         log("leg: pack")
         out_legs["pack"] = leg_pack(torch, awq, layers, g, zp)
     del reps, graph
     torch.cuda.empty_cache()
+    if "fused" in legs:
+        log("leg: fused decode")
+        out_legs["fused_decode_gemv"] = leg_fused_decode(torch, awq, workloads, g, zp, blocks=args.blocks)
     if "batched" in legs:
         log("leg: batched decode")
         out_legs["batched_decode_gemm"] = leg_batched_decode(torch, awq, workloads, g, zp)

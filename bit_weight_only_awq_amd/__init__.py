@@ -189,6 +189,41 @@ def pack(W: torch.Tensor, q_group_size: int = 128, zero_point: bool = True) -> P
     return PackedWeight(qw, sc, qz, W.shape[0], W.shape[1], q_group_size, bool(zero_point))
 
 
+def pack_fused(weights, q_group_size: int = 128, zero_point: bool = True) -> PackedWeight:
+    """Pack several weights that read the same input (e.g. the q, k and v
+    projections, or gate and up) as one weight of N = sum of their N, so one
+    launch computes all of them ("AI-Research-SKILLs AWQ 高级使用指南", section
+    层融合: Q, K, V merged into one GEMM, gate and up fused).
+
+    Each part is quantized by its own ``awq_pack`` call straight into its
+    slice of the fused buffers: rows are independent and the scales/zero
+    points are stored per octet of rows, so a part with N a multiple of 8 is a
+    contiguous slice of every array and the result is bit-identical to packing
+    the concatenated weight.  The output of ``linear`` is the concatenation of
+    the parts' outputs, in order."""
+    weights = list(weights)
+    if not weights:
+        raise ValueError("pack_fused needs at least one weight")
+    K = weights[0].shape[1]
+    if any(w.dim() != 2 or w.shape[1] != K for w in weights):
+        raise ValueError("fused weights must all be [N_i, K] with the same K")
+    N = sum(w.shape[0] for w in weights)
+    G = K // q_group_size if q_group_size > 0 else 0
+    dev = weights[0].device
+    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=dev)
+    scales = torch.empty((N // 8, G, 8), dtype=torch.float16, device=dev)
+    qzeros = torch.empty((N // 8, G), dtype=torch.int32, device=dev) if zero_point else None
+    n0 = 0
+    for w in weights:
+        n = w.shape[0]
+        if n % 8:
+            raise ValueError("every fused part needs N % 8 == 0")
+        awq_pack(w, q_group_size, zero_point, qweight=qweight[n0:n0 + n], scales=scales[n0 // 8:(n0 + n) // 8],
+                 qzeros=qzeros[n0 // 8:(n0 + n) // 8] if zero_point else None)
+        n0 += n
+    return PackedWeight(qweight, scales, qzeros, N, K, q_group_size, bool(zero_point))
+
+
 def linear(x: torch.Tensor, pw: PackedWeight, version: str = "auto") -> torch.Tensor:
     """Y = X . W'^T.  ``version`` "GEMV" (one token), "GEMM" (any batch) or "auto"."""
     x2 = x.reshape(-1, pw.K)

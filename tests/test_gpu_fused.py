@@ -1,0 +1,45 @@
+"""Fused projections: several weights that read the same input packed as one
+weight (q/k/v, gate/up) give bit-identical packed data and outputs to the
+separate layers, and match the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import awq_oracle as O
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _parts(shapes, K, cfg):
+    return [workloads.weight(N, K, cfg=cfg, layer=i) for i, N in enumerate(shapes)]
+
+
+@pytest.mark.parametrize("zp", [True, False])
+@pytest.mark.parametrize("shapes,K,g", [((4096, 4096, 4096), 4096, 128), ((11008, 11008), 4096, 128),
+                                        ((24, 40, 8), 512, 32)])
+def test_fused_pack_and_layers_match_separate(shapes, K, g, zp):
+    awq = G.lib()
+    Ws = _parts(shapes, K, cfg=6)
+    dev = [G.dev_f16(W) for W in Ws]
+    fused = awq.pack_fused(dev, g, zp)
+    sep = [awq.pack(w, g, zp) for w in dev]
+    torch.cuda.synchronize()
+    assert np.array_equal(G.host_u32(fused.qweight), np.concatenate([G.host_u32(p.qweight) for p in sep]))
+    assert np.array_equal(G.host_f16_bits(fused.scales), np.concatenate([G.host_f16_bits(p.scales) for p in sep]))
+    if zp:
+        assert np.array_equal(G.host_u32(fused.qzeros), np.concatenate([G.host_u32(p.qzeros) for p in sep]))
+    for M in (1, 4, 300):
+        X = workloads.activations(M, K, cfg=6, layer=M)
+        x = G.dev_f16(X)
+        yf = G.host_f16(awq.linear(x, fused))
+        ys = np.concatenate([G.host_f16(awq.linear(x, p)) for p in sep], axis=1)
+        torch.cuda.synchronize()
+        assert np.array_equal(yf.view(np.uint16), ys.view(np.uint16)), M
+        if M <= 4:
+            oq, os_, oz = O.pack(np.concatenate(Ws), g, zp)
+            y_ref, d = O.matmul_ref(X, O.dequant_packed(oq, os_, oz, sum(shapes), K, g, zp))
+            G.assert_within_tolerance(yf, y_ref, d, f"fused M={M}")
