@@ -156,6 +156,24 @@ def awq_gemv(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, qzero
     return y
 
 
+_WORKSPACES = {}
+
+
+def gemm_workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-initialised awq_gemm workspace of at least ``nbytes`` for the
+    current stream of ``device``, kept for later calls.  awq_gemm returns the
+    workspace's counters to zero, so calls in stream order can share it; each
+    stream gets its own, since concurrent calls must not share one."""
+    device = torch.device(device)
+    key = (device.index if device.index is not None else torch.cuda.current_device(),
+           torch.cuda.current_stream(device).cuda_stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def awq_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional[torch.Tensor], N: int,
              K: int, group_size: int = 128, zero_point: bool = True, y: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None):
@@ -165,7 +183,7 @@ def awq_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, qzero
     M = x.shape[0]
     need = awq_gemm_workspace_bytes(M, N, K, group_size)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        workspace = gemm_workspace(need, x.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.awq_gemm(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros) if zero_point else None, _ptr(y), M, N, K,
                       group_size, int(bool(zero_point)), _ptr(workspace), ws_bytes, _stream(x))

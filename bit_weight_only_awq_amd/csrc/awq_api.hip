@@ -13,10 +13,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128 || g == 256; }
 
+// Largest N and K: keeps every per-tile buffer-resource extent and offset of
+// the kernels below 2^31 bytes.
+constexpr int32_t kMaxDim = 1 << 21;
+
 // Checks shared by every entry point that reads or writes a packed weight.
 int check_weight_shape(int32_t N, int32_t K, int32_t group_size) {
   if (!valid_group(group_size)) return AWQ_ERR_GROUP;
-  if (N < 1 || K < 1 || (N & 7) != 0) return AWQ_ERR_SHAPE;
+  if (N < 1 || K < 1 || (N & 7) != 0 || N > kMaxDim || K > kMaxDim) return AWQ_ERR_SHAPE;
   if (K % group_size != 0) return AWQ_ERR_GROUP;
   return AWQ_OK;
 }
@@ -72,11 +76,8 @@ int awq_gemv(const void* x, const uint32_t* qweight, const void* scales, const u
 }
 
 size_t awq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t group_size) {
-  (void)M;
-  (void)N;
-  (void)K;
-  (void)group_size;
-  return 0;
+  if (M < 1 || check_weight_shape(N, K, group_size) != AWQ_OK) return 0;
+  return awq::gemm_workspace_bytes(M, N, K);
 }
 
 int awq_gemm(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* y, int32_t M,
@@ -92,8 +93,10 @@ int awq_gemm(const void* x, const uint32_t* qweight, const void* scales, const u
   const size_t need = awq_gemm_workspace_bytes(M, N, K, group_size);
   if (workspace_bytes < need) return AWQ_ERR_WORKSPACE;
   if (need > 0 && !workspace) return AWQ_ERR_NULL;
+  if (need > 0 && !aligned16(workspace)) return AWQ_ERR_ALIGN;
   return from_hip(awq::launch_gemm(x, qweight, scales, zero_point ? qzeros : nullptr, y, M, N, K, group_size,
-                                   zero_point != 0, static_cast<hipStream_t>(stream)));
+                                   zero_point != 0, need > 0 ? workspace : nullptr,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 const char* awq_strerror(int status) {

@@ -6,21 +6,24 @@
 // rounding of the product with the group scale) and multiplied on the gfx950
 // fp16 matrix cores with fp32 accumulation.  Two kernels:
 //
-//   * gemm_skinny_kernel (M <= 64): still bound by the weight stream.  A wave
-//     owns NT tiles of 16 output rows and all (<= 4) tiles of 16 tokens; its
+//   * gemm_skinny_kernel (M <= 64): bound by the weight stream (and, from
+//     ~16 tokens on, by the activation loads).  A workgroup owns NT tiles of
+//     16 output rows, all (<= 4) tiles of 16 tokens and one slice of K; its
 //     lanes load packed weights straight into MFMA B-operand registers (one
 //     128-bit load = 32 channels of one row = four 16x16x32 B fragments), so
-//     no LDS round trip sits on the weight path.  The NW waves of a workgroup
-//     split K and are summed through LDS in a fixed order (deterministic, no
-//     workspace, no atomics).
+//     no LDS round trip sits on the weight path.  The waves of a workgroup
+//     split its slice and are summed through LDS in a fixed order; when K is
+//     split across workgroups, fp32 partial tiles go through the caller's
+//     workspace and the last workgroup of each tile adds them in slice order
+//     (deterministic, one launch).
 //
-//   * gemm_large_kernel (M > 64): compute-bound.  256x256 output tile per
-//     workgroup of 4 waves (2x2, 128x128 each, 4x4 v_mfma_f32_32x32x16_f16
-//     tiles), K in steps of 64.  The next step's X tile and packed weights are
-//     fetched into registers while the current step multiplies out of LDS; the
-//     weights are then decoded and written to LDS as fp16 next to the X tile.
-//     LDS rows are padded to 72 halves so that the 128-bit fragment reads of 8
-//     consecutive rows hit distinct banks.  Workgroups are mapped so that each
+//   * gemm_large_kernel (M > 64): matrix-core bound.  256 x 256 output tile
+//     (or 256 x 128 for the last wave of tiles) per workgroup of 8 waves
+//     (2 x 4, 128 x 64 each, v_mfma_f32_32x32x16_f16), K in steps of 64.  X
+//     tiles go from HBM straight into LDS (buffer-to-LDS loads); packed
+//     weights are fetched two steps ahead into registers, decoded and stored
+//     to LDS as fp16 interleaved with the current step's MFMAs.  LDS tiles use
+//     an XOR swizzle instead of padding; workgroups are mapped so that each
 //     XCD (and its L2) works on a contiguous band of tiles.
 //
 // MFMA operand placement: a lane's 8 fp16 values of A and of B cover the same
@@ -46,35 +49,50 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past every resource: loads return 0
 
-// Global data of one 128-channel step for one lane: its 32 channels of one
-// weight row (4 packed words), the matching activations of its MT token rows,
-// and the row's raw scale and zero-point word for the lane's group.
-template <int MT>
+// Global data of one 128-channel step for one lane: its 32 channels of NT
+// weight rows (4 packed words each) with each row's raw scale and zero-point
+// word for the lane's group, and the matching activations of its MT token rows.
+template <int MT, int NT>
 struct SkinnyStep {
-  u32x4 w;
+  u32x4 w[NT];
+  uint32_t s[NT], z[NT];
   u32x4 x[MT][4];
-  uint32_t s, z;
 };
 
-// One workgroup per 16 output rows, KS waves splitting K.  Wave w handles the
-// 128-channel steps w, w + KS, ... in rounds of SPW steps; the loads of round
-// r + 1 are in flight while round r is multiplied.  A lane (i, h) = (lane % 16,
-// lane / 16) loads the 32 channels 128 c + 32 h .. +32 of row n0 + i as one
+// One workgroup computes a tile of 16 NT output rows x 16 MT token rows over
+// one slice of K (split-K across workgroups).  Its KS waves take the slice's
+// 128-channel steps round robin, in rounds of SPW steps whose loads are in
+// flight while the previous round is multiplied.  Lane (i, h) = (lane % 16,
+// lane / 16) loads the 32 channels 128 c + 32 h .. +32 of row 16 nt + i as one
 // 16-byte word, which is exactly its B operand for four 16x16x32 MFMAs, and
-// the same channels of token rows 16 mt + i as the A operands.  The waves'
-// partial sums meet in LDS and are added in wave order (deterministic).
-template <int MT, int KS, int SPW, bool ZP>
+// the same channels of token rows 16 mt + i as the A operands; one X fragment
+// serves NT weight tiles.  The waves' partial sums meet in LDS and are added
+// in wave order.  With one slice the tile is written to Y; with several, each
+// workgroup writes its fp32 partial tile to the workspace and the last of the
+// tile's workgroups to finish (an agent-scope counter per tile) adds the
+// partials in slice order and writes Y, then resets the counter to zero.  The
+// result does not depend on which workgroup finishes last.
+template <int MT, int NT, int KS, int SPW, bool ZP>
 __global__ __launch_bounds__(KS * 64) void gemm_skinny_kernel(const _Float16* __restrict__ X,
                                                               const uint32_t* __restrict__ qweight,
                                                               const uint16_t* __restrict__ scales,
                                                               const uint32_t* __restrict__ qzeros,
                                                               _Float16* __restrict__ Y, int M, int N, int K,
-                                                              int gshift) {
+                                                              int gshift, int splits, int steps_per_split,
+                                                              uint32_t* __restrict__ counters,
+                                                              float* __restrict__ partials) {
+  constexpr int kTileElems = MT * NT * 256;          // fp32 values of one 16 MT x 16 NT tile
+  constexpr int kPerThread = (kTileElems + KS * 64 - 1) / (KS * 64);  // tile values per thread (o < kTileElems)
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int li = lane & 15, lh = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  const int nrows = min(16, N - n0);  // 16, or 8 at the end of an N that is not a multiple of 16
+  // consecutive ids on one XCD: the slices of a tile share that XCD's L2
+  const int id = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  const int tile = id / splits, split = id - tile * splits;
+  const int n0 = tile * 16 * NT;
+  const int nrows = min(16 * NT, N - n0);  // a multiple of 8
   const int steps = (K + 127) >> 7;
+  const int c_begin = split * steps_per_split;
+  const int c_end = min(steps, c_begin + steps_per_split);
   const int G = K >> gshift;
   const DecodeConsts kc;
 
@@ -83,18 +101,28 @@ __global__ __launch_bounds__(KS * 64) void gemm_skinny_kernel(const _Float16* __
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(scales + scale_index(n0, 0, G), (uint32_t)(nrows >> 3) * G * 16);
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(ZP ? qzeros + zero_word_index(n0, 0, G) : qzeros,
                                               ZP ? (uint32_t)(nrows >> 3) * G * 4 : 0u);
-  const uint32_t wbase = (uint32_t)li * (K >> 1) + lh * 16;
-  const uint32_t sbase = (uint32_t)(((li >> 3) * G * 8 + (li & 7)) * 2);
-  const uint32_t zbase = (uint32_t)((li >> 3) * G * 4);
+  // row 16 nt + li of the tile: rows past nrows lie past the resources and read as 0
+  uint32_t wbase[NT], sbase[NT], zbase[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = 16 * nt + li;
+    wbase[nt] = (uint32_t)r * (K >> 1) + lh * 16;
+    sbase[nt] = (uint32_t)(((r >> 3) * G * 8 + (r & 7)) * 2);
+    zbase[nt] = (uint32_t)((r >> 3) * G * 4);
+  }
   const int zshift = 4 * (li & 7);
 
-  auto fetch = [&](SkinnyStep<MT>& r, int c) {
+  auto fetch = [&](SkinnyStep<MT, NT>& r, int c) {
     const int k0 = (c << 7) + (lh << 5);  // first channel of the lane's 32
-    const bool kin = c < steps && k0 < K;
+    const bool kin = c < c_end && k0 < K;
     const int grp = k0 >> gshift;
-    r.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, kin ? wbase + c * 64 : kOutOfRange, 0, 0));
-    r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, kin ? sbase + grp * 16 : kOutOfRange, 0, 0);
-    r.z = ZP ? __builtin_amdgcn_raw_buffer_load_b32(rz, kin ? zbase + grp * 4 : kOutOfRange, 0, 0) : 0u;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      r.w[nt] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, kin ? wbase[nt] + c * 64 : kOutOfRange, 0, 0));
+      r.s[nt] = __builtin_amdgcn_raw_buffer_load_b16(rs, kin ? sbase[nt] + grp * 16 : kOutOfRange, 0, 0);
+      r.z[nt] = ZP ? __builtin_amdgcn_raw_buffer_load_b32(rz, kin ? zbase[nt] + grp * 4 : kOutOfRange, 0, 0) : 0u;
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       // token rows past M lie past the end of the X resource and read as 0
@@ -105,38 +133,44 @@ __global__ __launch_bounds__(KS * 64) void gemm_skinny_kernel(const _Float16* __
     }
   };
 
-  float4_t acc[MT];
+  float4_t acc[MT][NT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const SkinnyStep<MT>& r) {
-    const uint32_t z = ZP ? ((r.z >> zshift) & 15u) : 8u;
-    const ZeroBias zb = zero_bias(z);
-    const half2_t s2 = splat2(__builtin_bit_cast(_Float16, (uint16_t)r.s));
+  auto compute = [&](const SkinnyStep<MT, NT>& r) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const half8_t b = decode_word_scaled(r.w[e], zb, kc, s2);
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t z = ZP ? ((r.z[nt] >> zshift) & 15u) : 8u;
+      const ZeroBias zb = zero_bias(z);
+      const half2_t s2 = splat2(__builtin_bit_cast(_Float16, (uint16_t)r.s[nt]));
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(r.x[mt][e]), b, acc[mt], 0, 0, 0);
+      for (int e = 0; e < 4; ++e) {
+        const half8_t b = decode_word_scaled(r.w[nt][e], zb, kc, s2);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(r.x[mt][e]), b, acc[mt][nt], 0, 0, 0);
+      }
     }
   };
 
   // rounds of SPW steps, double-buffered
   const int per_round = KS * SPW;
-  const int rounds = (steps + per_round - 1) / per_round;
-  SkinnyStep<MT> ra[SPW], rb[SPW];
+  const int rounds = (c_end - c_begin + per_round - 1) / per_round;
+  const int c0 = c_begin + wave;
+  SkinnyStep<MT, NT> ra[SPW], rb[SPW];
 #pragma unroll
-  for (int u = 0; u < SPW; ++u) fetch(ra[u], wave + KS * u);
+  for (int u = 0; u < SPW; ++u) fetch(ra[u], c0 + KS * u);
   int r = 0;
   for (; r + 1 < rounds; r += 2) {
 #pragma unroll
-    for (int u = 0; u < SPW; ++u) fetch(rb[u], wave + KS * (SPW * (r + 1) + u));
+    for (int u = 0; u < SPW; ++u) fetch(rb[u], c0 + KS * (SPW * (r + 1) + u));
 #pragma unroll
     for (int u = 0; u < SPW; ++u) compute(ra[u]);
     if (r + 2 < rounds) {
 #pragma unroll
-      for (int u = 0; u < SPW; ++u) fetch(ra[u], wave + KS * (SPW * (r + 2) + u));
+      for (int u = 0; u < SPW; ++u) fetch(ra[u], c0 + KS * (SPW * (r + 2) + u));
     }
 #pragma unroll
     for (int u = 0; u < SPW; ++u) compute(rb[u]);
@@ -147,22 +181,152 @@ __global__ __launch_bounds__(KS * 64) void gemm_skinny_kernel(const _Float16* __
   }
 
   // 16x16 accumulator layout: lane (li, lh) holds column li, rows 4 lh + j.
-  __shared__ float red[KS][MT * 4][64];
+  // Tile value o = 64 ((mt NT + nt) 4 + j) + lane.
+  __shared__ float red[KS][MT * NT * 4][64];
+  __shared__ int is_last;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) red[wave][mt * 4 + j][lane] = acc[mt][j];
-  __syncthreads();
-  for (int o = t; o < MT * 4 * 64; o += KS * 64) {
-    const int idx = o >> 6, ln = o & 63;
-    float sum = red[0][idx][ln];
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int w = 1; w < KS; ++w) sum += red[w][idx][ln];
-    const int m = 16 * (idx >> 2) + 4 * (ln >> 4) + (idx & 3), n = n0 + (ln & 15);
-    if (m < M && n < N) Y[(size_t)m * N + n] = (_Float16)sum;
+      for (int j = 0; j < 4; ++j) red[wave][(mt * NT + nt) * 4 + j][lane] = acc[mt][nt][j];
+  __syncthreads();
+  float sum[kPerThread];
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int o = t + q * KS * 64, idx = o >> 6, ln = o & 63;
+    float v = 0.0f;
+    if (o < kTileElems) {
+      v = red[0][idx][ln];
+#pragma unroll
+      for (int w = 1; w < KS; ++w) v += red[w][idx][ln];
+    }
+    sum[q] = v;
+  }
+
+  if (splits > 1) {
+    // Hand-off between the workgroups of a tile, which may run on different
+    // XCDs (separate L2s).  Partials are written and read with device-scope
+    // coherence (the SC1 cache-policy bit: the access is performed at the
+    // agent's coherence point, as for agent-scope atomics), and each thread
+    // waits for its partial stores to be acknowledged before the workgroup
+    // barrier that precedes the counter increment; the reads are issued after
+    // the increment has returned.  This orders the hand-off without
+    // agent-scope fences, which would write back and invalidate whole L2s.
+    constexpr int kDeviceScope = 1 << 4;  // SC1
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(partials + (size_t)tile * splits * kTileElems, (uint32_t)splits * kTileElems * 4);
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+      const int o = t + q * KS * 64;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sum[q]), rp,
+                                            o < kTileElems ? (uint32_t)(split * kTileElems + o) * 4 : kOutOfRange, 0,
+                                            kDeviceScope);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(counters + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      is_last = prev == (uint32_t)(splits - 1);
+      if (is_last) __hip_atomic_store(counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!is_last) return;
+    // slices in order, four loads in flight per value; this workgroup's own
+    // slice comes from its registers
+    float tot[kPerThread];
+    for (int s0 = 0; s0 < splits; s0 += 4) {
+      float p[4][kPerThread];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q) {
+          const int s = s0 + u, o = t + q * KS * 64;
+          const uint32_t off =
+              s < splits && s != split && o < kTileElems ? (uint32_t)(s * kTileElems + o) * 4 : kOutOfRange;
+          p[u][q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, off, 0, kDeviceScope));
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q) {
+          const int s = s0 + u;
+          const float v = s == split ? sum[q] : p[u][q];
+          if (s == 0) tot[q] = v;
+          else if (s < splits) tot[q] += v;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) sum[q] = tot[q];
+  }
+
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int o = t + q * KS * 64, idx = o >> 6, ln = o & 63;
+    const int mt = idx / (NT * 4), nt = (idx >> 2) % NT;
+    const int m = 16 * mt + 4 * (ln >> 4) + (idx & 3), n = 16 * nt + (ln & 15);
+    if (o < kTileElems && m < M && n < nrows) Y[(size_t)m * N + n0 + n] = (_Float16)sum[q];
   }
 }
 
+// Launch plan of the skinny kernel for an M x N x K product: token tiles,
+// row tiles per workgroup, waves, steps per round and the K split.  The
+// workspace size follows from it, so awq_gemm_workspace_bytes and the
+// launcher share this one function.
+struct SkinnyPlan {
+  int mt, nt, ks, spw;
+  int tiles_n, steps, splits, steps_per_split;
+};
+
+SkinnyPlan plan_skinny(int M, int N, int K) {
+  SkinnyPlan p;
+  p.mt = (M + 15) / 16;
+  // Measured on the Llama-7B decode shapes (4096 x 4096, 4096 -> 11008,
+  // 11008 -> 4096): up to 4 tokens the weight stream rules, and 16-row tiles
+  // with 8 waves of two steps in flight are best; beyond that the activations
+  // dominate the load traffic and wider row tiles (each X fragment reused by
+  // NT weight tiles) win, with K split to keep every compute unit busy.
+  int target_blocks;
+  if (M <= 4) {
+    p.nt = 1, p.ks = 8, p.spw = 2, target_blocks = 256;
+  } else if (p.mt == 1) {
+    p.nt = 2, p.ks = 4, p.spw = 2, target_blocks = 512;
+  } else {
+    p.nt = 4, p.ks = 4, p.spw = 1, target_blocks = 256;
+  }
+  p.tiles_n = (N + 16 * p.nt - 1) / (16 * p.nt);
+  p.steps = (K + 127) / 128;
+  int splits = (target_blocks + p.tiles_n - 1) / p.tiles_n;
+  const int max_splits = (p.steps + p.ks - 1) / p.ks;  // each wave gets a step
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  p.steps_per_split = (p.steps + splits - 1) / splits;
+  p.splits = (p.steps + p.steps_per_split - 1) / p.steps_per_split;  // no empty slice
+  return p;
+}
+
+// The workspace starts with a counter region of fixed size, one 32-bit
+// counter for every possible 16-row tile (N <= 2^21), so that calls of any
+// shape sharing one workspace find their counters at zero: partial tiles
+// always lie after it.
+constexpr size_t kCounterBytes = ((size_t)1 << 21) / 16 * 4;
+
+size_t skinny_workspace_bytes(const SkinnyPlan& p) {
+  if (p.splits <= 1) return 0;
+  return kCounterBytes + (size_t)p.tiles_n * p.splits * p.mt * p.nt * 256 * 4;
+}
+
+template <int MT, int NT, int KS, int SPW, bool ZP>
+hipError_t launch_skinny(const SkinnyPlan& p, const void* x, const uint32_t* qw, const uint16_t* sc,
+                         const uint32_t* qz, _Float16* Y, int M, int N, int K, int gs, void* workspace,
+                         hipStream_t stream) {
+  uint32_t* counters = static_cast<uint32_t*>(workspace);
+  float* partials = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes) : nullptr;
+  hipLaunchKernelGGL((gemm_skinny_kernel<MT, NT, KS, SPW, ZP>), dim3(p.tiles_n * p.splits), dim3(KS * 64), 0, stream,
+                     static_cast<const _Float16*>(x), qw, sc, qz, Y, M, N, K, gs, p.splits, p.steps_per_split,
+                     counters, partials);
+  return hipGetLastError();
+}
 // --------------------------------------------------------------------------
 // Large M: matrix-core bound.
 // --------------------------------------------------------------------------
@@ -357,14 +521,6 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
     }
 }
 
-template <int MT, int KS, int SPW, bool ZP>
-hipError_t launch_skinny(const void* x, const uint32_t* qw, const uint16_t* sc, const uint32_t* qz, _Float16* Y, int M,
-                         int N, int K, int gs, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_skinny_kernel<MT, KS, SPW, ZP>), dim3((N + 15) / 16), dim3(KS * 64), 0, stream,
-                     static_cast<const _Float16*>(x), qw, sc, qz, Y, M, N, K, gs);
-  return hipGetLastError();
-}
-
 int compute_units() {
   static int cus = [] {
     int dev = 0, n = 0;
@@ -414,17 +570,19 @@ hipError_t launch_large(const _Float16* X, const uint32_t* qw, const uint16_t* s
 
 template <bool ZP>
 hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* y,
-                     int M, int N, int K, int group_size, hipStream_t stream) {
+                     int M, int N, int K, int group_size, void* workspace, hipStream_t stream) {
   const uint16_t* sc = static_cast<const uint16_t*>(scales);
   _Float16* Y = static_cast<_Float16*>(y);
   const int gs = log2_group(group_size);
   if (M <= 64) {
-    // up to 32 tokens: 8 waves of 2 steps per round; more tokens: 8 waves of 1 step
-    switch ((M + 15) / 16) {
-      case 1: return launch_skinny<1, 8, 2, ZP>(x, qweight, sc, qzeros, Y, M, N, K, gs, stream);
-      case 2: return launch_skinny<2, 8, 2, ZP>(x, qweight, sc, qzeros, Y, M, N, K, gs, stream);
-      case 3: return launch_skinny<3, 8, 1, ZP>(x, qweight, sc, qzeros, Y, M, N, K, gs, stream);
-      default: return launch_skinny<4, 8, 1, ZP>(x, qweight, sc, qzeros, Y, M, N, K, gs, stream);
+    const SkinnyPlan p = plan_skinny(M, N, K);
+    switch (p.mt) {
+      case 1:
+        return p.nt == 1 ? launch_skinny<1, 1, 8, 2, ZP>(p, x, qweight, sc, qzeros, Y, M, N, K, gs, workspace, stream)
+                         : launch_skinny<1, 2, 4, 2, ZP>(p, x, qweight, sc, qzeros, Y, M, N, K, gs, workspace, stream);
+      case 2: return launch_skinny<2, 4, 4, 1, ZP>(p, x, qweight, sc, qzeros, Y, M, N, K, gs, workspace, stream);
+      case 3: return launch_skinny<3, 4, 4, 1, ZP>(p, x, qweight, sc, qzeros, Y, M, N, K, gs, workspace, stream);
+      default: return launch_skinny<4, 4, 4, 1, ZP>(p, x, qweight, sc, qzeros, Y, M, N, K, gs, workspace, stream);
     }
   }
   return launch_large<ZP>(static_cast<const _Float16*>(x), qweight, sc, qzeros, Y, M, N, K, gs, stream);
@@ -433,10 +591,12 @@ hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales,
 
 }  // namespace
 
+size_t gemm_workspace_bytes(int M, int N, int K) { return M <= 64 ? skinny_workspace_bytes(plan_skinny(M, N, K)) : 0; }
+
 hipError_t launch_gemm(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* y,
-                       int M, int N, int K, int group_size, bool zero_point, hipStream_t stream) {
-  return zero_point ? launch_zp<true>(x, qweight, scales, qzeros, y, M, N, K, group_size, stream)
-                    : launch_zp<false>(x, qweight, scales, qzeros, y, M, N, K, group_size, stream);
+                       int M, int N, int K, int group_size, bool zero_point, void* workspace, hipStream_t stream) {
+  return zero_point ? launch_zp<true>(x, qweight, scales, qzeros, y, M, N, K, group_size, workspace, stream)
+                    : launch_zp<false>(x, qweight, scales, qzeros, y, M, N, K, group_size, workspace, stream);
 }
 
 }  // namespace awq

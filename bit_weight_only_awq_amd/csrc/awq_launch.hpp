@@ -17,7 +17,13 @@ hipError_t launch_dequant(const uint32_t* qweight, const void* scales, const uin
 hipError_t launch_gemv(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros,
                        void* y, int N, int K, int group_size, bool zero_point, hipStream_t stream);
 
+// Workspace bytes launch_gemm needs for an M x N x K product (0: none).
+size_t gemm_workspace_bytes(int M, int N, int K);
+
+// `workspace` holds gemm_workspace_bytes(M, N, K) bytes whose leading
+// per-tile counters are zero; the call leaves them zero again.
 hipError_t launch_gemm(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros,
-                       void* y, int M, int N, int K, int group_size, bool zero_point, hipStream_t stream);
+                       void* y, int M, int N, int K, int group_size, bool zero_point, void* workspace,
+                       hipStream_t stream);
 
 }  // namespace awq

@@ -17,15 +17,17 @@
  * Conventions for every entry point
  *   - All buffer pointers are DEVICE pointers on the current HIP device; the
  *     caller allocates and owns them.  The library never allocates, frees or
- *     keeps mutable state between calls, and never synchronizes the device.
+ *     keeps mutable state of its own between calls, and never synchronizes
+ *     the device (awq_gemm's workspace, owned by the caller, is the one
+ *     buffer a call hands on to the next; see there).
  *   - fp16 buffers are passed as void* and hold IEEE binary16 values.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Work is enqueued asynchronously; the return value reports argument
  *     validation and launch errors only.  On any error nothing is launched.
  *   - Every pointer must be 16-byte aligned.  Buffers must not overlap.
  *   - Shapes: N (output features) >= 1 and a multiple of 8; K (input
- *     features) >= 1 and a multiple of group_size; group_size in
- *     {32, 64, 128, 256}; M (tokens) >= 1.  G = K / group_size.
+ *     features) >= 1 and a multiple of group_size; N, K <= 2^21;
+ *     group_size in {32, 64, 128, 256}; M (tokens) >= 1.  G = K / group_size.
  *   - Weights must be finite; results for NaN/Inf weights are unspecified.
  *
  * Storage layout of a packed weight (the pages fix none; this one is ours):
@@ -112,9 +114,19 @@ int awq_gemv(const void* x, const uint32_t* qweight, const void* scales, const u
  * decoded to fp16 in registers and multiplied on the fp16 matrix cores with
  * fp32 accumulation; the output is rounded once to fp16.
  * X in fp16 [M][K]; Y out fp16 [M][N].  Same accuracy contract as awq_gemv.
+ * Deterministic run to run.
+ *
  * workspace: device scratch of at least awq_gemm_workspace_bytes(M, N, K,
- * group_size) bytes (may be NULL when that is 0), owned by the caller and
- * not read before it is written.  Deterministic run to run.
+ * group_size) bytes, 16-byte aligned, owned by the caller (may be NULL when
+ * that size is 0).  For small M (<= 64) the K dimension is split across
+ * workgroups: the workspace then starts with a 512 KiB region of 32-bit
+ * per-tile counters, followed by fp32 partial tiles, and the last workgroup
+ * of a tile to finish adds the partials in a fixed order (the result does not
+ * depend on which one finishes last).  The counter region must be ZERO when
+ * the buffer is first used (e.g. allocated zero-filled); every call returns
+ * it to zero, so one buffer serves any number of calls of any shape in
+ * stream order.  Calls that may run concurrently (different streams) need
+ * separate workspaces.
  */
 int awq_gemm(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros,
              void* y, int32_t M, int32_t N, int32_t K, int32_t group_size, int32_t zero_point,

@@ -93,7 +93,24 @@ def test_gemv_gemm_validation(lib):
     assert gemm(4, 8, 160, 64, 1) == awq.AWQ_ERR_GROUP
     assert gemm(4, 8, 128, 32, 1, sc=0) == awq.AWQ_ERR_NULL
     assert gemm(4, 8, 128, 32, 1, y=E + 6) == awq.AWQ_ERR_ALIGN
+    assert gemm(4, 1 << 22, 128, 32, 1) == awq.AWQ_ERR_SHAPE
+    assert gemv(1, 8, 1 << 22, 32, 1) == awq.AWQ_ERR_SHAPE
     assert ok  # silence unused
+
+
+def test_gemm_split_k_workspace_contract(lib):
+    """Shapes whose K is split across workgroups need a workspace: a 512 KiB
+    counter region plus one fp32 partial tile per workgroup.  Too small, NULL
+    or misaligned workspaces are rejected before any launch."""
+    M, N, K, g = 16, 4096, 4096, 128
+    need = awq.awq_gemm_workspace_bytes(M, N, K, g)
+    assert need > 512 * 1024 and (need - 512 * 1024) % (16 * 16 * 4) == 0
+    assert awq.awq_gemm_workspace_bytes(M, N, K, 100) == 0  # invalid shapes need nothing
+    assert awq.awq_gemm_workspace_bytes(0, N, K, g) == 0
+    call = lambda ws, wsb: lib.awq_gemm(A, B, C, D, E, M, N, K, g, 1, ws, wsb, None)  # noqa: E731
+    assert call(None, need - 1) == awq.AWQ_ERR_WORKSPACE
+    assert call(None, need) == awq.AWQ_ERR_NULL
+    assert call(A + 8, need) == awq.AWQ_ERR_ALIGN
 
 
 def test_dequant_validation(lib):

@@ -66,6 +66,40 @@ def test_gemm_ragged_tiles(M, N, K, g):
     check(M, N, K, g, False)
 
 
+@pytest.mark.parametrize("M,N,K,g", [(7, 264, 2080, 32), (40, 8, 4096, 128), (64, 4104, 11008, 128),
+                                     (2, 40, 1664, 64), (17, 136, 8192, 256)])
+def test_gemm_split_k(M, N, K, g):
+    """Shapes whose K is split across workgroups (partials in the workspace,
+    reduced by the last workgroup of each tile), with ragged row tiles and
+    a short last slice."""
+    assert G.lib().awq_gemm_workspace_bytes(M, N, K, g) > 0
+    check(M, N, K, g, True)
+    check(M, N, K, g, False)
+
+
+def test_gemm_split_k_workspace_reuse():
+    """One workspace serves consecutive calls of different shapes: every call
+    leaves the per-tile counters at zero, and the result is bit-identical
+    whichever workgroup of a tile finishes last."""
+    awq = G.lib()
+    g = 128
+    shapes = [(16, 4096, 4096), (64, 4104, 11008), (4, 11008, 4096), (64, 1024, 8192), (3, 4096, 4096)]
+    need = max(awq.awq_gemm_workspace_bytes(M, N, K, g) for M, N, K in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for M, N, K in shapes:
+        W = workloads.weight(N, K, cfg=3, layer=M)
+        X = workloads.activations(M, K, cfg=3, layer=M)
+        qw, sc, qz = G.upload_packed(*O.pack(W, g, True))
+        x = G.dev_f16(X)
+        ys = [awq.awq_gemm(x, qw, sc, qz, N, K, g, True, workspace=ws) for _ in range(4)]
+        torch.cuda.synchronize()
+        # a counter left non-zero would make the next call skip (or repeat) the reduction of its tile
+        for y in ys[1:]:
+            assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    y_ref, d = O.matmul_ref(X, O.dequant_packed(*O.pack(W, g, True), N, K, g, True))
+    G.assert_within_tolerance(G.host_f16(ys[-1]), y_ref, d, "reused workspace")
+
+
 @pytest.mark.parametrize("M", [4, 200])
 @pytest.mark.parametrize("zp", [True, False])
 def test_gemm_one_hot_reproduces_decoded_weights(M, zp):
