@@ -11,13 +11,16 @@ step streams ~3.3 GB and no launch is served from the 256 MB Infinity Cache.
 value  = algorithmic bytes of a step / step time, GB/s (whole job, one GPU)
 roofline = the GEMV kernel against 8 TB/s HBM; its average launch time comes
          from HIP events around back-to-back launches on the launch stream.
-legs   = awq_pack, batched-decode awq_gemm (M = 4/16/64), prefill awq_gemm
-         (M = 2048, 70B-shaped MLP), GEMV vs GEMM at M = 1.
+legs   = awq_pack, fused-projection decode (qkv and gate_up as one awq_gemv
+         each), batched-decode awq_gemm (M = 4/16/64; GEMV vs GEMM at M = 1),
+         prefill awq_gemm (M = 2048, 70B-shaped MLP).
 cpu_baseline = the CPU oracle (decode + fp64 product) on one block, timed on
          the host; a reported reference, not a target.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--blocks 32]
                        [--legs all|none|<comma list>] [--no-cpu-baseline]
+       python bench.py --leg-only pack|fused|batched|prefill   (one leg, for profiling)
+       python bench.py --copy-calibration | --summarize DB... [--kernel-filter NAME]
 """
 from __future__ import annotations
 
@@ -56,6 +59,8 @@ def parse():
     ap.add_argument("--summarize", nargs="+", metavar="DB",
                     help="print a per-kernel summary of rocprofv3 result databases and exit")
     ap.add_argument("--kernel-filter", default=None, help="with --summarize: only kernels whose name contains this")
+    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "prefill"],
+                    help="run just this leg (no headline, no CPU baseline) and print its JSON; for profiling")
     return ap.parse_args()
 
 
@@ -275,8 +280,12 @@ def leg_batched_decode(torch, awq, workloads, g=128, zp=True, blocks=16, iters=2
     return out
 
 
-def leg_prefill(torch, awq, workloads, g=128, zp=True, iters=5):
-    """M = 2048 prefill through the two 70B-shaped MLP linears (matrix-core bound)."""
+def leg_prefill(torch, awq, workloads, g=128, zp=True, iters=30, warm=20):
+    """M = 2048 prefill through the two 70B-shaped MLP linears (matrix-core bound).
+
+    The kernel runs at the chip's power limit, where the clock takes several
+    milliseconds of load to settle: ``warm`` untimed launches (about 20 ms)
+    come before the ``iters`` timed ones."""
     out = {}
     M = 2048
     for li, (name, K, N) in enumerate(workloads.LLAMA70B_MLP):
@@ -285,7 +294,7 @@ def leg_prefill(torch, awq, workloads, g=128, zp=True, iters=5):
         del W
         X = torch.from_numpy(workloads.activations(M, K, cfg=4, layer=li)).cuda()
         Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
-        for _ in range(2):
+        for _ in range(warm):
             awq.awq_gemm(X, qw, sc, qz, N, K, g, zp, y=Y)
         torch.cuda.synchronize()
         tm = Timer(torch)
@@ -404,6 +413,12 @@ def main():
         return 0
 
     g, zp = 128, True
+    if args.leg_only in ("fused", "batched", "prefill"):
+        fn = {"fused": lambda: leg_fused_decode(torch, awq, workloads, g, zp, blocks=args.blocks),
+              "batched": lambda: leg_batched_decode(torch, awq, workloads, g, zp),
+              "prefill": lambda: leg_prefill(torch, awq, workloads, g, zp)}[args.leg_only]
+        print(json.dumps({"leg": args.leg_only, "result": fn()}), flush=True)
+        return 0
     log(f"building {args.blocks} decode blocks")
     layers, reps = build_decode_block(torch, awq, workloads, args.blocks, g, zp)
     step_bytes = args.blocks * sum(algorithmic_bytes(1, L["N"], L["K"], g, zp) for L in layers)
@@ -480,6 +495,9 @@ def main():
     legs = set(args.legs.split(",")) if args.legs not in ("all", "none") else (
         {"pack", "fused", "batched", "prefill"} if args.legs == "all" else set())
     out_legs = {}
+    if args.leg_only == "pack":
+        print(json.dumps({"leg": "pack", "result": leg_pack(torch, awq, layers, g, zp)}), flush=True)
+        return 0
     if "pack" in legs:
         log("leg: pack")
         out_legs["pack"] = leg_pack(torch, awq, layers, g, zp)

@@ -157,18 +157,23 @@ def awq_gemv(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, qzero
 
 
 _WORKSPACES = {}
+_RETIRED_WORKSPACES = []
 
 
 def gemm_workspace(nbytes: int, device) -> torch.Tensor:
-    """A zero-initialised awq_gemm workspace of at least ``nbytes`` for the
-    current stream of ``device``, kept for later calls.  awq_gemm returns the
-    workspace's counters to zero, so calls in stream order can share it; each
-    stream gets its own, since concurrent calls must not share one."""
+    """The zero-initialised awq_gemm workspace of ``device`` (at least
+    ``nbytes``), kept for later calls.  awq_gemm returns the workspace's
+    counters to zero, so calls in stream order share it, including calls
+    captured into a HIP graph.  It is one buffer per device: calls that may
+    run concurrently on different streams must each pass a workspace of their
+    own (``torch.zeros(awq_gemm_workspace_bytes(...), dtype=torch.uint8)``)."""
     device = torch.device(device)
-    key = (device.index if device.index is not None else torch.cuda.current_device(),
-           torch.cuda.current_stream(device).cuda_stream)
+    key = device.index if device.index is not None else torch.cuda.current_device()
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            # a captured graph may still hold the old buffer's address: keep it alive
+            _RETIRED_WORKSPACES.append(ws)
         ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws

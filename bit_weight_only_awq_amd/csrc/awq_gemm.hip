@@ -368,14 +368,17 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
                                                          const uint16_t* __restrict__ scales,
                                                          const uint32_t* __restrict__ qzeros,
                                                          _Float16* __restrict__ Y, int M, int N, int K, int gshift,
-                                                         int tiles_m, int ldy) {
+                                                         int tiles_m, int group_m, int ldy) {
   constexpr int WN = 32 * NB;                 // wave tile width (N): 64, or 32 for half-width tiles
   constexpr int TBN = 4 * WN;                 // workgroup tile width: 256 or 128
   __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE_BYTES];  // [buffer][X | W']
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const int tiles_n = gridDim.x / tiles_m;
+  const int per_group = group_m * tiles_n, grp = tile / per_group, first_m = grp * group_m;
+  const int gm = min(tiles_m - first_m, group_m), r_in = tile - grp * per_group;
+  const int tm = first_m + r_in % gm, tn = r_in / gm;
   const int m0 = tm * BM, n0 = tn * TBN;
   const int rows_m = min(BM, M - m0), rows_n = min(TBN, N - n0);  // rows_n is a multiple of 8
   const int wm = (wave & 1) * 128, wn = (wave >> 1) * WN;
@@ -537,15 +540,20 @@ void launch_large_part(const _Float16* X, const uint32_t* qw, const uint16_t* sc
   constexpr int TBN = 128 * NB;
   const int G = K >> gs;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + TBN - 1) / TBN;
+  // tiles are ordered in groups of 4 tile rows (all tile columns of a group
+  // before the next group), so the 32-tile band that one XCD works on spans
+  // 4 row bands of X and 8 column bands of W instead of all row bands: about
+  // 35% less traffic from HBM / Infinity Cache into the XCDs' L2s
+  const int group_m = tiles_m < 4 ? tiles_m : 4;
   const uint32_t* qwp = qw + (size_t)n_base * (K >> 3);
   const uint16_t* scp = sc + scale_index(n_base, 0, G);
   const uint32_t* qzp = ZP ? qz + zero_word_index(n_base, 0, G) : qz;
   if (K % BK == 0)
     hipLaunchKernelGGL((gemm_large_kernel<ZP, false, NB>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, X, qwp, scp,
-                       qzp, Y + n_base, M, N, K, gs, tiles_m, ldy);
+                       qzp, Y + n_base, M, N, K, gs, tiles_m, group_m, ldy);
   else
     hipLaunchKernelGGL((gemm_large_kernel<ZP, true, NB>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, X, qwp, scp,
-                       qzp, Y + n_base, M, N, K, gs, tiles_m, ldy);
+                       qzp, Y + n_base, M, N, K, gs, tiles_m, group_m, ldy);
 }
 
 // 256x256 tiles; when the last wave of tiles over the compute units would run
