@@ -38,7 +38,9 @@ AWQ_ERR_UNSUPPORTED = -5
 AWQ_ERR_WORKSPACE = -6
 AWQ_ERR_HIP = -7
 
-EXPORTED = ("awq_pack", "awq_dequant", "awq_gemv", "awq_gemm", "awq_gemm_workspace_bytes", "awq_strerror")
+EXPORTED = ("awq_pack", "awq_dequant", "awq_gemv", "awq_gemm", "awq_gemm_workspace_bytes", "awq_strerror",
+            "awq_scale_candidates", "awq_scale_candidates_workspace_bytes", "awq_scale_loss",
+            "awq_scale_loss_workspace_bytes")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -71,6 +73,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.awq_gemm_workspace_bytes.restype = SZ
     lib.awq_strerror.argtypes = [ctypes.c_int]
     lib.awq_strerror.restype = ctypes.c_char_p
+    lib.awq_scale_candidates.argtypes = [P, I32, I32, P, I32, P, P, SZ, P]
+    lib.awq_scale_candidates.restype = ctypes.c_int
+    lib.awq_scale_candidates_workspace_bytes.argtypes = [I32, I32]
+    lib.awq_scale_candidates_workspace_bytes.restype = SZ
+    lib.awq_scale_loss.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, SZ, P, P]
+    lib.awq_scale_loss.restype = ctypes.c_int
+    lib.awq_scale_loss_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.awq_scale_loss_workspace_bytes.restype = SZ
     _lib = lib
     return lib
 
@@ -256,3 +266,57 @@ def linear(x: torch.Tensor, pw: PackedWeight, version: str = "auto") -> torch.Te
     fn = awq_gemv if v == "GEMV" else awq_gemm
     y = fn(x2, pw.qweight, pw.scales, pw.qzeros, pw.N, pw.K, pw.group_size, pw.zero_point)
     return y.reshape(*x.shape[:-1], pw.N)
+
+
+def awq_scale_candidates(x: torch.Tensor, alphas) -> torch.Tensor:
+    """Candidate per-channel scales s[c] = max(mean |x|, 1e-4) ** alphas[c] for fp16
+    calibration activations ``x`` [M, K]; returns fp32 [len(alphas), K] on x's device."""
+    lib = load_library()
+    alphas = [float(a) for a in alphas]
+    M, K = x.shape
+    s = torch.empty((len(alphas), K), dtype=torch.float32, device=x.device)
+    ws = torch.empty(max(1, int(lib.awq_scale_candidates_workspace_bytes(M, K))), dtype=torch.uint8, device=x.device)
+    arr = (ctypes.c_float * len(alphas))(*alphas)
+    st = lib.awq_scale_candidates(_ptr(x), M, K, ctypes.cast(arr, ctypes.c_void_p), len(alphas), _ptr(s), _ptr(ws),
+                                  ws.numel(), _stream(x))
+    _check(st, "awq_scale_candidates")
+    return s
+
+
+def awq_scale_loss(x: torch.Tensor, w: torch.Tensor, s: torch.Tensor, group_size: int = 128,
+                   zero_point: bool = True) -> torch.Tensor:
+    """L(s_c) = ||Q(W s_c)(s_c^-1 X) - W X||_F for every row s_c of the fp32 ``s``
+    [count, K]; ``x`` fp16 [M, K], ``w`` fp16 [N, K].  Returns fp64 [count] on the GPU."""
+    lib = load_library()
+    M, K = x.shape
+    N = w.shape[0]
+    s2 = s.reshape(-1, K)
+    count = s2.shape[0]
+    loss = torch.empty(count, dtype=torch.float64, device=x.device)
+    ws = torch.empty(max(1, int(lib.awq_scale_loss_workspace_bytes(count, M, N, K))), dtype=torch.uint8,
+                     device=x.device)
+    st = lib.awq_scale_loss(_ptr(x), _ptr(w), _ptr(s2), count, M, N, K, group_size, int(bool(zero_point)), _ptr(ws),
+                            ws.numel(), _ptr(loss), _stream(x))
+    _check(st, "awq_scale_loss")
+    return loss
+
+
+class ScaleSearch(NamedTuple):
+    alpha: float
+    scale: torch.Tensor   # fp32 [K], the chosen s
+    losses: list          # L(s) of every candidate, in the order of alphas
+    alphas: list
+
+
+def search_scale(x: torch.Tensor, w: torch.Tensor, group_size: int = 128, zero_point: bool = True,
+                 alphas=None) -> ScaleSearch:
+    """Activation-aware scale search: evaluate L(s) for s = a ** alpha over a
+    grid of exponents (default 0, 1/20, ..., 19/20) and keep the best.  The
+    chosen s is applied as W * s before packing and s^-1 on the activations."""
+    if alphas is None:
+        alphas = [i / 20 for i in range(20)]
+    alphas = [float(a) for a in alphas]
+    S = awq_scale_candidates(x, alphas)
+    losses = awq_scale_loss(x, w, S, group_size, zero_point).cpu().tolist()
+    best = min(range(len(alphas)), key=lambda i: (losses[i], i))
+    return ScaleSearch(alphas[best], S[best].clone(), losses, alphas)

@@ -21,7 +21,7 @@ LIB_NAME = "libawq_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 ARCH = "gfx950"
-SOURCES = ("awq_api.hip", "awq_pack.hip", "awq_gemv.hip", "awq_gemm.hip")
+SOURCES = ("awq_api.hip", "awq_pack.hip", "awq_gemv.hip", "awq_gemm.hip", "awq_scale.hip")
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

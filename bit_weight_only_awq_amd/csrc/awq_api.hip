@@ -99,6 +99,41 @@ int awq_gemm(const void* x, const uint32_t* qweight, const void* scales, const u
                                    static_cast<hipStream_t>(stream)));
 }
 
+size_t awq_scale_candidates_workspace_bytes(int32_t M, int32_t K) {
+  if (M < 1 || K < 8 || K > kMaxDim || (K & 7) != 0) return 0;
+  return awq::scale_candidates_workspace_bytes(M, K);
+}
+
+int awq_scale_candidates(const void* x, int32_t M, int32_t K, const float* alphas, int32_t count, float* s,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 1 || K < 8 || K > kMaxDim || (K & 7) != 0) return AWQ_ERR_SHAPE;
+  if (count < 1 || count > awq::kMaxScaleCandidates) return AWQ_ERR_SHAPE;
+  if (!x || !alphas || !s || !workspace) return AWQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(s) || !aligned16(workspace)) return AWQ_ERR_ALIGN;
+  if (workspace_bytes < awq::scale_candidates_workspace_bytes(M, K)) return AWQ_ERR_WORKSPACE;
+  return from_hip(awq::launch_scale_candidates(x, M, K, alphas, count, s, workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t awq_scale_loss_workspace_bytes(int32_t count, int32_t M, int32_t N, int32_t K) {
+  if (count < 1 || count > 65535 || M < 1 || N < 8 || K < 8 || N > kMaxDim || K > kMaxDim) return 0;
+  return awq::scale_loss_workspace_bytes(count, M, N, K);
+}
+
+int awq_scale_loss(const void* x, const void* w, const float* s, int32_t count, int32_t M, int32_t N, int32_t K,
+                   int32_t group_size, int32_t zero_point, void* workspace, size_t workspace_bytes, double* loss,
+                   void* stream) {
+  int st = check_weight_shape(N, K, group_size);
+  if (st != AWQ_OK) return st;
+  if (M < 1 || count < 1 || count > 65535) return AWQ_ERR_SHAPE;
+  if (!x || !w || !s || !workspace || !loss) return AWQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(loss) & 7u) != 0)
+    return AWQ_ERR_ALIGN;
+  if (workspace_bytes < awq::scale_loss_workspace_bytes(count, M, N, K)) return AWQ_ERR_WORKSPACE;
+  return from_hip(awq::launch_scale_loss(x, w, s, count, M, N, K, group_size, zero_point != 0, workspace, loss,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 const char* awq_strerror(int status) {
   switch (status) {
     case AWQ_OK: return "ok";

@@ -26,4 +26,20 @@ hipError_t launch_gemm(const void* x, const uint32_t* qweight, const void* scale
                        void* y, int M, int N, int K, int group_size, bool zero_point, void* workspace,
                        hipStream_t stream);
 
+// Candidate scales for the activation-aware scale search (at most
+// kMaxScaleCandidates exponents per call; `alphas` is a host array).
+constexpr int kMaxScaleCandidates = 64;
+size_t scale_candidates_workspace_bytes(int M, int K);
+hipError_t launch_scale_candidates(const void* x, int M, int K, const float* alphas, int count, float* s,
+                                   void* workspace, hipStream_t stream);
+
+// e[c][n][k] = fp16(Dq(Q(fp16(w[n][k] * s[c][k]))) / s[c][k] - w[n][k]) for each candidate c.
+hipError_t launch_scale_error(const void* w, const float* s, int count, int N, int K, int group_size, bool zero_point,
+                              void* e, hipStream_t stream);
+
+// loss[c] = || X e_c^T ||_F for each candidate scale vector s[c].
+size_t scale_loss_workspace_bytes(int count, int M, int N, int K);
+hipError_t launch_scale_loss(const void* x, const void* w, const float* s, int count, int M, int N, int K,
+                             int group_size, bool zero_point, void* workspace, double* loss, hipStream_t stream);
+
 }  // namespace awq

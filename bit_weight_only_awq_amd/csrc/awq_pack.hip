@@ -22,13 +22,55 @@ namespace {
 constexpr int kPackThreads = 256;  // 8 rows x 32 lanes
 constexpr float kRangeFloor = 1e-5f;
 
+// Scale and zero point of the group a lane's 8 weights belong to.  A group of
+// g channels is GW = g/8 consecutive lanes of one row, reduced with butterfly
+// shuffles (GW divides 32, so a group never leaves its half-wave, and all
+// lanes of a group are active or inactive together).  s16 is the fp16 scale,
+// s its fp32 value, zf the zero point as a float.
+template <int GW, bool ZP>
+__device__ __forceinline__ void group_scale_zero(const float (&a)[8], _Float16& s16, float& s, float& zf) {
+  if constexpr (ZP) {
+    float mn = a[0], mx = a[0];
+#pragma unroll
+    for (int c = 1; c < 8; ++c) {
+      mn = fminf(mn, a[c]);
+      mx = fmaxf(mx, a[c]);
+    }
+#pragma unroll
+    for (int off = 1; off < GW; off <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, off));
+      mx = fmaxf(mx, __shfl_xor(mx, off));
+    }
+    float rng = mx - mn;
+    if (rng < kRangeFloor) rng = kRangeFloor;
+    s16 = (_Float16)(rng / 15.0f);
+    s = (float)s16;
+    zf = rintf(-mn / s);
+    zf = fminf(fmaxf(zf, 0.0f), 15.0f);
+  } else {
+    float amax = fabsf(a[0]);
+#pragma unroll
+    for (int c = 1; c < 8; ++c) amax = fmaxf(amax, fabsf(a[c]));
+#pragma unroll
+    for (int off = 1; off < GW; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if (amax < kRangeFloor) amax = kRangeFloor;
+    s16 = (_Float16)(amax / 7.0f);
+    s = (float)s16;
+    zf = 8.0f;
+  }
+}
+
+// Code of one weight: clamp(rne(a / s) + z, 0, 15), as a float.
+__device__ __forceinline__ float code_of(float a, float s, float zf) {
+  const float v = rintf(a / s) + zf;
+  return fminf(fmaxf(v, 0.0f), 15.0f);
+}
+
 // One block quantizes one octet of rows (n0 .. n0+7).  Thread t works on row
 // n0 + (t >> 5); its lane l = t & 31 owns one packed word (8 channels) of each
-// 256-channel pass over the row.  A group of g channels is GW = g/8
-// consecutive lanes of the same row, reduced with butterfly shuffles (GW
-// divides 32, so a group never leaves its half-wave).  The octet's scales and
-// zero points are staged in LDS and stored as one 16-byte scale vector and one
-// zero-point word per group (row-octet-major layout).
+// 256-channel pass over the row.  The octet's scales and zero points are
+// staged in LDS and stored as one 16-byte scale vector and one zero-point word
+// per group (row-octet-major layout).
 template <int GW, bool ZP>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restrict__ w, int N, int K,
                                                             uint32_t* __restrict__ qweight,
@@ -58,43 +100,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restr
 
     float s, zf;
     _Float16 s16;
-    if constexpr (ZP) {
-      float mn = a[0], mx = a[0];
-#pragma unroll
-      for (int c = 1; c < 8; ++c) {
-        mn = fminf(mn, a[c]);
-        mx = fmaxf(mx, a[c]);
-      }
-#pragma unroll
-      for (int off = 1; off < GW; off <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, off));
-        mx = fmaxf(mx, __shfl_xor(mx, off));
-      }
-      float rng = mx - mn;
-      if (rng < kRangeFloor) rng = kRangeFloor;
-      s16 = (_Float16)(rng / 15.0f);
-      s = (float)s16;
-      zf = rintf(-mn / s);
-      zf = fminf(fmaxf(zf, 0.0f), 15.0f);
-    } else {
-      float amax = fabsf(a[0]);
-#pragma unroll
-      for (int c = 1; c < 8; ++c) amax = fmaxf(amax, fabsf(a[c]));
-#pragma unroll
-      for (int off = 1; off < GW; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-      if (amax < kRangeFloor) amax = kRangeFloor;
-      s16 = (_Float16)(amax / 7.0f);
-      s = (float)s16;
-      zf = 8.0f;
-    }
+    group_scale_zero<GW, ZP>(a, s16, s, zf);
 
     uint32_t word = 0;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float v = rintf(a[c] / s) + zf;
-      v = fminf(fmaxf(v, 0.0f), 15.0f);
-      word |= (uint32_t)v << nibble_shift(c);
-    }
+    for (int c = 0; c < 8; ++c) word |= (uint32_t)code_of(a[c], s, zf) << nibble_shift(c);
     if (active) qweight[(size_t)n * kw + j] = word;
 
     if (active && (l % GW) == 0) {
@@ -114,6 +124,62 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restr
       }
     }
     __syncthreads();
+  }
+}
+
+// Weight error of the activation-aware scaling, for the objective
+//   L(s) = || Q(W diag(s)) (diag(s)^-1 X) - W X ||
+// ("AI-Research-SKILLs AWQ 高级使用指南", section 算法原理).  For candidate c
+// (blockIdx.y) with per-input-channel scales s_c:
+//   e[n][k] = fp16( w'[n][k] / s_c[k] - w[n][k] ),  w' = Dq(Q(fp16(w[n][k] * s_c[k])))
+// so that L(s_c) = || X e^T ||_F: one dense product instead of two.  The
+// quantizer is the one of pack_kernel (same code, same fp32 order); w * s is
+// an fp32 product rounded to fp16, w' = (q - z) * s is exact, and the division
+// and subtraction are single fp32 roundings.  Same block shape as pack_kernel:
+// one octet of rows per block.
+template <int GW, bool ZP>
+__global__ __launch_bounds__(kPackThreads) void scale_error_kernel(const u32x4* __restrict__ w,
+                                                                   const float* __restrict__ s_all, int N, int K,
+                                                                   u32x4* __restrict__ e_all) {
+  const int t = threadIdx.x;
+  const int r = t >> 5, l = t & 31;
+  const int n = blockIdx.x * 8 + r;
+  const int kw = K >> 3;
+  const float* sc = s_all + (size_t)blockIdx.y * K;
+  u32x4* e = e_all + (size_t)blockIdx.y * N * kw;
+
+  for (int w0 = 0; w0 < kw; w0 += 32) {
+    const int j = w0 + l;
+    const bool active = j < kw;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    float4_t s0 = {1.f, 1.f, 1.f, 1.f}, s1 = {1.f, 1.f, 1.f, 1.f};
+    if (active) {
+      raw = w[(size_t)n * kw + j];
+      s0 = *reinterpret_cast<const float4_t*>(sc + 8 * j);
+      s1 = *reinterpret_cast<const float4_t*>(sc + 8 * j + 4);
+    }
+    const half8_t h = as_half8(raw);
+    float sv[8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      sv[c] = s0[c];
+      sv[c + 4] = s1[c];
+    }
+    float a[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a[c] = (float)(_Float16)((float)h[c] * sv[c]);
+
+    float s, zf;
+    _Float16 s16;
+    group_scale_zero<GW, ZP>(a, s16, s, zf);
+
+    half8_t out;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float wq = (code_of(a[c], s, zf) - zf) * s;
+      out[c] = (_Float16)(wq / sv[c] - (float)h[c]);
+    }
+    if (active) e[(size_t)n * kw + j] = __builtin_bit_cast(u32x4, out);
   }
 }
 
@@ -164,7 +230,29 @@ hipError_t launch_pack_zp(const void* w, int N, int K, int group_size, uint32_t*
 
 int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 128 ? 7 : 8; }
 
+template <bool ZP>
+hipError_t launch_scale_error_zp(const void* w, const float* s, int count, int N, int K, int group_size, void* e,
+                                 hipStream_t stream) {
+  const dim3 grid(N / 8, count), block(kPackThreads);
+  const u32x4* wv = static_cast<const u32x4*>(w);
+  u32x4* ev = static_cast<u32x4*>(e);
+  switch (group_size) {
+    case 32: hipLaunchKernelGGL((scale_error_kernel<4, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
+    case 64: hipLaunchKernelGGL((scale_error_kernel<8, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
+    case 128: hipLaunchKernelGGL((scale_error_kernel<16, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
+    case 256: hipLaunchKernelGGL((scale_error_kernel<32, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_scale_error(const void* w, const float* s, int count, int N, int K, int group_size, bool zero_point,
+                              void* e, hipStream_t stream) {
+  return zero_point ? launch_scale_error_zp<true>(w, s, count, N, K, group_size, e, stream)
+                    : launch_scale_error_zp<false>(w, s, count, N, K, group_size, e, stream);
+}
 
 hipError_t launch_pack(const void* w, int N, int K, int group_size, bool zero_point, uint32_t* qweight,
                        void* scales, uint32_t* qzeros, hipStream_t stream) {

@@ -1,0 +1,260 @@
+// Activation-aware scale search: candidate per-channel scales from activation
+// statistics (awq_scale_candidates) and the reconstruction error L(s) of each
+// candidate (awq_scale_loss).
+//
+// "AI-Research-SKILLs AWQ 高级使用指南", section 算法原理: AWQ finds the ~1% of
+// salient weight channels from the distribution of the activations, multiplies
+// them by a scaling factor before quantization, and chooses the scaling to
+// make the reconstruction error
+//   L(s) = || Q(W * s)(s^-1 * X) - W * X ||
+// small.  "AWQ Activation-aware Weight Quantization (Lin 2023年)" lists the
+// ingredients as activation statistics and per-channel scaling.  The pages do
+// not give the family of candidate scales; the one used here is
+//   s_k = a_k ^ alpha,  a_k = max(mean_m |x_mk|, 1e-4)
+// for a grid of exponents alpha (alpha = 0 is plain round-to-nearest).
+//
+// L(s) is evaluated as || X e^T ||_F with e = Q(W s) s^-1 - W (built by
+// scale_error_kernel next to the quantizer): the same quantity, one dense
+// product instead of two.  The product runs on the fp16 matrix cores with fp32
+// accumulation; the squares are summed per tile and the tiles are added in a
+// fixed order in fp64 (deterministic).
+#include "awq_device.hpp"
+#include "awq_launch.hpp"
+
+namespace awq {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Activation statistics and candidates.
+// ---------------------------------------------------------------------------
+constexpr int kStatRows = 64;  // rows of X summed per partial
+constexpr float kActFloor = 1e-4f;
+
+// partial[b][k] = sum over rows 64 b .. 64 b + 63 of |x_mk|, in row order.
+// One thread per channel; consecutive threads read consecutive channels.
+__global__ __launch_bounds__(256) void act_partial_kernel(const _Float16* __restrict__ x, int M, int K,
+                                                          float* __restrict__ partial) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= K) return;
+  const int m0 = blockIdx.y * kStatRows, m1 = min(M, m0 + kStatRows);
+  float acc = 0.0f;
+  for (int m = m0; m < m1; ++m) acc += fabsf((float)x[(size_t)m * K + k]);
+  partial[(size_t)blockIdx.y * K + k] = acc;
+}
+
+struct Alphas {
+  float v[kMaxScaleCandidates];
+};
+
+// a_k = max((sum of the partials in order) / M, 1e-4); s[c][k] = a_k ^ alpha_c.
+__global__ __launch_bounds__(256) void candidates_kernel(const float* __restrict__ partial, int nparts, int M, int K,
+                                                         Alphas alphas, int count, float* __restrict__ s) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= K) return;
+  float sum = 0.0f;
+  for (int b = 0; b < nparts; ++b) sum += partial[(size_t)b * K + k];
+  const float a = fmaxf(sum / (float)M, kActFloor);
+  for (int c = 0; c < count; ++c) s[(size_t)c * K + k] = alphas.v[c] == 0.0f ? 1.0f : powf(a, alphas.v[c]);
+}
+
+// ---------------------------------------------------------------------------
+// Sum of squares of X e_c^T.
+// ---------------------------------------------------------------------------
+// Buffer resource over `bytes` bytes at `base`: loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+constexpr int TM = 128, TN = 128, TK = 64;   // workgroup tile and K step
+constexpr int OP_BYTES = TM * TK * 2;        // one 128 x 64 fp16 operand tile in LDS (16 KiB)
+
+// 16-byte chunk c of LDS row r sits in slot c ^ ((r >> 1) & 7): with 128-byte
+// rows, 16 consecutive rows read at the same logical chunk hit 16 distinct
+// bank groups, and a 1 KiB run of slots is what one buffer-to-LDS load of 64
+// lanes x 16 bytes writes.
+__device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// Workgroup: 4 waves (2 x 2) of 64 x 64 outputs, 2 x 2 v_mfma_f32_32x32x16_f16
+// tiles each; grid (tiles, candidates).  Both operands stream from HBM into
+// LDS by buffer-to-LDS loads, double-buffered, one barrier per K step.  Rows
+// past M or N read as zero and add nothing to the sum.  Output: the fp64 sum
+// of the squares of the tile's 128 x 128 outputs (each square and the per-lane
+// sums in fp32, the wave and workgroup sums in a fixed order).
+template <bool KTAIL>
+__global__ __launch_bounds__(256) void sumsq_gemm_kernel(const _Float16* __restrict__ X,
+                                                         const _Float16* __restrict__ E_all, int M, int N, int K,
+                                                         int tiles_m, double* __restrict__ partial) {
+  // the two buffers of each operand are separate arrays, so the compiler can
+  // tell them apart and does not make reads of one wait for the loads into
+  // the other
+  __shared__ __attribute__((aligned(1024))) char lx0[OP_BYTES], lx1[OP_BYTES], le0[OP_BYTES], le1[OP_BYTES];
+  __shared__ double wsum[4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int tile = blockIdx.x;
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const int m0 = tm * TM, n0 = tn * TN;
+  const _Float16* E = E_all + (size_t)blockIdx.y * N * K;
+  const int rows_m = min(TM, M - m0), rows_n = min(TN, N - n0);
+  const int nsteps = (K + TK - 1) / TK;
+
+  const __amdgpu_buffer_rsrc_t rx = rsrc(X + (size_t)m0 * K, (uint32_t)rows_m * K * 2);
+  const __amdgpu_buffer_rsrc_t re = rsrc(E + (size_t)n0 * K, (uint32_t)rows_n * K * 2);
+
+  // wave w fills rows 32 w .. 32 w + 31 of both tiles with 4 loads of 8 rows
+  // x 128 B each; lane l of load j writes slot l of that 1 KiB run: row
+  // 32 w + 8 j + l / 8, physical chunk l % 8, holding the logical chunk that
+  // swizzles there (the swizzle is an involution)
+  int chunk[4];
+  uint32_t off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 32 * wave + 8 * j + (lane >> 3);
+    chunk[j] = swz_chunk(row, lane & 7);
+    off[j] = (uint32_t)row * K * 2 + chunk[j] * 16;
+  }
+  // `buf` is a constant at every call site (the K loop below is unrolled by two)
+  auto load = [&](int step, int buf) {
+    char* dx = (buf ? lx1 : lx0) + wave * 4096;
+    char* de = (buf ? le1 : le0) + wave * 4096;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t o = off[j];
+      if constexpr (KTAIL) {  // channels past K of the last step load as zero
+        if (step * TK + 8 * chunk[j] >= K) o = kOutOfRange;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(dx + 1024 * j), 16, o,
+                                               step * TK * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (__attribute__((address_space(3))) void*)(de + 1024 * j), 16, o,
+                                               step * TK * 2, 0, 0);
+    }
+  };
+
+  float16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  const int fi = lane & 31, fh = lane >> 5;  // fragment row and k-half of this lane
+  const int fsw = (fi >> 1) & 7;             // swizzle of the fragment rows (bases are multiples of 32)
+
+  auto compute = [&](int buf) {
+    const char* xa = (buf ? lx1 : lx0) + (wm + fi) * 128;
+    const char* eb = (buf ? le1 : le0) + (wn + fi) * 128;
+#pragma unroll
+    for (int ks = 0; ks < TK / 16; ++ks) {
+      const int slot = 16 * ((2 * ks + fh) ^ fsw);
+      half8_t af[2], bf[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) af[a] = *reinterpret_cast<const half8_t*>(xa + 32 * 128 * a + slot);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) bf[b] = *reinterpret_cast<const half8_t*>(eb + 32 * 128 * b + slot);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+    }
+  };
+
+  // Two steps per trip.  The loads of a step past the end stay inside the
+  // resources (or read zero) and land in a buffer no one reads again.
+  load(0, 0);
+  __syncthreads();
+  int step = 0;
+  // the scheduling barriers keep each step's loads ahead of the multiplies
+  // that hide their latency
+  for (; step + 1 < nsteps; step += 2) {
+    load(step + 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+    __syncthreads();
+    load(step + 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+    __syncthreads();
+  }
+  if (step < nsteps) compute(0);
+
+  float ss = 0.0f;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ss += acc[a][b][r] * acc[a][b][r];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  if (lane == 0) wsum[wave] = (double)ss;
+  __syncthreads();
+  if (t == 0) partial[(size_t)blockIdx.y * gridDim.x + tile] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+}
+
+// loss[c] = sqrt(sum of candidate c's tile partials), summed by one workgroup
+// in a fixed order.
+__global__ __launch_bounds__(256) void loss_finalize_kernel(const double* __restrict__ partial, int tiles,
+                                                            double* __restrict__ loss) {
+  __shared__ double red[256];
+  const int t = threadIdx.x;
+  const double* p = partial + (size_t)blockIdx.x * tiles;
+  double v = 0.0;
+  for (int i = t; i < tiles; i += 256) v += p[i];
+  red[t] = v;
+  __syncthreads();
+  for (int h = 128; h >= 1; h >>= 1) {
+    if (t < h) red[t] += red[t + h];
+    __syncthreads();
+  }
+  if (t == 0) loss[blockIdx.x] = sqrt(red[0]);
+}
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t scale_candidates_workspace_bytes(int M, int K) {
+  return align256((size_t)((M + kStatRows - 1) / kStatRows) * K * 4);
+}
+
+hipError_t launch_scale_candidates(const void* x, int M, int K, const float* alphas, int count, float* s,
+                                   void* workspace, hipStream_t stream) {
+  const int nparts = (M + kStatRows - 1) / kStatRows;
+  float* partial = static_cast<float*>(workspace);
+  hipLaunchKernelGGL(act_partial_kernel, dim3((K + 255) / 256, nparts), dim3(256), 0, stream,
+                     static_cast<const _Float16*>(x), M, K, partial);
+  Alphas a;
+  for (int c = 0; c < kMaxScaleCandidates; ++c) a.v[c] = c < count ? alphas[c] : 0.0f;
+  hipLaunchKernelGGL(candidates_kernel, dim3((K + 255) / 256), dim3(256), 0, stream, partial, nparts, M, K, a, count,
+                     s);
+  return hipGetLastError();
+}
+
+size_t scale_loss_workspace_bytes(int count, int M, int N, int K) {
+  const size_t tiles = (size_t)((M + TM - 1) / TM) * ((N + TN - 1) / TN);
+  return align256((size_t)count * N * K * 2) + align256((size_t)count * tiles * 8);
+}
+
+hipError_t launch_scale_loss(const void* x, const void* w, const float* s, int count, int M, int N, int K,
+                             int group_size, bool zero_point, void* workspace, double* loss, hipStream_t stream) {
+  const int tiles_m = (M + TM - 1) / TM, tiles_n = (N + TN - 1) / TN;
+  char* ws = static_cast<char*>(workspace);
+  _Float16* e = reinterpret_cast<_Float16*>(ws);
+  double* partial = reinterpret_cast<double*>(ws + align256((size_t)count * N * K * 2));
+  hipError_t err = launch_scale_error(w, s, count, N, K, group_size, zero_point, e, stream);
+  if (err != hipSuccess) return err;
+  const dim3 grid(tiles_m * tiles_n, count);
+  if (K % TK == 0)
+    hipLaunchKernelGGL(sumsq_gemm_kernel<false>, grid, dim3(256), 0, stream, static_cast<const _Float16*>(x), e, M, N,
+                       K, tiles_m, partial);
+  else
+    hipLaunchKernelGGL(sumsq_gemm_kernel<true>, grid, dim3(256), 0, stream, static_cast<const _Float16*>(x), e, M, N,
+                       K, tiles_m, partial);
+  hipLaunchKernelGGL(loss_finalize_kernel, dim3(count), dim3(256), 0, stream, partial, tiles_m * tiles_n, loss);
+  return hipGetLastError();
+}
+
+}  // namespace awq

@@ -135,6 +135,52 @@ int awq_gemm(const void* x, const uint32_t* qweight, const void* scales, const u
 /* Bytes of workspace awq_gemm needs for this shape (0 when it needs none). */
 size_t awq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t group_size);
 
+/*
+ * awq_scale_candidates - candidate per-input-channel scales for the
+ * activation-aware scale search.
+ *
+ * "AI-Research-SKILLs AWQ 高级使用指南", section 算法原理: salient channels are
+ * found from the activation distribution and scaled up before quantization;
+ * "AWQ Activation-aware Weight Quantization (Lin 2023年)": activation
+ * statistics and per-channel scaling.  The pages give no candidate family;
+ * this one is
+ *   a_k = max(mean_m |x[m][k]|, 1e-4),   s[c][k] = a_k ^ alphas[c]
+ * (fp32; the mean is an fp32 sum in row order divided by M; alphas[c] == 0
+ * gives exactly 1).
+ * x       in   fp16 [M][K] calibration activations (device).
+ * alphas  in   HOST array of `count` exponents, 1 <= count <= 64.
+ * s       out  fp32 [count][K] (device).
+ * workspace: device scratch of awq_scale_candidates_workspace_bytes(M, K)
+ * bytes, 16-byte aligned, contents not needed before or after the call.
+ * K must be a multiple of 8.  Deterministic.
+ */
+int awq_scale_candidates(const void* x, int32_t M, int32_t K, const float* alphas, int32_t count, float* s,
+                         void* workspace, size_t workspace_bytes, void* stream);
+size_t awq_scale_candidates_workspace_bytes(int32_t M, int32_t K);
+
+/*
+ * awq_scale_loss - reconstruction error of the activation-aware scaling,
+ *   loss[c] = L(s_c) = || (X diag(s_c)^-1) . Q(fp16(W diag(s_c)))'^T - X . W^T ||_F
+ * ("AI-Research-SKILLs AWQ 高级使用指南", section 算法原理, the objective
+ * L(s) = ||Q(W * s)(s^-1 * X) - W * X||), for `count` candidate scale vectors.
+ * Q(.)' is the quantize-then-decode of awq_pack (same group size and zero
+ * point mode; W * s is an fp32 product rounded to fp16).
+ * x     in   fp16 [M][K] calibration activations.
+ * w     in   fp16 [N][K] unquantized weights.
+ * s     in   fp32 [count][K], every entry finite and > 0 (not checked).
+ * loss  out  fp64 [count] (device, 8-byte aligned).
+ * workspace: device scratch of awq_scale_loss_workspace_bytes(count, M, N, K)
+ * bytes (count * N * K * 2 for the per-candidate weight errors, plus the
+ * per-tile sums), 16-byte aligned; contents not needed before or after.
+ * Accuracy: the weight error Q(W s) s^-1 - W is formed in fp32 and rounded to
+ * fp16 (relative 2^-11), the product accumulates in fp32 and the sum of
+ * squares in fp64: |loss - L| <= 1e-3 * L.  Deterministic.
+ */
+int awq_scale_loss(const void* x, const void* w, const float* s, int32_t count, int32_t M, int32_t N, int32_t K,
+                   int32_t group_size, int32_t zero_point, void* workspace, size_t workspace_bytes, double* loss,
+                   void* stream);
+size_t awq_scale_loss_workspace_bytes(int32_t count, int32_t M, int32_t N, int32_t K);
+
 /* Static, NUL-terminated description of a status code. */
 const char* awq_strerror(int status);
 

@@ -45,6 +45,12 @@ of the repository):
    an exact w' need at most 27 significant bits, so each product is exact in
    fp64; only the summation rounds.
 7. L(s) = || (X diag(s)^-1) . Dq(f16(W diag(s)))^T - X . W^T ||_F in fp64.
+8. Activation-aware scale search ([P5] "算法原理": salient channels are found
+   from the activation distribution and scaled before quantization; [P4]
+   "主な特徴・仕組み": activation statistics, per-channel scaling).  The pages
+   give no candidate family; the reading taken is s = a^alpha with
+   a_k = max(mean_m |x_mk|, 1e-4) and alpha on a grid in [0, 1); the search
+   keeps the candidate with the smallest L(s) (the first one on ties).
 
 Parity pins: every function here is pinned by tests that do not re-type its
 formula (hand-worked examples, brute force over every fp16 value of a range,
@@ -280,3 +286,29 @@ def recon_loss(W16: np.ndarray, X: np.ndarray, s: np.ndarray, g: int, zero_point
     ref = np.asarray(X, dtype=np.float64) @ W16.astype(np.float64).T
     return float(np.linalg.norm(Xs @ Wq.T - ref))
 
+
+ACT_FLOOR = 1e-4
+
+
+def activation_scale(X16: np.ndarray) -> np.ndarray:
+    """Per-input-channel activation statistic a_k = max(mean_m |x_mk|, 1e-4)
+    (reading 8), fp64."""
+    X = np.asarray(X16, dtype=np.float64)
+    if X.ndim != 2 or X.shape[0] < 1:
+        raise ValueError("X must be [M, K] with M >= 1")
+    return np.maximum(np.abs(X).mean(axis=0), ACT_FLOOR)
+
+
+def scale_candidates(X16: np.ndarray, alphas) -> np.ndarray:
+    """Candidate scales s_c = a^alpha_c (reading 8), as fp32 [len(alphas), K];
+    alpha = 0 gives exactly 1."""
+    a = activation_scale(X16)
+    return np.stack([np.power(a, float(al)).astype(F32) for al in alphas])
+
+
+def search_scale(W16: np.ndarray, X16: np.ndarray, g: int, zero_point: bool, alphas):
+    """Evaluate L(s_c) (reading 7) for every candidate of reading 8 and return
+    (index of the smallest loss, the candidates, the losses)."""
+    S = scale_candidates(X16, alphas)
+    losses = [recon_loss(W16, X16, s, g, zero_point) for s in S]
+    return int(np.argmin(losses)), S, losses

@@ -124,3 +124,32 @@ def test_binding_rejects_host_tensors():
     w = torch.zeros((8, 128), dtype=torch.float16)
     with pytest.raises(ValueError):
         awq.awq_pack(w, 32, True)
+
+
+def test_scale_search_validation(lib):
+    alphas = (ctypes.c_float * 2)(0.0, 0.5)
+    cand = lambda M, K, cnt, **kw: lib.awq_scale_candidates(  # noqa: E731
+        kw.get("x", A) or None, M, K, ctypes.cast(alphas, ctypes.c_void_p) if kw.get("al", 1) else None, cnt,
+        kw.get("s", B) or None, kw.get("ws", C) or None, kw.get("wsb", 1 << 30), None)
+    assert cand(0, 64, 2) == awq.AWQ_ERR_SHAPE
+    assert cand(4, 12, 2) == awq.AWQ_ERR_SHAPE
+    assert cand(4, 64, 0) == awq.AWQ_ERR_SHAPE
+    assert cand(4, 64, 65) == awq.AWQ_ERR_SHAPE
+    assert cand(4, 64, 2, al=0) == awq.AWQ_ERR_NULL
+    assert cand(4, 64, 2, s=0) == awq.AWQ_ERR_NULL
+    assert cand(4, 64, 2, x=A + 2) == awq.AWQ_ERR_ALIGN
+    assert cand(4, 64, 2, wsb=0) == awq.AWQ_ERR_WORKSPACE
+    assert awq.load_library().awq_scale_candidates_workspace_bytes(100, 64) >= 2 * 64 * 4
+    loss = lambda cnt, M, N, K, g, **kw: lib.awq_scale_loss(  # noqa: E731
+        kw.get("x", A) or None, kw.get("w", B) or None, kw.get("s", C) or None, cnt, M, N, K, g, 1,
+        kw.get("ws", D) or None, kw.get("wsb", 1 << 40), kw.get("loss", E) or None, None)
+    assert loss(1, 4, 12, 128, 32) == awq.AWQ_ERR_SHAPE
+    assert loss(1, 4, 8, 100, 32) == awq.AWQ_ERR_GROUP
+    assert loss(0, 4, 8, 128, 32) == awq.AWQ_ERR_SHAPE
+    assert loss(1, 0, 8, 128, 32) == awq.AWQ_ERR_SHAPE
+    assert loss(1, 4, 8, 128, 32, loss=0) == awq.AWQ_ERR_NULL
+    assert loss(1, 4, 8, 128, 32, loss=E + 4) == awq.AWQ_ERR_ALIGN
+    assert loss(1, 4, 8, 128, 32, s=C + 8) == awq.AWQ_ERR_ALIGN
+    need = awq.load_library().awq_scale_loss_workspace_bytes(3, 4, 8, 128)
+    assert need >= 3 * 8 * 128 * 2
+    assert loss(3, 4, 8, 128, 32, wsb=need - 1) == awq.AWQ_ERR_WORKSPACE

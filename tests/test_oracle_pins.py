@@ -324,6 +324,34 @@ def check_recon_loss(seed=7):
         assert O.recon_loss(W, X, s_rand, 64, zp) >= 0.0
 
 
+def check_scale_candidates():
+    # a = mean |x| per channel with the 1e-4 floor: [2, 1, 1e-4, 0.5]
+    X = np.array([[1, -2, 0, 0.5], [3, 0, 0, -0.5]], np.float16)
+    a = O.activation_scale(X)
+    assert np.array_equal(a, np.array([2.0, 1.0, 1e-4, 0.5]))
+    S = O.scale_candidates(X, [0.0, 0.5, 1.0])
+    assert S.dtype == np.float32 and S.shape == (3, 4)
+    assert np.array_equal(S[0], np.ones(4, np.float32))
+    assert np.array_equal(S[2], np.array([2.0, 1.0, 1e-4, 0.5], np.float32))
+    assert np.array_equal(S[1], np.sqrt(np.array([2.0, 1.0, 1e-4, 0.5])).astype(np.float32))
+
+
+def check_search_scale():
+    W = workloads.weight(64, 256, cfg=96, layer=1)
+    X = workloads.activations(64, 256, cfg=96, layer=1)
+    alphas = [i / 10 for i in range(10)]
+    best, S, losses = O.search_scale(W, X, 64, True, alphas)
+    assert len(losses) == 10 and S.shape == (10, 256)
+    # alpha = 0 is plain round-to-nearest: s = 1
+    assert losses[0] == O.recon_loss(W, X, np.ones(256, np.float32), 64, True)
+    assert losses[best] == min(losses) and all(losses[best] < losses[i] for i in range(best))
+    # the outlier channels (x20) get the largest scales for alpha > 0
+    out = np.argsort(O.activation_scale(X))[-3:]
+    assert np.all(S[5][out] > np.median(S[5]))
+    # with 1% outlier channels, scaling them protects the weights that meet them
+    assert best > 0 and losses[best] < 0.8 * losses[0]
+
+
 def check_matmul_exact(seed=8):
     W = workloads.weight(512, 512, cfg=0, layer=0, seed=0)
     X = workloads.activations(1, 512, cfg=0, layer=0, seed=0)
@@ -392,6 +420,14 @@ def test_recon_loss():
     check_recon_loss()
 
 
+def test_scale_candidates():
+    check_scale_candidates()
+
+
+def test_search_scale():
+    check_search_scale()
+
+
 def test_matmul_ref_against_fsum():
     check_matmul_exact()
 
@@ -433,6 +469,8 @@ ALL_CHECKS = (
     check_layout,
     check_recon_loss,
     check_matmul_exact,
+    check_scale_candidates,
+    check_search_scale,
 )
 
 
@@ -459,6 +497,9 @@ MUTATIONS = {
     "dequant_drops_zero": None,
     "matmul_wrong_operand_index": None,
     "recon_loss_scales_x_by_s": None,
+    "act_stat_max_not_mean": None,
+    "candidate_inverse_power": None,
+    "search_keeps_largest_loss": None,
 }
 
 
@@ -516,6 +557,20 @@ def _patch_function(mp, name):
             return float(np.linalg.norm(Xs @ Wq.T - ref))
 
         mp.setattr(O, "recon_loss", rl)
+    elif name == "act_stat_max_not_mean":
+        mp.setattr(O, "activation_scale",
+                   lambda X16: np.maximum(np.abs(np.asarray(X16, np.float64)).max(axis=0), O.ACT_FLOOR))
+    elif name == "candidate_inverse_power":
+        mp.setattr(O, "scale_candidates", lambda X16, alphas: np.stack(
+            [np.power(O.activation_scale(X16), -float(al)).astype(np.float32) for al in alphas]))
+    elif name == "search_keeps_largest_loss":
+        orig_search = O.search_scale
+
+        def search(W16, X16, g, zero_point, alphas):
+            _, S, losses = orig_search(W16, X16, g, zero_point, alphas)
+            return int(np.argmax(losses)), S, losses
+
+        mp.setattr(O, "search_scale", search)
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
