@@ -13,13 +13,14 @@ roofline = the GEMV kernel against 8 TB/s HBM; its average launch time comes
          from HIP events around back-to-back launches on the launch stream.
 legs   = awq_pack, fused-projection decode (qkv and gate_up as one awq_gemv
          each), batched-decode awq_gemm (M = 4/16/64; GEMV vs GEMM at M = 1),
-         prefill awq_gemm (M = 2048, 70B-shaped MLP).
+         prefill awq_gemm (M = 2048, 70B-shaped MLP), activation-aware scale
+         search (L(s) for 20 candidates over 512 calibration tokens).
 cpu_baseline = the CPU oracle (decode + fp64 product) on one block, timed on
          the host; a reported reference, not a target.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--blocks 32]
                        [--legs all|none|<comma list>] [--no-cpu-baseline]
-       python bench.py --leg-only pack|fused|batched|prefill   (one leg, for profiling)
+       python bench.py --leg-only pack|fused|batched|prefill|scale   (one leg, for profiling)
        python bench.py --copy-calibration | --summarize DB... [--kernel-filter NAME]
 """
 from __future__ import annotations
@@ -59,7 +60,7 @@ def parse():
     ap.add_argument("--summarize", nargs="+", metavar="DB",
                     help="print a per-kernel summary of rocprofv3 result databases and exit")
     ap.add_argument("--kernel-filter", default=None, help="with --summarize: only kernels whose name contains this")
-    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "prefill"],
+    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "prefill", "scale"],
                     help="run just this leg (no headline, no CPU baseline) and print its JSON; for profiling")
     return ap.parse_args()
 
@@ -314,6 +315,39 @@ def leg_prefill(torch, awq, workloads, g=128, zp=True, iters=30, warm=20):
     return out
 
 
+def leg_scale_search(torch, awq, workloads, g=128, zp=True, M=512, count=20, iters=5):
+    """Activation-aware scale search: L(s) for `count` candidate scale vectors
+    s = a^alpha over M calibration tokens, on the Llama-7B q (4096x4096) and
+    gate (4096->11008) shapes.  Per candidate: one scale-quantize-error pass
+    over W (read 2 B, write 2 B per weight) and one dense M x N x K product
+    with a sum-of-squares epilogue."""
+    out = {}
+    alphas = [i / count for i in range(count)]
+    for li, name in ((0, "q_proj"), (4, "gate_proj")):
+        _, K, N = workloads.LLAMA7B_BLOCK[li]
+        W = torch.from_numpy(workloads.weight(N, K, cfg=6, layer=li)).cuda()
+        X = torch.from_numpy(workloads.activations(M, K, cfg=6, layer=li)).cuda()
+        S = awq.awq_scale_candidates(X, alphas)
+        for _ in range(2):
+            L = awq.awq_scale_loss(X, W, S, g, zp)
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        tm.start()
+        for _ in range(iters):
+            L = awq.awq_scale_loss(X, W, S, g, zp)
+        ms = tm.stop_ms() / iters
+        losses = L.cpu().tolist()
+        best = min(range(count), key=lambda i: (losses[i], i))
+        flops = 2.0 * M * N * K * count
+        out[name] = {"M": M, "K": K, "N": N, "candidates": count, "us": round(ms * 1e3, 1),
+                     "us_per_candidate": round(ms * 1e3 / count, 2),
+                     "TFLOPS_product": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "best_alpha": alphas[best], "L_rtn": round(losses[0], 4), "L_best": round(losses[best], 4)}
+        del W, X, S, L
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(layers, g, zp, min_seconds=10.0, max_passes=40):
     """The CPU oracle as it stands (unpack + fp64 decode + fp64 product) on the
     seven linears of one block, M = 1."""
@@ -413,10 +447,11 @@ def main():
         return 0
 
     g, zp = 128, True
-    if args.leg_only in ("fused", "batched", "prefill"):
+    if args.leg_only in ("fused", "batched", "prefill", "scale"):
         fn = {"fused": lambda: leg_fused_decode(torch, awq, workloads, g, zp, blocks=args.blocks),
               "batched": lambda: leg_batched_decode(torch, awq, workloads, g, zp),
-              "prefill": lambda: leg_prefill(torch, awq, workloads, g, zp)}[args.leg_only]
+              "prefill": lambda: leg_prefill(torch, awq, workloads, g, zp),
+              "scale": lambda: leg_scale_search(torch, awq, workloads, g, zp)}[args.leg_only]
         print(json.dumps({"leg": args.leg_only, "result": fn()}), flush=True)
         return 0
     log(f"building {args.blocks} decode blocks")
@@ -493,7 +528,7 @@ def main():
     }
 
     legs = set(args.legs.split(",")) if args.legs not in ("all", "none") else (
-        {"pack", "fused", "batched", "prefill"} if args.legs == "all" else set())
+        {"pack", "fused", "batched", "prefill", "scale"} if args.legs == "all" else set())
     out_legs = {}
     if args.leg_only == "pack":
         print(json.dumps({"leg": "pack", "result": leg_pack(torch, awq, layers, g, zp)}), flush=True)
@@ -512,6 +547,9 @@ def main():
     if "prefill" in legs:
         log("leg: prefill")
         out_legs["prefill_gemm_70b"] = leg_prefill(torch, awq, workloads, g, zp)
+    if "scale" in legs:
+        log("leg: scale search")
+        out_legs["scale_search"] = leg_scale_search(torch, awq, workloads, g, zp)
     if out_legs:
         result["legs"] = out_legs
     if not args.no_cpu_baseline:

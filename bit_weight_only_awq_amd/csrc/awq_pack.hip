@@ -87,11 +87,16 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restr
   const int kw = K >> 3;            // packed words per row
   const int ngroups = kw / GW;      // groups per row
 
+  // the next pass's weights are loaded while this pass is quantized
+  const u32x4* wrow = w + (size_t)n * kw;
+  u32x4 next = {0u, 0u, 0u, 0u};
+  if (l < kw) next = wrow[l];
   for (int w0 = 0; w0 < kw; w0 += 32) {
     const int j = w0 + l;
     const bool active = j < kw;
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (active) raw = w[(size_t)n * kw + j];
+    const u32x4 raw = next;
+    next = u32x4{0u, 0u, 0u, 0u};
+    if (j + 32 < kw) next = wrow[j + 32];
     const half8_t h = as_half8(raw);
 
     float a[8];
@@ -134,8 +139,9 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restr
 //   e[n][k] = fp16( w'[n][k] / s_c[k] - w[n][k] ),  w' = Dq(Q(fp16(w[n][k] * s_c[k])))
 // so that L(s_c) = || X e^T ||_F: one dense product instead of two.  The
 // quantizer is the one of pack_kernel (same code, same fp32 order); w * s is
-// an fp32 product rounded to fp16, w' = (q - z) * s is exact, and the division
-// and subtraction are single fp32 roundings.  Same block shape as pack_kernel:
+// an fp32 product rounded to fp16, w' = (q - z) * s is exact, and the
+// product by the reciprocal of s_c[k] (1 ulp) and the subtraction are fp32
+// roundings far below the final fp16 one.  Same block shape as pack_kernel:
 // one octet of rows per block.
 template <int GW, bool ZP>
 __global__ __launch_bounds__(kPackThreads) void scale_error_kernel(const u32x4* __restrict__ w,
@@ -148,16 +154,27 @@ __global__ __launch_bounds__(kPackThreads) void scale_error_kernel(const u32x4* 
   const float* sc = s_all + (size_t)blockIdx.y * K;
   u32x4* e = e_all + (size_t)blockIdx.y * N * kw;
 
+  // the next pass's weights and scales are loaded while this pass is processed
+  const u32x4* wrow = w + (size_t)n * kw;
+  u32x4 nraw = {0u, 0u, 0u, 0u};
+  float4_t ns0 = {1.f, 1.f, 1.f, 1.f}, ns1 = {1.f, 1.f, 1.f, 1.f};
+  auto fetch = [&](int j) {
+    nraw = u32x4{0u, 0u, 0u, 0u};
+    ns0 = float4_t{1.f, 1.f, 1.f, 1.f};
+    ns1 = ns0;
+    if (j < kw) {
+      nraw = wrow[j];
+      ns0 = *reinterpret_cast<const float4_t*>(sc + 8 * j);
+      ns1 = *reinterpret_cast<const float4_t*>(sc + 8 * j + 4);
+    }
+  };
+  fetch(l);
   for (int w0 = 0; w0 < kw; w0 += 32) {
     const int j = w0 + l;
     const bool active = j < kw;
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    float4_t s0 = {1.f, 1.f, 1.f, 1.f}, s1 = {1.f, 1.f, 1.f, 1.f};
-    if (active) {
-      raw = w[(size_t)n * kw + j];
-      s0 = *reinterpret_cast<const float4_t*>(sc + 8 * j);
-      s1 = *reinterpret_cast<const float4_t*>(sc + 8 * j + 4);
-    }
+    const u32x4 raw = nraw;
+    const float4_t s0 = ns0, s1 = ns1;
+    fetch(j + 32);
     const half8_t h = as_half8(raw);
     float sv[8];
 #pragma unroll
@@ -173,11 +190,12 @@ __global__ __launch_bounds__(kPackThreads) void scale_error_kernel(const u32x4* 
     _Float16 s16;
     group_scale_zero<GW, ZP>(a, s16, s, zf);
 
+    // e only needs fp16 accuracy: w' / s by a reciprocal (1 ulp in fp32)
     half8_t out;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float wq = (code_of(a[c], s, zf) - zf) * s;
-      out[c] = (_Float16)(wq / sv[c] - (float)h[c]);
+      out[c] = (_Float16)(wq * __builtin_amdgcn_rcpf(sv[c]) - (float)h[c]);
     }
     if (active) e[(size_t)n * kw + j] = __builtin_bit_cast(u32x4, out);
   }

@@ -66,8 +66,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 }
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-constexpr int TM = 128, TN = 128, TK = 64;   // workgroup tile and K step
-constexpr int OP_BYTES = TM * TK * 2;        // one 128 x 64 fp16 operand tile in LDS (16 KiB)
+constexpr int TK = 64;  // K step
 
 // 16-byte chunk c of LDS row r sits in slot c ^ ((r >> 1) & 7): with 128-byte
 // rows, 16 consecutive rows read at the same logical chunk hit 16 distinct
@@ -75,27 +74,34 @@ constexpr int OP_BYTES = TM * TK * 2;        // one 128 x 64 fp16 operand tile i
 // lanes x 16 bytes writes.
 __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-// Workgroup: 4 waves (2 x 2) of 64 x 64 outputs, 2 x 2 v_mfma_f32_32x32x16_f16
-// tiles each; grid (tiles, candidates).  Both operands stream from HBM into
-// LDS by buffer-to-LDS loads, double-buffered, one barrier per K step.  Rows
-// past M or N read as zero and add nothing to the sum.  Output: the fp64 sum
-// of the squares of the tile's 128 x 128 outputs (each square and the per-lane
-// sums in fp32, the wave and workgroup sums in a fixed order).
-template <bool KTAIL>
-__global__ __launch_bounds__(256) void sumsq_gemm_kernel(const _Float16* __restrict__ X,
-                                                         const _Float16* __restrict__ E_all, int M, int N, int K,
-                                                         int tiles_m, double* __restrict__ partial) {
+// Workgroup of WM x WN waves; tile (32 WM WN) x (32 WM WN) with every wave
+// loading 32 rows of each operand: 2 x 2 waves of 64 x 64 (128 x 128 tile) or
+// 2 x 4 waves of 128 x 64 (256 x 256 tile), v_mfma_f32_32x32x16_f16; grid
+// (tiles, candidates).  Both operands stream from HBM into LDS by
+// buffer-to-LDS loads, double-buffered, one barrier per K step.  Rows past M
+// or N read as zero and add nothing to the sum.  Output: the fp64 sum of the
+// squares of the tile's outputs (each square and the per-lane sums in fp32,
+// the wave and workgroup sums in a fixed order).
+template <int WM, int WN, bool KTAIL>
+__global__ __launch_bounds__(WM * WN * 64) void sumsq_gemm_kernel(const _Float16* __restrict__ X,
+                                                                  const _Float16* __restrict__ E_all, int M, int N,
+                                                                  int K, int tiles_m, double* __restrict__ partial) {
+  constexpr int NW = WM * WN;
+  constexpr int T = 32 * NW;             // tile rows of X and of E
+  constexpr int AM = T / WM / 32;        // 32x32 MFMA tiles per wave along M
+  constexpr int AN = T / WN / 32;        // ... along N
+  constexpr int OP = T * TK * 2;         // bytes of one operand tile
   // the two buffers of each operand are separate arrays, so the compiler can
   // tell them apart and does not make reads of one wait for the loads into
   // the other
-  __shared__ __attribute__((aligned(1024))) char lx0[OP_BYTES], lx1[OP_BYTES], le0[OP_BYTES], le1[OP_BYTES];
-  __shared__ double wsum[4];
+  __shared__ __attribute__((aligned(1024))) char lx0[OP], lx1[OP], le0[OP], le1[OP];
+  __shared__ double wsum[NW];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int tile = blockIdx.x;
   const int tm = tile % tiles_m, tn = tile / tiles_m;
-  const int m0 = tm * TM, n0 = tn * TN;
+  const int m0 = tm * T, n0 = tn * T;
   const _Float16* E = E_all + (size_t)blockIdx.y * N * K;
-  const int rows_m = min(TM, M - m0), rows_n = min(TN, N - n0);
+  const int rows_m = min(T, M - m0), rows_n = min(T, N - n0);
   const int nsteps = (K + TK - 1) / TK;
 
   const __amdgpu_buffer_rsrc_t rx = rsrc(X + (size_t)m0 * K, (uint32_t)rows_m * K * 2);
@@ -130,15 +136,15 @@ __global__ __launch_bounds__(256) void sumsq_gemm_kernel(const _Float16* __restr
     }
   };
 
-  float16_t acc[2][2];
+  float16_t acc[AM][AN];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < AM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < AN; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  const int wm = (wave & 1) * 64, wn = (wave >> 1) * 64;
+  const int wm = (wave % WM) * (32 * AM), wn = (wave / WM) * (32 * AN);
   const int fi = lane & 31, fh = lane >> 5;  // fragment row and k-half of this lane
   const int fsw = (fi >> 1) & 7;             // swizzle of the fragment rows (bases are multiples of 32)
 
@@ -148,26 +154,26 @@ __global__ __launch_bounds__(256) void sumsq_gemm_kernel(const _Float16* __restr
 #pragma unroll
     for (int ks = 0; ks < TK / 16; ++ks) {
       const int slot = 16 * ((2 * ks + fh) ^ fsw);
-      half8_t af[2], bf[2];
+      half8_t af[AM], bf[AN];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) af[a] = *reinterpret_cast<const half8_t*>(xa + 32 * 128 * a + slot);
+      for (int a = 0; a < AM; ++a) af[a] = *reinterpret_cast<const half8_t*>(xa + 32 * 128 * a + slot);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) bf[b] = *reinterpret_cast<const half8_t*>(eb + 32 * 128 * b + slot);
+      for (int b = 0; b < AN; ++b) bf[b] = *reinterpret_cast<const half8_t*>(eb + 32 * 128 * b + slot);
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < AM; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < AN; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
   };
 
-  // Two steps per trip.  The loads of a step past the end stay inside the
-  // resources (or read zero) and land in a buffer no one reads again.
+  // Two steps per trip; the scheduling barriers keep each step's loads ahead
+  // of the multiplies that hide their latency.  Loads of a step past the end
+  // stay inside the resources (or read zero) and land in a buffer no one
+  // reads again.
   load(0, 0);
   __syncthreads();
   int step = 0;
-  // the scheduling barriers keep each step's loads ahead of the multiplies
-  // that hide their latency
   for (; step + 1 < nsteps; step += 2) {
     load(step + 1, 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -182,17 +188,25 @@ __global__ __launch_bounds__(256) void sumsq_gemm_kernel(const _Float16* __restr
 
   float ss = 0.0f;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < AM; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < AN; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) ss += acc[a][b][r] * acc[a][b][r];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
   if (lane == 0) wsum[wave] = (double)ss;
   __syncthreads();
-  if (t == 0) partial[(size_t)blockIdx.y * gridDim.x + tile] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  if (t == 0) {
+    double v = wsum[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += wsum[w];
+    partial[(size_t)blockIdx.y * gridDim.x + tile] = v;
+  }
 }
+
+// Tile edge of the loss product: 256 (8 waves) once M fills it, else 128.
+int loss_tile(int M) { return M > 128 ? 256 : 128; }
 
 // loss[c] = sqrt(sum of candidate c's tile partials), summed by one workgroup
 // in a fixed order.
@@ -234,25 +248,34 @@ hipError_t launch_scale_candidates(const void* x, int M, int K, const float* alp
 }
 
 size_t scale_loss_workspace_bytes(int count, int M, int N, int K) {
-  const size_t tiles = (size_t)((M + TM - 1) / TM) * ((N + TN - 1) / TN);
+  const int T = loss_tile(M);
+  const size_t tiles = (size_t)((M + T - 1) / T) * ((N + T - 1) / T);
   return align256((size_t)count * N * K * 2) + align256((size_t)count * tiles * 8);
 }
 
 hipError_t launch_scale_loss(const void* x, const void* w, const float* s, int count, int M, int N, int K,
                              int group_size, bool zero_point, void* workspace, double* loss, hipStream_t stream) {
-  const int tiles_m = (M + TM - 1) / TM, tiles_n = (N + TN - 1) / TN;
+  const int T = loss_tile(M);
+  const int tiles_m = (M + T - 1) / T, tiles_n = (N + T - 1) / T;
   char* ws = static_cast<char*>(workspace);
   _Float16* e = reinterpret_cast<_Float16*>(ws);
   double* partial = reinterpret_cast<double*>(ws + align256((size_t)count * N * K * 2));
   hipError_t err = launch_scale_error(w, s, count, N, K, group_size, zero_point, e, stream);
   if (err != hipSuccess) return err;
   const dim3 grid(tiles_m * tiles_n, count);
-  if (K % TK == 0)
-    hipLaunchKernelGGL(sumsq_gemm_kernel<false>, grid, dim3(256), 0, stream, static_cast<const _Float16*>(x), e, M, N,
-                       K, tiles_m, partial);
-  else
-    hipLaunchKernelGGL(sumsq_gemm_kernel<true>, grid, dim3(256), 0, stream, static_cast<const _Float16*>(x), e, M, N,
-                       K, tiles_m, partial);
+  const _Float16* xv = static_cast<const _Float16*>(x);
+  const bool tail = K % TK != 0;
+  if (T == 256) {
+    if (tail)
+      hipLaunchKernelGGL((sumsq_gemm_kernel<2, 4, true>), grid, dim3(512), 0, stream, xv, e, M, N, K, tiles_m, partial);
+    else
+      hipLaunchKernelGGL((sumsq_gemm_kernel<2, 4, false>), grid, dim3(512), 0, stream, xv, e, M, N, K, tiles_m, partial);
+  } else {
+    if (tail)
+      hipLaunchKernelGGL((sumsq_gemm_kernel<2, 2, true>), grid, dim3(256), 0, stream, xv, e, M, N, K, tiles_m, partial);
+    else
+      hipLaunchKernelGGL((sumsq_gemm_kernel<2, 2, false>), grid, dim3(256), 0, stream, xv, e, M, N, K, tiles_m, partial);
+  }
   hipLaunchKernelGGL(loss_finalize_kernel, dim3(count), dim3(256), 0, stream, partial, tiles_m * tiles_n, loss);
   return hipGetLastError();
 }
