@@ -14,13 +14,14 @@ roofline = the GEMV kernel against 8 TB/s HBM; its average launch time comes
 legs   = awq_pack, fused-projection decode (qkv and gate_up as one awq_gemv
          each), batched-decode awq_gemm (M = 4/16/64; GEMV vs GEMM at M = 1),
          prefill awq_gemm (M = 2048, 70B-shaped MLP), activation-aware scale
-         search (L(s) for 20 candidates over 512 calibration tokens).
+         search (L(s) for 20 candidates over 512 calibration tokens), weight
+         clipping search (20 ratios, same tokens).
 cpu_baseline = the CPU oracle (decode + fp64 product) on one block, timed on
          the host; a reported reference, not a target.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--blocks 32]
                        [--legs all|none|<comma list>] [--no-cpu-baseline]
-       python bench.py --leg-only pack|fused|batched|prefill|scale   (one leg, for profiling)
+       python bench.py --leg-only pack|fused|batched|prefill|scale|clip   (one leg, for profiling)
        python bench.py --copy-calibration | --summarize DB... [--kernel-filter NAME]
 """
 from __future__ import annotations
@@ -60,7 +61,7 @@ def parse():
     ap.add_argument("--summarize", nargs="+", metavar="DB",
                     help="print a per-kernel summary of rocprofv3 result databases and exit")
     ap.add_argument("--kernel-filter", default=None, help="with --summarize: only kernels whose name contains this")
-    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "prefill", "scale"],
+    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "prefill", "scale", "clip"],
                     help="run just this leg (no headline, no CPU baseline) and print its JSON; for profiling")
     return ap.parse_args()
 
@@ -348,6 +349,37 @@ def leg_scale_search(torch, awq, workloads, g=128, zp=True, M=512, count=20, ite
     return out
 
 
+def leg_clip_search(torch, awq, workloads, g=128, zp=True, M=512, iters=5):
+    """Weight-clipping search (20 ratios, 1.0 down to 0.525) over M calibration
+    tokens on the Llama-7B q (4096x4096) and gate (4096->11008) shapes: per
+    ratio one clip-quantize-error pass over W and one M x N x K product whose
+    squares are summed per weight group, then the choice and the clipped
+    weights."""
+    out = {}
+    ratios = list(awq.DEFAULT_CLIP_RATIOS)
+    for li, name in ((0, "q_proj"), (4, "gate_proj")):
+        _, K, N = workloads.LLAMA7B_BLOCK[li]
+        W = torch.from_numpy(workloads.weight(N, K, cfg=7, layer=li)).cuda()
+        X = torch.from_numpy(workloads.activations(M, K, cfg=7, layer=li)).cuda()
+        for _ in range(2):
+            wc, choice = awq.awq_clip_search(X, W, g, zp, ratios)
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        tm.start()
+        for _ in range(iters):
+            wc, choice = awq.awq_clip_search(X, W, g, zp, ratios)
+        ms = tm.stop_ms() / iters
+        hist = torch.bincount(choice.flatten().long(), minlength=len(ratios)).cpu().tolist()
+        flops = 2.0 * M * N * K * len(ratios)
+        out[name] = {"M": M, "K": K, "N": N, "ratios": len(ratios), "us": round(ms * 1e3, 1),
+                     "us_per_ratio": round(ms * 1e3 / len(ratios), 2),
+                     "TFLOPS_product": round(flops / (ms * 1e-3) / 1e12, 1),
+                     "groups_clipped": round(1.0 - hist[0] / sum(hist), 4)}
+        del W, X, wc, choice
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(layers, g, zp, min_seconds=10.0, max_passes=40):
     """The CPU oracle as it stands (unpack + fp64 decode + fp64 product) on the
     seven linears of one block, M = 1."""
@@ -447,11 +479,12 @@ def main():
         return 0
 
     g, zp = 128, True
-    if args.leg_only in ("fused", "batched", "prefill", "scale"):
+    if args.leg_only in ("fused", "batched", "prefill", "scale", "clip"):
         fn = {"fused": lambda: leg_fused_decode(torch, awq, workloads, g, zp, blocks=args.blocks),
               "batched": lambda: leg_batched_decode(torch, awq, workloads, g, zp),
               "prefill": lambda: leg_prefill(torch, awq, workloads, g, zp),
-              "scale": lambda: leg_scale_search(torch, awq, workloads, g, zp)}[args.leg_only]
+              "scale": lambda: leg_scale_search(torch, awq, workloads, g, zp),
+              "clip": lambda: leg_clip_search(torch, awq, workloads, g, zp)}[args.leg_only]
         print(json.dumps({"leg": args.leg_only, "result": fn()}), flush=True)
         return 0
     log(f"building {args.blocks} decode blocks")
@@ -528,7 +561,7 @@ def main():
     }
 
     legs = set(args.legs.split(",")) if args.legs not in ("all", "none") else (
-        {"pack", "fused", "batched", "prefill", "scale"} if args.legs == "all" else set())
+        {"pack", "fused", "batched", "prefill", "scale", "clip"} if args.legs == "all" else set())
     out_legs = {}
     if args.leg_only == "pack":
         print(json.dumps({"leg": "pack", "result": leg_pack(torch, awq, layers, g, zp)}), flush=True)
@@ -550,6 +583,9 @@ def main():
     if "scale" in legs:
         log("leg: scale search")
         out_legs["scale_search"] = leg_scale_search(torch, awq, workloads, g, zp)
+    if "clip" in legs:
+        log("leg: clip search")
+        out_legs["clip_search"] = leg_clip_search(torch, awq, workloads, g, zp)
     if out_legs:
         result["legs"] = out_legs
     if not args.no_cpu_baseline:

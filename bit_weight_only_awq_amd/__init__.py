@@ -40,7 +40,8 @@ AWQ_ERR_HIP = -7
 
 EXPORTED = ("awq_pack", "awq_dequant", "awq_gemv", "awq_gemm", "awq_gemm_workspace_bytes", "awq_strerror",
             "awq_scale_candidates", "awq_scale_candidates_workspace_bytes", "awq_scale_loss",
-            "awq_scale_loss_workspace_bytes")
+            "awq_scale_loss_workspace_bytes", "awq_scale_columns", "awq_clip_search",
+            "awq_clip_search_workspace_bytes")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -81,6 +82,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.awq_scale_loss.restype = ctypes.c_int
     lib.awq_scale_loss_workspace_bytes.argtypes = [I32, I32, I32, I32]
     lib.awq_scale_loss_workspace_bytes.restype = SZ
+    lib.awq_scale_columns.argtypes = [P, I32, I32, P, I32, P, P]
+    lib.awq_scale_columns.restype = ctypes.c_int
+    lib.awq_clip_search.argtypes = [P, P, I32, I32, I32, I32, I32, P, I32, P, P, P, SZ, P]
+    lib.awq_clip_search.restype = ctypes.c_int
+    lib.awq_clip_search_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    lib.awq_clip_search_workspace_bytes.restype = SZ
     _lib = lib
     return lib
 
@@ -320,3 +327,61 @@ def search_scale(x: torch.Tensor, w: torch.Tensor, group_size: int = 128, zero_p
     losses = awq_scale_loss(x, w, S, group_size, zero_point).cpu().tolist()
     best = min(range(len(alphas)), key=lambda i: (losses[i], i))
     return ScaleSearch(alphas[best], S[best].clone(), losses, alphas)
+
+
+def awq_scale_columns(src: torch.Tensor, s: torch.Tensor, divide: bool = False,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp16(src * s) per input channel (or fp16(src / s) with ``divide``)."""
+    lib = load_library()
+    rows, K = src.shape
+    if out is None:
+        out = torch.empty_like(src)
+    st = lib.awq_scale_columns(_ptr(src), rows, K, _ptr(s), int(bool(divide)), _ptr(out), _stream(src))
+    _check(st, "awq_scale_columns")
+    return out
+
+
+DEFAULT_CLIP_RATIOS = tuple(1.0 - 0.025 * i for i in range(20))
+
+
+def awq_clip_search(x: torch.Tensor, w: torch.Tensor, group_size: int = 128, zero_point: bool = True,
+                    ratios=DEFAULT_CLIP_RATIOS):
+    """Weight clipping: per group, the ratio in ``ratios`` with the smallest
+    output error over ``x``.  Returns (clipped fp16 weights [N, K], chosen
+    ratio index int32 [N, K / group_size])."""
+    lib = load_library()
+    M, K = x.shape
+    N = w.shape[0]
+    ratios = [float(r) for r in ratios]
+    out = torch.empty_like(w)
+    choice = torch.empty((N, K // group_size), dtype=torch.int32, device=w.device)
+    ws = torch.empty(max(1, int(lib.awq_clip_search_workspace_bytes(len(ratios), M, N, K, group_size))),
+                     dtype=torch.uint8, device=w.device)
+    arr = (ctypes.c_float * len(ratios))(*ratios)
+    st = lib.awq_clip_search(_ptr(x), _ptr(w), M, N, K, group_size, int(bool(zero_point)),
+                             ctypes.cast(arr, ctypes.c_void_p), len(ratios), _ptr(out), _ptr(choice), _ptr(ws),
+                             ws.numel(), _stream(x))
+    _check(st, "awq_clip_search")
+    return out, choice
+
+
+class QuantizedLinear(NamedTuple):
+    packed: PackedWeight
+    input_scale: torch.Tensor  # fp32 [K]: the layer computes on fp16(x / input_scale)
+    alpha: float
+
+
+def quantize_awq(w: torch.Tensor, x: torch.Tensor, q_group_size: int = 128, zero_point: bool = True,
+                 alphas=None, clip_ratios=DEFAULT_CLIP_RATIOS, apply_clip: bool = True) -> QuantizedLinear:
+    """The activation-aware quantization of one linear layer from calibration
+    activations ``x`` [M, K]: scale search (s = a ** alpha with the smallest
+    L(s)), weights scaled by s, optional clipping search on the scaled layer,
+    then packing.  The packed layer expects activations divided by
+    ``input_scale`` (``awq_scale_columns(x, s, divide=True)``, or folded into
+    the producer of x)."""
+    res = search_scale(x, w, q_group_size, zero_point, alphas)
+    ws = awq_scale_columns(w, res.scale)
+    if apply_clip:
+        xs = awq_scale_columns(x, res.scale, divide=True)
+        ws, _ = awq_clip_search(xs, ws, q_group_size, zero_point, clip_ratios)
+    return QuantizedLinear(pack(ws, q_group_size, zero_point), res.scale, res.alpha)

@@ -134,6 +134,37 @@ int awq_scale_loss(const void* x, const void* w, const float* s, int32_t count, 
                                          static_cast<hipStream_t>(stream)));
 }
 
+int awq_scale_columns(const void* src, int32_t rows, int32_t K, const float* s, int32_t divide, void* dst,
+                      void* stream) {
+  if (rows < 1 || K < 8 || K > kMaxDim || (K & 7) != 0) return AWQ_ERR_SHAPE;
+  if (!src || !s || !dst) return AWQ_ERR_NULL;
+  if (!aligned16(src) || !aligned16(s) || !aligned16(dst)) return AWQ_ERR_ALIGN;
+  return from_hip(awq::launch_scale_columns(src, rows, K, s, divide != 0, dst, static_cast<hipStream_t>(stream)));
+}
+
+size_t awq_clip_search_workspace_bytes(int32_t count, int32_t M, int32_t N, int32_t K, int32_t group_size) {
+  if (count < 1 || count > awq::kMaxClipCandidates || M < 1 || check_weight_shape(N, K, group_size) != AWQ_OK)
+    return 0;
+  return awq::clip_search_workspace_bytes(count, M, N, K, group_size);
+}
+
+int awq_clip_search(const void* x, const void* w, int32_t M, int32_t N, int32_t K, int32_t group_size,
+                    int32_t zero_point, const float* ratios, int32_t count, void* w_clipped, int32_t* choice,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_weight_shape(N, K, group_size);
+  if (st != AWQ_OK) return st;
+  if (M < 1 || count < 1 || count > awq::kMaxClipCandidates) return AWQ_ERR_SHAPE;
+  if (!x || !w || !ratios || !w_clipped || !workspace) return AWQ_ERR_NULL;
+  for (int c = 0; c < count; ++c)
+    if (!(ratios[c] > 0.0f && ratios[c] <= 1.0f)) return AWQ_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(w_clipped) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(choice) & 3u) != 0)
+    return AWQ_ERR_ALIGN;
+  if (workspace_bytes < awq::clip_search_workspace_bytes(count, M, N, K, group_size)) return AWQ_ERR_WORKSPACE;
+  return from_hip(awq::launch_clip_search(x, w, M, N, K, group_size, zero_point != 0, ratios, count, w_clipped, choice,
+                                          workspace, static_cast<hipStream_t>(stream)));
+}
+
 const char* awq_strerror(int status) {
   switch (status) {
     case AWQ_OK: return "ok";

@@ -37,6 +37,28 @@ hipError_t launch_scale_candidates(const void* x, int M, int K, const float* alp
 hipError_t launch_scale_error(const void* w, const float* s, int count, int N, int K, int group_size, bool zero_point,
                               void* e, hipStream_t stream);
 
+// dst = fp16(src * s) or fp16(src / s), s per column (input channel).
+hipError_t launch_scale_columns(const void* src, int rows, int K, const float* s, bool divide, void* dst,
+                                hipStream_t stream);
+
+// Candidate clipping ratios, passed by value to the kernels.
+constexpr int kMaxClipCandidates = 64;
+struct ClipRatios {
+  float v[kMaxClipCandidates];
+};
+
+// e[c][n][k] = fp16(Dq(Q(clip_c(w)))[n][k] - w[n][k]) for each ratio c.
+hipError_t launch_clip_error(const void* w, const ClipRatios& ratios, int count, int N, int K, int group_size,
+                             bool zero_point, void* e, hipStream_t stream);
+// Per group: the ratio with the smallest summed partial error; clipped weights to w_out.
+hipError_t launch_clip_apply(const void* w, const float* part, int parts, const ClipRatios& ratios, int count, int N,
+                             int K, int group_size, bool zero_point, void* w_out, int32_t* choice, hipStream_t stream);
+// Clip search: errors of every ratio, then choice and clipped weights.
+size_t clip_search_workspace_bytes(int count, int M, int N, int K, int group_size);
+hipError_t launch_clip_search(const void* x, const void* w, int M, int N, int K, int group_size, bool zero_point,
+                              const float* ratios, int count, void* w_out, int32_t* choice, void* workspace,
+                              hipStream_t stream);
+
 // loss[c] = || X e_c^T ||_F for each candidate scale vector s[c].
 size_t scale_loss_workspace_bytes(int count, int M, int N, int K);
 hipError_t launch_scale_loss(const void* x, const void* w, const float* s, int count, int M, int N, int K,

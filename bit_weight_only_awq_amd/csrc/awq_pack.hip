@@ -66,6 +66,36 @@ __device__ __forceinline__ float code_of(float a, float s, float zf) {
   return fminf(fmaxf(v, 0.0f), 15.0f);
 }
 
+// Range of the group a lane's 8 weights belong to, shrunk by `r` (weight
+// clipping): [r * min, r * max] with a zero point, [-r * amax, r * amax]
+// without (fp32 products).
+template <int GW, bool ZP>
+__device__ __forceinline__ void group_clip_bounds(const float (&a)[8], float r, float& lo, float& hi) {
+  if constexpr (ZP) {
+    float mn = a[0], mx = a[0];
+#pragma unroll
+    for (int c = 1; c < 8; ++c) {
+      mn = fminf(mn, a[c]);
+      mx = fmaxf(mx, a[c]);
+    }
+#pragma unroll
+    for (int off = 1; off < GW; off <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, off));
+      mx = fmaxf(mx, __shfl_xor(mx, off));
+    }
+    lo = r * mn;
+    hi = r * mx;
+  } else {
+    float amax = fabsf(a[0]);
+#pragma unroll
+    for (int c = 1; c < 8; ++c) amax = fmaxf(amax, fabsf(a[c]));
+#pragma unroll
+    for (int off = 1; off < GW; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    hi = r * amax;
+    lo = -hi;
+  }
+}
+
 // One block quantizes one octet of rows (n0 .. n0+7).  Thread t works on row
 // n0 + (t >> 5); its lane l = t & 31 owns one packed word (8 channels) of each
 // 256-channel pass over the row.  The octet's scales and zero points are
@@ -201,6 +231,98 @@ __global__ __launch_bounds__(kPackThreads) void scale_error_kernel(const u32x4* 
   }
 }
 
+// Output error of weight clipping, for the search of apply_clip ("AI-Research-
+// SKILLs AWQ 高级使用指南", section 自定义校准数据: clip the weights to reduce
+// the effect of outliers on the quantization error).  For candidate ratio
+// r_c (blockIdx.y): every group is clamped to its range shrunk by r_c (fp32,
+// then fp16), quantized as by pack_kernel, decoded, and compared with the
+// unclipped weight:  e[c][n][k] = fp16(Dq(Q(clip_c(w)))[n][k] - w[n][k]).
+template <int GW, bool ZP>
+__global__ __launch_bounds__(kPackThreads) void clip_error_kernel(const u32x4* __restrict__ w, ClipRatios ratios,
+                                                                  int N, int K, u32x4* __restrict__ e_all) {
+  const int t = threadIdx.x;
+  const int r = t >> 5, l = t & 31;
+  const int n = blockIdx.x * 8 + r;
+  const int kw = K >> 3;
+  const float ratio = ratios.v[blockIdx.y];
+  u32x4* e = e_all + (size_t)blockIdx.y * N * kw;
+  const u32x4* wrow = w + (size_t)n * kw;
+  u32x4 next = {0u, 0u, 0u, 0u};
+  if (l < kw) next = wrow[l];
+  for (int w0 = 0; w0 < kw; w0 += 32) {
+    const int j = w0 + l;
+    const bool active = j < kw;
+    const u32x4 raw = next;
+    next = u32x4{0u, 0u, 0u, 0u};
+    if (j + 32 < kw) next = wrow[j + 32];
+    const half8_t h = as_half8(raw);
+    float a[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a[c] = (float)h[c];
+    float lo, hi;
+    group_clip_bounds<GW, ZP>(a, ratio, lo, hi);
+    float cl[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) cl[c] = (float)(_Float16)fminf(fmaxf(a[c], lo), hi);
+    float s, zf;
+    _Float16 s16;
+    group_scale_zero<GW, ZP>(cl, s16, s, zf);
+    half8_t out;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) out[c] = (_Float16)((code_of(cl[c], s, zf) - zf) * s - a[c]);
+    if (active) e[(size_t)n * kw + j] = __builtin_bit_cast(u32x4, out);
+  }
+}
+
+// Chooses each group's clipping ratio and writes the clipped weights.  The
+// error of group (n, j) under ratio c is the sum, in a fixed order, of the
+// per-tile partials part[c][tm][h][j][n] (tile rows tm, half h of a tile's
+// rows); the group keeps the first ratio with the smallest error, is clamped
+// to its range shrunk by that ratio, and `choice[n][j]` (if given) records it.
+template <int GW, bool ZP>
+__global__ __launch_bounds__(kPackThreads) void clip_apply_kernel(const u32x4* __restrict__ w,
+                                                                  const float* __restrict__ part, int parts, int N,
+                                                                  int K, ClipRatios ratios, int count,
+                                                                  u32x4* __restrict__ w_out,
+                                                                  int32_t* __restrict__ choice) {
+  const int t = threadIdx.x;
+  const int r = t >> 5, l = t & 31, lane = t & 63;
+  const int n = blockIdx.x * 8 + r;
+  const int kw = K >> 3;
+  const int G = kw / GW;
+  for (int w0 = 0; w0 < kw; w0 += 32) {
+    const int j = w0 + l;
+    const bool active = j < kw;
+    const int grp = j / GW;
+    int best = 0;
+    if (active && (l % GW) == 0) {
+      double best_v = 0.0;
+      for (int c = 0; c < count; ++c) {
+        double v = 0.0;
+        for (int p = 0; p < parts; ++p) v += (double)part[(((size_t)c * parts + p) * G + grp) * N + n];
+        if (c == 0 || v < best_v) {
+          best_v = v;
+          best = c;
+        }
+      }
+      if (choice) choice[(size_t)n * G + grp] = best;
+    }
+    best = __shfl(best, lane & ~(GW - 1));
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (active) raw = w[(size_t)n * kw + j];
+    const half8_t h = as_half8(raw);
+    float a[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a[c] = (float)h[c];
+    float lo, hi;
+    group_clip_bounds<GW, ZP>(a, ratios.v[best], lo, hi);
+    half8_t out;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) out[c] = (_Float16)fminf(fmaxf(a[c], lo), hi);
+    if (active) w_out[(size_t)n * kw + j] = __builtin_bit_cast(u32x4, out);
+  }
+}
+
 // One thread per packed word: w_out[n][8j .. 8j+7] = fp16((q - z) * s).
 // (q - z) * s is exact in fp32 (a 5-bit by 11-bit product), so the single
 // conversion to fp16 is the only rounding.
@@ -264,7 +386,48 @@ hipError_t launch_scale_error_zp(const void* w, const float* s, int count, int N
   return hipGetLastError();
 }
 
+template <bool ZP>
+hipError_t launch_clip_zp(const void* w, const ClipRatios& ratios, int count, int N, int K, int group_size, void* e,
+                          const float* part, int parts, void* w_out, int32_t* choice, bool apply, hipStream_t stream) {
+  const u32x4* wv = static_cast<const u32x4*>(w);
+  const dim3 block(kPackThreads);
+#define AWQ_CLIP_CASE(G_, GW_)                                                                                   \
+  case G_:                                                                                                     \
+    if (!apply)                                                                                                \
+      hipLaunchKernelGGL((clip_error_kernel<GW_, ZP>), dim3(N / 8, count), block, 0, stream, wv, ratios, N, K,   \
+                         static_cast<u32x4*>(e));                                                              \
+    else                                                                                                       \
+      hipLaunchKernelGGL((clip_apply_kernel<GW_, ZP>), dim3(N / 8), block, 0, stream, wv, part, parts, N, K,     \
+                         ratios, count, static_cast<u32x4*>(w_out), choice);                                   \
+    break;
+  switch (group_size) {
+    AWQ_CLIP_CASE(32, 4)
+    AWQ_CLIP_CASE(64, 8)
+    AWQ_CLIP_CASE(128, 16)
+    AWQ_CLIP_CASE(256, 32)
+    default: return hipErrorInvalidValue;
+  }
+#undef AWQ_CLIP_CASE
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_clip_error(const void* w, const ClipRatios& ratios, int count, int N, int K, int group_size,
+                             bool zero_point, void* e, hipStream_t stream) {
+  return zero_point ? launch_clip_zp<true>(w, ratios, count, N, K, group_size, e, nullptr, 0, nullptr, nullptr, false,
+                                           stream)
+                    : launch_clip_zp<false>(w, ratios, count, N, K, group_size, e, nullptr, 0, nullptr, nullptr, false,
+                                            stream);
+}
+
+hipError_t launch_clip_apply(const void* w, const float* part, int parts, const ClipRatios& ratios, int count, int N,
+                             int K, int group_size, bool zero_point, void* w_out, int32_t* choice, hipStream_t stream) {
+  return zero_point ? launch_clip_zp<true>(w, ratios, count, N, K, group_size, nullptr, part, parts, w_out, choice,
+                                           true, stream)
+                    : launch_clip_zp<false>(w, ratios, count, N, K, group_size, nullptr, part, parts, w_out, choice,
+                                            true, stream);
+}
 
 hipError_t launch_scale_error(const void* w, const float* s, int count, int N, int K, int group_size, bool zero_point,
                               void* e, hipStream_t stream) {

@@ -57,6 +57,28 @@ __global__ __launch_bounds__(256) void candidates_kernel(const float* __restrict
   for (int c = 0; c < count; ++c) s[(size_t)c * K + k] = alphas.v[c] == 0.0f ? 1.0f : powf(a, alphas.v[c]);
 }
 
+// dst[r][k] = fp16(src[r][k] * s[k]) (or / s[k]): fp32 product or correctly
+// rounded fp32 quotient, rounded once to fp16.  One thread per 8 channels.
+__global__ __launch_bounds__(256) void scale_columns_kernel(const u32x4* __restrict__ src, int rows, int K,
+                                                            const float* __restrict__ s, int divide,
+                                                            u32x4* __restrict__ dst) {
+  const int kw = K >> 3;
+  const size_t total = (size_t)rows * kw;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+    const int j = (int)(i % kw);
+    const half8_t h = as_half8(src[i]);
+    const float4_t s0 = *reinterpret_cast<const float4_t*>(s + 8 * j);
+    const float4_t s1 = *reinterpret_cast<const float4_t*>(s + 8 * j + 4);
+    half8_t out;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float sc = c < 4 ? s0[c] : s1[c - 4];
+      out[c] = (_Float16)(divide ? (float)h[c] / sc : (float)h[c] * sc);
+    }
+    dst[i] = __builtin_bit_cast(u32x4, out);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Sum of squares of X e_c^T.
 // ---------------------------------------------------------------------------
@@ -82,10 +104,17 @@ __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((
 // or N read as zero and add nothing to the sum.  Output: the fp64 sum of the
 // squares of the tile's outputs (each square and the per-lane sums in fp32,
 // the wave and workgroup sums in a fixed order).
-template <int WM, int WN, bool KTAIL>
+//
+// GROUPED: the squares are taken per group of g input channels instead (the
+// output error of each weight group, for the clipping search): at every group
+// boundary each wave adds the squares of its accumulators over its rows, per
+// column, writes them to gpart[c][tm][wave row half][group][n] and restarts
+// its accumulators from zero.
+template <int WM, int WN, bool KTAIL, bool GROUPED>
 __global__ __launch_bounds__(WM * WN * 64) void sumsq_gemm_kernel(const _Float16* __restrict__ X,
                                                                   const _Float16* __restrict__ E_all, int M, int N,
-                                                                  int K, int tiles_m, double* __restrict__ partial) {
+                                                                  int K, int tiles_m, double* __restrict__ partial,
+                                                                  int gshift, float* __restrict__ gpart) {
   constexpr int NW = WM * WN;
   constexpr int T = 32 * NW;             // tile rows of X and of E
   constexpr int AM = T / WM / 32;        // 32x32 MFMA tiles per wave along M
@@ -148,7 +177,28 @@ __global__ __launch_bounds__(WM * WN * 64) void sumsq_gemm_kernel(const _Float16
   const int fi = lane & 31, fh = lane >> 5;  // fragment row and k-half of this lane
   const int fsw = (fi >> 1) & 7;             // swizzle of the fragment rows (bases are multiples of 32)
 
-  auto compute = [&](int buf) {
+  // per-group flush (GROUPED): squares per column over this wave's rows
+  const int G = K >> gshift;
+  float* gout = GROUPED ? gpart + (((size_t)blockIdx.y * tiles_m + tm) * WM + (wave % WM)) * G * N : nullptr;
+  auto flush = [&](int grp) {
+#pragma unroll
+    for (int b = 0; b < AN; ++b) {
+      float v = 0.0f;
+#pragma unroll
+      for (int a = 0; a < AM; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          v += acc[a][b][r] * acc[a][b][r];
+          acc[a][b][r] = 0.0f;
+        }
+      // lanes l and l + 32 hold the two row halves of column l % 32
+      v += __shfl_xor(v, 32);
+      const int n = n0 + wn + 32 * b + lane;
+      if (lane < 32 && n < N) gout[(size_t)grp * N + n] = v;
+    }
+  };
+
+  auto compute = [&](int buf, int step) {
     const char* xa = (buf ? lx1 : lx0) + (wm + fi) * 128;
     const char* eb = (buf ? le1 : le0) + (wn + fi) * 128;
 #pragma unroll
@@ -164,6 +214,10 @@ __global__ __launch_bounds__(WM * WN * 64) void sumsq_gemm_kernel(const _Float16
 #pragma unroll
         for (int b = 0; b < AN; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+      if constexpr (GROUPED) {
+        const int kend = step * TK + (ks + 1) * 16;  // channels done after this slice
+        if ((kend & ((1 << gshift) - 1)) == 0 && kend <= K) flush((kend >> gshift) - 1);
+      }
     }
   };
 
@@ -177,14 +231,15 @@ __global__ __launch_bounds__(WM * WN * 64) void sumsq_gemm_kernel(const _Float16
   for (; step + 1 < nsteps; step += 2) {
     load(step + 1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(0);
+    compute(0, step);
     __syncthreads();
     load(step + 2, 0);
     __builtin_amdgcn_sched_barrier(0);
-    compute(1);
+    compute(1, step + 1);
     __syncthreads();
   }
-  if (step < nsteps) compute(0);
+  if (step < nsteps) compute(0, step);
+  if constexpr (GROUPED) return;
 
   float ss = 0.0f;
 #pragma unroll
@@ -228,6 +283,8 @@ __global__ __launch_bounds__(256) void loss_finalize_kernel(const double* __rest
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
+int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 128 ? 7 : 8; }
+
 }  // namespace
 
 size_t scale_candidates_workspace_bytes(int M, int K) {
@@ -247,6 +304,31 @@ hipError_t launch_scale_candidates(const void* x, int M, int K, const float* alp
   return hipGetLastError();
 }
 
+// The loss product: whole-tile sums (scale search) or per-group sums (clip search).
+static hipError_t launch_sumsq(const _Float16* x, const _Float16* e, int M, int N, int K, int T, int tiles_m,
+                               dim3 grid, double* partial, int gshift, float* gpart, bool grouped,
+                               hipStream_t stream) {
+  const bool tail = K % TK != 0;
+#define AWQ_SUMSQ(WM_, WN_, TAIL_, GR_)                                                                          \
+  hipLaunchKernelGGL((sumsq_gemm_kernel<WM_, WN_, TAIL_, GR_>), grid, dim3(WM_ * WN_ * 64), 0, stream, x, e, M, N, \
+                     K, tiles_m, partial, gshift, gpart)
+  if (T == 256) {
+    if (grouped) {
+      if (tail) AWQ_SUMSQ(2, 4, true, true); else AWQ_SUMSQ(2, 4, false, true);
+    } else {
+      if (tail) AWQ_SUMSQ(2, 4, true, false); else AWQ_SUMSQ(2, 4, false, false);
+    }
+  } else {
+    if (grouped) {
+      if (tail) AWQ_SUMSQ(2, 2, true, true); else AWQ_SUMSQ(2, 2, false, true);
+    } else {
+      if (tail) AWQ_SUMSQ(2, 2, true, false); else AWQ_SUMSQ(2, 2, false, false);
+    }
+  }
+#undef AWQ_SUMSQ
+  return hipGetLastError();
+}
+
 size_t scale_loss_workspace_bytes(int count, int M, int N, int K) {
   const int T = loss_tile(M);
   const size_t tiles = (size_t)((M + T - 1) / T) * ((N + T - 1) / T);
@@ -263,21 +345,45 @@ hipError_t launch_scale_loss(const void* x, const void* w, const float* s, int c
   hipError_t err = launch_scale_error(w, s, count, N, K, group_size, zero_point, e, stream);
   if (err != hipSuccess) return err;
   const dim3 grid(tiles_m * tiles_n, count);
-  const _Float16* xv = static_cast<const _Float16*>(x);
-  const bool tail = K % TK != 0;
-  if (T == 256) {
-    if (tail)
-      hipLaunchKernelGGL((sumsq_gemm_kernel<2, 4, true>), grid, dim3(512), 0, stream, xv, e, M, N, K, tiles_m, partial);
-    else
-      hipLaunchKernelGGL((sumsq_gemm_kernel<2, 4, false>), grid, dim3(512), 0, stream, xv, e, M, N, K, tiles_m, partial);
-  } else {
-    if (tail)
-      hipLaunchKernelGGL((sumsq_gemm_kernel<2, 2, true>), grid, dim3(256), 0, stream, xv, e, M, N, K, tiles_m, partial);
-    else
-      hipLaunchKernelGGL((sumsq_gemm_kernel<2, 2, false>), grid, dim3(256), 0, stream, xv, e, M, N, K, tiles_m, partial);
-  }
+  err = launch_sumsq(static_cast<const _Float16*>(x), e, M, N, K, T, tiles_m, grid, partial, 0, nullptr, false, stream);
+  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(loss_finalize_kernel, dim3(count), dim3(256), 0, stream, partial, tiles_m * tiles_n, loss);
   return hipGetLastError();
+}
+
+hipError_t launch_scale_columns(const void* src, int rows, int K, const float* s, bool divide, void* dst,
+                                hipStream_t stream) {
+  const size_t words = (size_t)rows * (K >> 3);
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(scale_columns_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(src), rows, K, s, divide ? 1 : 0, static_cast<u32x4*>(dst));
+  return hipGetLastError();
+}
+
+// Per-group partial errors: part[c][tm][h][j][n], h the two row halves of a tile.
+size_t clip_search_workspace_bytes(int count, int M, int N, int K, int group_size) {
+  const int T = loss_tile(M);
+  const size_t tiles_m = (M + T - 1) / T;
+  return align256((size_t)count * N * K * 2) + align256((size_t)count * tiles_m * 2 * (K / group_size) * N * 4);
+}
+
+hipError_t launch_clip_search(const void* x, const void* w, int M, int N, int K, int group_size, bool zero_point,
+                              const float* ratios, int count, void* w_out, int32_t* choice, void* workspace,
+                              hipStream_t stream) {
+  const int T = loss_tile(M);
+  const int tiles_m = (M + T - 1) / T, tiles_n = (N + T - 1) / T;
+  char* ws = static_cast<char*>(workspace);
+  _Float16* e = reinterpret_cast<_Float16*>(ws);
+  float* gpart = reinterpret_cast<float*>(ws + align256((size_t)count * N * K * 2));
+  ClipRatios r;
+  for (int c = 0; c < kMaxClipCandidates; ++c) r.v[c] = c < count ? ratios[c] : 1.0f;
+  hipError_t err = launch_clip_error(w, r, count, N, K, group_size, zero_point, e, stream);
+  if (err != hipSuccess) return err;
+  err = launch_sumsq(static_cast<const _Float16*>(x), e, M, N, K, T, tiles_m, dim3(tiles_m * tiles_n, count), nullptr,
+                     log2_group(group_size), gpart, true, stream);
+  if (err != hipSuccess) return err;
+  return launch_clip_apply(w, gpart, tiles_m * 2, r, count, N, K, group_size, zero_point, w_out, choice, stream);
 }
 
 }  // namespace awq

@@ -181,6 +181,47 @@ int awq_scale_loss(const void* x, const void* w, const float* s, int32_t count, 
                    void* stream);
 size_t awq_scale_loss_workspace_bytes(int32_t count, int32_t M, int32_t N, int32_t K);
 
+/*
+ * awq_scale_columns - apply per-input-channel scales: dst[r][k] =
+ * fp16(src[r][k] * s[k]) (divide == 0, the weights W * s) or
+ * fp16(src[r][k] / s[k]) (divide != 0, the activations s^-1 * X); fp32
+ * product or correctly rounded fp32 quotient, one rounding to fp16
+ * ("AI-Research-SKILLs AWQ 高级使用指南", section 算法原理: the weights are
+ * scaled by s and the activations by s^-1).
+ * src, dst  fp16 [rows][K] (may be the same buffer); s fp32 [K] > 0.
+ * K must be a multiple of 8.
+ */
+int awq_scale_columns(const void* src, int32_t rows, int32_t K, const float* s, int32_t divide, void* dst,
+                      void* stream);
+
+/*
+ * awq_clip_search - weight clipping for the quantizer (apply_clip:
+ * "AI-Research-SKILLs AWQ 高级使用指南", section 自定义校准数据, clip the
+ * weights to reduce the effect of outliers on the quantization error).  The
+ * pages give no rule; this one: for each ratio r in `ratios` every group's
+ * range shrinks to [r*min, r*max] (zero_point != 0) or [-r*amax, r*amax]
+ * (fp32 products) and its weights are clamped to it (fp32, then fp16); the
+ * error of group (n, j) is
+ *   err(n, j, r) = sum_m ( sum_{k in group j} x[m][k] (Dq(Q(clip_r(W)))[n][k] - w[n][k]) )^2
+ * (Q and Dq as in awq_pack / awq_dequant).  Each group keeps the first ratio
+ * with the smallest error, and w_clipped holds the weights clamped with it;
+ * packing w_clipped with awq_pack gives the clipped quantization.
+ * x          in   fp16 [M][K] calibration activations.
+ * w          in   fp16 [N][K] weights.
+ * ratios     in   HOST array of `count` ratios, each in (0, 1], 1 <= count <= 64.
+ * w_clipped  out  fp16 [N][K].
+ * choice     out  int32 [N][K/group_size]: index of the chosen ratio (may be NULL).
+ * workspace: device scratch of awq_clip_search_workspace_bytes(count, M, N,
+ * K, group_size) bytes, 16-byte aligned; contents not needed before or after.
+ * The errors are evaluated with fp16 weight errors and fp32 accumulation
+ * (relative error ~1e-3); a ratio whose error is within that of the best may
+ * be chosen instead.  Deterministic.
+ */
+int awq_clip_search(const void* x, const void* w, int32_t M, int32_t N, int32_t K, int32_t group_size,
+                    int32_t zero_point, const float* ratios, int32_t count, void* w_clipped, int32_t* choice,
+                    void* workspace, size_t workspace_bytes, void* stream);
+size_t awq_clip_search_workspace_bytes(int32_t count, int32_t M, int32_t N, int32_t K, int32_t group_size);
+
 /* Static, NUL-terminated description of a status code. */
 const char* awq_strerror(int status);
 

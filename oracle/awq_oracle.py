@@ -51,6 +51,14 @@ of the repository):
    give no candidate family; the reading taken is s = a^alpha with
    a_k = max(mean_m |x_mk|, 1e-4) and alpha on a grid in [0, 1); the search
    keeps the candidate with the smallest L(s) (the first one on ties).
+9. Weight clipping ([P5] "自定义校准数据", ``apply_clip``: clip the weights to
+   further reduce the effect of outliers on the quantization error).  The pages
+   give no rule; the reading taken: each group tries ratios r in (0, 1]; its
+   range shrinks to [r*mn, r*mx] (symmetric: [-r*amax, r*amax], fp32 products)
+   and its weights are clamped to it (fp32, then fp16).  The group keeps the r
+   with the smallest output error over the calibration activations,
+   err(n, j, r) = sum_m (sum_{k in group j} x_mk (Dq(Q(clip_r(W)))_nk - w_nk))^2
+   (the first r on ties); the clipped weights are then packed as usual.
 
 Parity pins: every function here is pinned by tests that do not re-type its
 formula (hand-worked examples, brute force over every fp16 value of a range,
@@ -312,3 +320,42 @@ def search_scale(W16: np.ndarray, X16: np.ndarray, g: int, zero_point: bool, alp
     S = scale_candidates(X16, alphas)
     losses = [recon_loss(W16, X16, s, g, zero_point) for s in S]
     return int(np.argmin(losses)), S, losses
+
+
+def clip_weight(W16: np.ndarray, g: int, zero_point: bool, ratio) -> np.ndarray:
+    """Clamp every group of W to its range shrunk by ``ratio`` (reading 9);
+    ``ratio`` is one value or an [N, G] array.  Returns fp16 [N, K]."""
+    N, K, G = _check_shape(W16, g)
+    a = W16.astype(F32).reshape(N, G, g)
+    r = np.broadcast_to(np.asarray(ratio, dtype=F32), (N, G))[:, :, None]
+    if zero_point:
+        lo = (r * a.min(axis=2)[:, :, None]).astype(F32)
+        hi = (r * a.max(axis=2)[:, :, None]).astype(F32)
+    else:
+        hi = (r * np.abs(a).max(axis=2)[:, :, None]).astype(F32)
+        lo = -hi
+    return np.minimum(np.maximum(a, lo), hi).astype(F32).astype(np.float16).reshape(N, K)
+
+
+def clip_errors(W16: np.ndarray, X16: np.ndarray, g: int, zero_point: bool, ratios) -> np.ndarray:
+    """err[i, n, j]: the output error of group (n, j) over the calibration
+    activations when every group is clipped by ratios[i] (reading 9), fp64."""
+    N, K, G = _check_shape(W16, g)
+    X = np.asarray(X16, dtype=np.float64)
+    W = W16.astype(np.float64)
+    out = np.empty((len(ratios), N, G))
+    for i, r in enumerate(ratios):
+        E = fake_quant(clip_weight(W16, g, zero_point, r), g, zero_point) - W
+        for j in range(G):
+            Y = X[:, j * g:(j + 1) * g] @ E[:, j * g:(j + 1) * g].T
+            out[i, :, j] = (Y * Y).sum(axis=0)
+    return out
+
+
+def search_clip(W16: np.ndarray, X16: np.ndarray, g: int, zero_point: bool, ratios):
+    """Per group, the ratio with the smallest output error (reading 9).
+    Returns (choice int [N, G], clipped weights fp16 [N, K], err)."""
+    err = clip_errors(W16, X16, g, zero_point, ratios)
+    best = np.argmin(err, axis=0)
+    Wc = clip_weight(W16, g, zero_point, np.asarray(ratios, dtype=F32)[best])
+    return best, Wc, err

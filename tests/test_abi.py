@@ -153,3 +153,30 @@ def test_scale_search_validation(lib):
     need = awq.load_library().awq_scale_loss_workspace_bytes(3, 4, 8, 128)
     assert need >= 3 * 8 * 128 * 2
     assert loss(3, 4, 8, 128, 32, wsb=need - 1) == awq.AWQ_ERR_WORKSPACE
+
+
+def test_clip_and_scale_columns_validation(lib):
+    ratios = (ctypes.c_float * 3)(1.0, 0.9, 0.8)
+    bad = (ctypes.c_float * 2)(1.0, 1.5)
+    rp = lambda arr: ctypes.cast(arr, ctypes.c_void_p)  # noqa: E731
+    clip = lambda M, N, K, g, cnt, **kw: lib.awq_clip_search(  # noqa: E731
+        kw.get("x", A) or None, kw.get("w", B) or None, M, N, K, g, 1, kw.get("r", rp(ratios)), cnt,
+        kw.get("out", C) or None, kw.get("choice", D) or None, kw.get("ws", E) or None, kw.get("wsb", 1 << 40), None)
+    assert clip(4, 12, 128, 32, 3) == awq.AWQ_ERR_SHAPE
+    assert clip(4, 8, 100, 32, 3) == awq.AWQ_ERR_GROUP
+    assert clip(0, 8, 128, 32, 3) == awq.AWQ_ERR_SHAPE
+    assert clip(4, 8, 128, 32, 0) == awq.AWQ_ERR_SHAPE
+    assert clip(4, 8, 128, 32, 65) == awq.AWQ_ERR_SHAPE
+    assert clip(4, 8, 128, 32, 2, r=rp(bad)) == awq.AWQ_ERR_SHAPE
+    assert clip(4, 8, 128, 32, 3, out=0) == awq.AWQ_ERR_NULL
+    assert clip(4, 8, 128, 32, 3, choice=D + 2) == awq.AWQ_ERR_ALIGN
+    assert clip(4, 8, 128, 32, 3, w=B + 8) == awq.AWQ_ERR_ALIGN
+    need = awq.load_library().awq_clip_search_workspace_bytes(3, 4, 8, 128, 32)
+    assert need >= 3 * 8 * 128 * 2
+    assert clip(4, 8, 128, 32, 3, wsb=need - 1) == awq.AWQ_ERR_WORKSPACE
+    cols = lambda rows, K, **kw: lib.awq_scale_columns(  # noqa: E731
+        kw.get("src", A) or None, rows, K, kw.get("s", B) or None, 0, kw.get("dst", C) or None, None)
+    assert cols(0, 64) == awq.AWQ_ERR_SHAPE
+    assert cols(4, 12) == awq.AWQ_ERR_SHAPE
+    assert cols(4, 64, s=0) == awq.AWQ_ERR_NULL
+    assert cols(4, 64, dst=C + 2) == awq.AWQ_ERR_ALIGN

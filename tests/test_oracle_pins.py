@@ -352,6 +352,67 @@ def check_search_scale():
     assert best > 0 and losses[best] < 0.8 * losses[0]
 
 
+def check_clip_weight():
+    gold = read_golden("hand_asym_g8.txt")
+    w = _num(gold["w"]).astype(np.float16)[None, :]
+    for zp in (True, False):
+        assert np.array_equal(O.clip_weight(w, 8, zp, 1.0).view(np.uint16), w.view(np.uint16))
+    # r = 1/2: asymmetric range [-0.125, 0.34375]; symmetric [-0.34375, 0.34375]
+    half = [-0.125, 0.34375, 0, 0.125, -0.0625, 0.3125, 0.34375, 0.03125]
+    assert np.array_equal(O.clip_weight(w, 8, True, 0.5)[0].astype(np.float64), half)
+    sym = [-0.25, 0.34375, 0, 0.125, -0.0625, 0.3125, 0.34375, 0.03125]
+    assert np.array_equal(O.clip_weight(w, 8, False, 0.5)[0].astype(np.float64), sym)
+    # per-group ratios: each group uses its own
+    W = workloads.weight(8, 64, cfg=97, layer=3)
+    r = np.linspace(0.5, 1.0, 16, dtype=np.float32).reshape(8, 2)
+    Wc = O.clip_weight(W, 32, True, r)
+    for n in range(8):
+        for j in range(2):
+            assert np.array_equal(Wc[n, 32 * j:32 * j + 32], O.clip_weight(W[n:n + 1, 32 * j:32 * j + 32], 32, True,
+                                                                              r[n, j])[0])
+
+
+def check_clip_errors():
+    # brute force on a tiny layer, straight from the definition
+    W = workloads.weight(8, 16, cfg=97, layer=4)
+    X = workloads.activations(3, 16, cfg=97, layer=4)
+    ratios = [1.0, 0.75, 0.5]
+    for zp in (True, False):
+        err = O.clip_errors(W, X, 8, zp, ratios)
+        for i, r in enumerate(ratios):
+            Wq = O.fake_quant(O.clip_weight(W, 8, zp, r), 8, zp)
+            for n in range(8):
+                for j in range(2):
+                    tot = 0.0
+                    for m in range(3):
+                        y = math.fsum(float(X[m, k]) * (Wq[n, k] - float(W[n, k])) for k in range(8 * j, 8 * j + 8))
+                        tot += y * y
+                    assert abs(err[i, n, j] - tot) <= 1e-12 * max(tot, 1e-30)
+    # one group per row: the unclipped errors add up to L(1)^2
+    W = workloads.weight(16, 128, cfg=97, layer=5)
+    X = workloads.activations(8, 128, cfg=97, layer=5)
+    e1 = O.clip_errors(W, X, 128, True, [1.0])
+    L = O.recon_loss(W, X, np.ones(128, np.float32), 128, True)
+    assert abs(e1.sum() - L * L) <= 1e-12 * L * L
+
+
+def check_search_clip():
+    W = workloads.weight(64, 256, cfg=97, layer=1)
+    X = workloads.activations(64, 256, cfg=97, layer=1)
+    ratios = [1 - 0.025 * i for i in range(20)]
+    best, Wc, err = O.search_clip(W, X, 64, True, ratios)
+    assert best.shape == (64, 4) and Wc.dtype == np.float16
+    n, j = np.meshgrid(np.arange(64), np.arange(4), indexing="ij")
+    assert np.all(err[best, n, j] == err.min(axis=0))
+    assert np.all(err[best, n, j] <= err[0])
+    # clipping pays off on these weights, and the clipped layer has a lower L(1)
+    assert np.count_nonzero(best) > 64
+    Xd = X.astype(np.float64)
+    ref = Xd @ W.astype(np.float64).T
+    assert np.linalg.norm(Xd @ O.fake_quant(Wc, 64, True).T - ref) < 0.8 * O.recon_loss(
+        W, X, np.ones(256, np.float32), 64, True)
+
+
 def check_matmul_exact(seed=8):
     W = workloads.weight(512, 512, cfg=0, layer=0, seed=0)
     X = workloads.activations(1, 512, cfg=0, layer=0, seed=0)
@@ -428,6 +489,18 @@ def test_search_scale():
     check_search_scale()
 
 
+def test_clip_weight():
+    check_clip_weight()
+
+
+def test_clip_errors():
+    check_clip_errors()
+
+
+def test_search_clip():
+    check_search_clip()
+
+
 def test_matmul_ref_against_fsum():
     check_matmul_exact()
 
@@ -471,6 +544,9 @@ ALL_CHECKS = (
     check_matmul_exact,
     check_scale_candidates,
     check_search_scale,
+    check_clip_weight,
+    check_clip_errors,
+    check_search_clip,
 )
 
 
@@ -500,6 +576,8 @@ MUTATIONS = {
     "act_stat_max_not_mean": None,
     "candidate_inverse_power": None,
     "search_keeps_largest_loss": None,
+    "clip_low_bound_unscaled": None,
+    "clip_error_against_clipped_weight": None,
 }
 
 
@@ -571,6 +649,30 @@ def _patch_function(mp, name):
             return int(np.argmax(losses)), S, losses
 
         mp.setattr(O, "search_scale", search)
+    elif name == "clip_low_bound_unscaled":
+        def cw(W16, g, zero_point, ratio):
+            N, K = W16.shape
+            a = W16.astype(np.float32).reshape(N, K // g, g)
+            r = np.broadcast_to(np.asarray(ratio, dtype=np.float32), (N, K // g))[:, :, None]
+            hi = (r * (a.max(axis=2) if zero_point else np.abs(a).max(axis=2))[:, :, None]).astype(np.float32)
+            lo = a.min(axis=2)[:, :, None] if zero_point else -hi
+            return np.minimum(np.maximum(a, lo), hi).astype(np.float16).reshape(N, K)
+
+        mp.setattr(O, "clip_weight", cw)
+    elif name == "clip_error_against_clipped_weight":
+        def ce(W16, X16, g, zero_point, ratios):
+            N, K = W16.shape
+            X = np.asarray(X16, dtype=np.float64)
+            out = np.empty((len(ratios), N, K // g))
+            for i, r in enumerate(ratios):
+                Wc = O.clip_weight(W16, g, zero_point, r)
+                E = O.fake_quant(Wc, g, zero_point) - Wc.astype(np.float64)
+                for j in range(K // g):
+                    Y = X[:, j * g:(j + 1) * g] @ E[:, j * g:(j + 1) * g].T
+                    out[i, :, j] = (Y * Y).sum(axis=0)
+            return out
+
+        mp.setattr(O, "clip_errors", ce)
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
