@@ -232,7 +232,7 @@ __global__ __launch_bounds__(kPackThreads) void scale_error_kernel(const u32x4* 
 }
 
 // Output error of weight clipping, for the search of apply_clip ("AI-Research-
-// SKILLs AWQ 高级使用指南", section 自定义校准数据: clip the weights to reduce
+// SKILLs AWQ 高级使用指南", section 自定义校准策略 (校准参数全景): clip the weights to reduce
 // the effect of outliers on the quantization error).  For candidate ratio
 // r_c (blockIdx.y): every group is clamped to its range shrunk by r_c (fp32,
 // then fp16), quantized as by pack_kernel, decoded, and compared with the

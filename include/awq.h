@@ -196,7 +196,7 @@ int awq_scale_columns(const void* src, int32_t rows, int32_t K, const float* s, 
 
 /*
  * awq_clip_search - weight clipping for the quantizer (apply_clip:
- * "AI-Research-SKILLs AWQ 高级使用指南", section 自定义校准数据, clip the
+ * "AI-Research-SKILLs AWQ 高级使用指南", section 自定义校准策略 (校准参数全景), clip the
  * weights to reduce the effect of outliers on the quantization error).  The
  * pages give no rule; this one: for each ratio r in `ratios` every group's
  * range shrinks to [r*min, r*max] (zero_point != 0) or [-r*amax, r*amax]

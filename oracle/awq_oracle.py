@@ -51,7 +51,7 @@ of the repository):
    give no candidate family; the reading taken is s = a^alpha with
    a_k = max(mean_m |x_mk|, 1e-4) and alpha on a grid in [0, 1); the search
    keeps the candidate with the smallest L(s) (the first one on ties).
-9. Weight clipping ([P5] "自定义校准数据", ``apply_clip``: clip the weights to
+9. Weight clipping ([P5] "自定义校准策略" (校准参数全景), ``apply_clip``: clip the weights to
    further reduce the effect of outliers on the quantization error).  The pages
    give no rule; the reading taken: each group tries ratios r in (0, 1]; its
    range shrinks to [r*mn, r*mx] (symmetric: [-r*amax, r*amax], fp32 products)
