@@ -21,10 +21,10 @@
 //     (or 256 x 128 for the last wave of tiles) per workgroup of 8 waves
 //     (2 x 4, 128 x 64 each, v_mfma_f32_32x32x16_f16), K in steps of 64.  X
 //     tiles go from HBM straight into LDS (buffer-to-LDS loads); packed
-//     weights are fetched two steps ahead into registers, decoded and stored
-//     to LDS as fp16 interleaved with the current step's MFMAs.  LDS tiles use
-//     an XOR swizzle instead of padding; workgroups are mapped so that each
-//     XCD (and its L2) works on a contiguous band of tiles.
+//     weights are fetched two steps ahead into registers and decoded straight
+//     into MFMA B operands (no LDS on the weight path).  LDS tiles use an XOR
+//     swizzle instead of padding; workgroups are mapped so that each XCD (and
+//     its L2) works on a contiguous band of tiles, in groups of 4 tile rows.
 //
 // MFMA operand placement: a lane's 8 fp16 values of A and of B cover the same
 // 8 reduction indices, so any assignment of channels to (lane group, element)
@@ -341,46 +341,41 @@ constexpr int TILE_BYTES = BM * BK * 2;  // one 256 x 64 fp16 tile in LDS (32 Ki
 // the MFMA fragment reads are conflict-free without padding, and a 1 KiB run
 // of slots is exactly what one buffer-to-LDS load of 64 lanes x 16 bytes writes.
 __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
-__device__ __forceinline__ uint32_t swz(int row, int chunk) { return (uint32_t)(row * 128 + 16 * swz_chunk(row, chunk)); }
-
-// Registers holding one K step of packed weights on their way to LDS.
-struct StepRegs {
-  u32x4 w;       // 32 channels of packed weights
-  uint32_t s;    // raw fp16 scale (low half)
-  uint32_t z;    // zero-point word
-};
 
 // 2 x 4 waves of 128 x (32 NB) outputs (two waves per SIMD); tile width
-// 128 NB.  Every global access goes through a buffer resource based at the
-// tile: a thread's 32-bit offsets are fixed for the whole K loop and the step
-// advances an SGPR offset; rows past M or N read as zero.
-// Software pipeline, one barrier per K step:
-//   iteration s: load the X tile of step s + 1 straight into LDS buffer
-//   (s + 1) & 1 (buffer-to-LDS DMA, no registers), issue the packed-weight
-//   loads of step s + 2 into registers, multiply step s out of buffer s & 1
-//   and, interleaved with those MFMAs, decode step s + 1's weights into
-//   buffer (s + 1) & 1.
-// The loop has no branches: loads for steps past the end stay inside the
-// buffers (or return zero) and land in an LDS buffer no one reads again.
+// 128 NB.  Only X goes through LDS: tiles go from HBM straight into LDS by
+// buffer-to-LDS loads, double-buffered, one step ahead.  The weights go to the
+// matrix cores without LDS: with the channel-to-slot assignment below, the B
+// fragment of a lane for one 16-channel slice is one packed word of one
+// weight row, so lane (n, h) of a wave loads the 32 channels 64 s + 32 h .. +32
+// of its row as one 16-byte word (four slices) two steps ahead and decodes
+// each word right before its MFMAs.  Both M-halves of the workgroup decode
+// the same rows, in exchange for no weight stores, no weight fragment reads
+// and no barrier on the weights.  Every global access goes through a buffer
+// resource based at the tile (rows past M or N read as zero), and the K loop
+// has no branches: loads for steps past the end stay inside the buffers (or
+// return zero) and land where no one reads again.
+//   MFMA slice ks of step s, lane half h, element j  <->  channel 64 s + 32 h + 8 ks + j
+// (A and B use the same assignment, so the product is unchanged.)
 template <bool ZP, bool KTAIL, int NB>
 __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restrict__ X,
-                                                         const uint32_t* __restrict__ qweight,
-                                                         const uint16_t* __restrict__ scales,
-                                                         const uint32_t* __restrict__ qzeros,
-                                                         _Float16* __restrict__ Y, int M, int N, int K, int gshift,
-                                                         int tiles_m, int group_m, int ldy) {
-  constexpr int WN = 32 * NB;                 // wave tile width (N): 64, or 32 for half-width tiles
-  constexpr int TBN = 4 * WN;                 // workgroup tile width: 256 or 128
-  __shared__ __attribute__((aligned(1024))) char lds[2][2][TILE_BYTES];  // [buffer][X | W']
+                                                             const uint32_t* __restrict__ qweight,
+                                                             const uint16_t* __restrict__ scales,
+                                                             const uint32_t* __restrict__ qzeros,
+                                                             _Float16* __restrict__ Y, int M, int N, int K, int gshift,
+                                                             int tiles_m, int group_m, int ldy) {
+  constexpr int WN = 32 * NB;  // wave tile width (N)
+  constexpr int TBN = 4 * WN;  // workgroup tile width
+  __shared__ __attribute__((aligned(1024))) char lx0[TILE_BYTES], lx1[TILE_BYTES];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
   const int tiles_n = gridDim.x / tiles_m;
-  const int per_group = group_m * tiles_n, grp = tile / per_group, first_m = grp * group_m;
-  const int gm = min(tiles_m - first_m, group_m), r_in = tile - grp * per_group;
+  const int per_group = group_m * tiles_n, grp0 = tile / per_group, first_m = grp0 * group_m;
+  const int gm = min(tiles_m - first_m, group_m), r_in = tile - grp0 * per_group;
   const int tm = first_m + r_in % gm, tn = r_in / gm;
   const int m0 = tm * BM, n0 = tn * TBN;
-  const int rows_m = min(BM, M - m0), rows_n = min(TBN, N - n0);  // rows_n is a multiple of 8
+  const int rows_m = min(BM, M - m0), rows_n = min(TBN, N - n0);
   const int wm = (wave & 1) * 128, wn = (wave >> 1) * WN;
   const int nsteps = (K + BK - 1) / BK;
   const int G = K >> gshift;
@@ -392,10 +387,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(ZP ? qzeros + zero_word_index(n0, 0, G) : qzeros,
                                               ZP ? (uint32_t)(rows_n >> 3) * G * 4 : 0u);
 
-  // X: wave w fills LDS rows 32 w .. 32 w + 31 with 4 loads of 8 rows x 128 B;
-  // lane l of load j writes slot l of that 1 KiB run: row 32 w + 8 j + l / 8,
-  // physical chunk l % 8, which holds the logical chunk that swizzles there
-  // (the swizzle is an involution).
+  // X: as in gemm_large_kernel (wave w fills rows 32 w .. 32 w + 31)
   int xchunk[4];
   uint32_t xoff[4];
 #pragma unroll
@@ -404,23 +396,13 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
     xchunk[j] = swz_chunk(row, lane & 7);
     xoff[j] = (uint32_t)row * K * 2 + xchunk[j] * 16;
   }
-
-  // W: thread t loads one 16-byte piece (32 channels) of row t >> 1, plus the
-  // scale and zero-point word of the piece's group (threads past the tile's
-  // 2 * TBN pieces of a half-width tile read rows past its end: zeros, unused).
-  const int wr = t >> 1, piece = t & 1;
-  const uint32_t woff = (uint32_t)wr * (K >> 1) + piece * 16;
-  const bool g32 = gshift == 5;  // with g = 32 the two pieces of a step are two groups
-  const uint32_t soff = (uint32_t)(((wr >> 3) * G * 8 + (wr & 7)) * 2) + (g32 ? piece * 16 : 0);
-  const uint32_t zoff = (uint32_t)((wr >> 3) * G * 4) + (g32 ? piece * 4 : 0);
-  const int zshift = 4 * (wr & 7);
-
-  auto load_x = [&](int step) {
-    char* dst = lds[step & 1][0] + wave * 4096;
+  // `buf` is a constant at every call site (the K loop is unrolled by two)
+  auto load_x = [&](int step, int buf) {
+    char* dst = (buf ? lx1 : lx0) + wave * 4096;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint32_t off = xoff[j];
-      if constexpr (KTAIL) {  // channels past K of the last step load as zero
+      if constexpr (KTAIL) {
         if (step * BK + 8 * xchunk[j] >= K) off = kOutOfRange;
       }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16, off,
@@ -428,18 +410,34 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
     }
   };
 
-  auto fetch_w = [&](StepRegs& r, int step) {
-    const int grp = (step * BK) >> gshift;  // group of piece 0
-    r.w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, woff, step * (BK / 2), 0));
-    r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, soff, grp * 16, 0);
-    r.z = ZP ? __builtin_amdgcn_raw_buffer_load_b32(rz, zoff, grp * 4, 0) : 0u;
+  // W: lane (n = lane % 32, h = lane / 32) of this wave, rows wn + 32 b + n
+  const int fi = lane & 31, fh = lane >> 5;
+  uint32_t woff[NB], soff[NB], zoff[NB];
+  int zshift[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int row = wn + 32 * b + fi;
+    woff[b] = (uint32_t)row * (K >> 1) + fh * 16;
+    soff[b] = (uint32_t)(((row >> 3) * G * 8 + (row & 7)) * 2);
+    zoff[b] = (uint32_t)((row >> 3) * G * 4);
+    zshift[b] = 4 * (row & 7);
+  }
+  struct WRegs {
+    u32x4 w[NB];
+    uint32_t s[NB], z[NB];
   };
-
-  // One quarter (q = 0..3) of a step's W' stash: one decoded word per thread.
-  auto stash_part = [&](const StepRegs& r, int buf, int q) {
-    const uint32_t z = ZP ? ((r.z >> zshift) & 15u) : 8u;
-    const half8_t v = decode_word_scaled(r.w[q], zero_bias(z), kc, splat2(__builtin_bit_cast(_Float16, (uint16_t)r.s)));
-    if (TBN == BN || wr < TBN) *reinterpret_cast<half8_t*>(lds[buf][1] + swz(wr, 4 * piece + q)) = v;
+  auto fetch_w = [&](WRegs& r, int step) {
+    const int k0 = step * BK + 32 * fh;
+    const bool kin = !KTAIL || k0 < K;
+    const int grp = k0 >> gshift;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      r.w[b] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, kin ? woff[b] : kOutOfRange, step * (BK / 2), 0));
+      // the group depends on the lane half: a per-lane offset, not a uniform one
+      r.s[b] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[b] + grp * 16, 0, 0);
+      r.z[b] = ZP ? __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[b] + grp * 4, 0, 0) : 0u;
+    }
   };
 
   float16_t acc[4][NB];
@@ -450,64 +448,58 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-  const int fi = lane & 31, fh = lane >> 5;  // fragment row and k-half of this lane
-  const int fsw = (fi >> 1) & 7;             // swizzle of the fragment rows (tile row bases are multiples of 32)
-
-  // Multiply step `step` out of LDS buffer step & 1 and stash `nxt` (packed
-  // weights of step + 1) into the other buffer, a quarter per 16-channel slice.
-  auto compute = [&](int step, const StepRegs& nxt) {
-    const int buf = step & 1;
-    const char* xa = lds[buf][0] + (wm + fi) * 128;
-    const char* wb = lds[buf][1] + (wn + fi) * 128;
-    half8_t af[2][4], bf[2][NB];
+  const int fsw = (fi >> 1) & 7;  // swizzle of the fragment rows (tile row bases are multiples of 32)
+  auto compute = [&](int buf, const WRegs& r) {
+    const char* xa = (buf ? lx1 : lx0) + (wm + fi) * 128;
+    ZeroBias zb[NB];
+    half2_t s2[NB];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) af[0][a] = *reinterpret_cast<const half8_t*>(xa + 32 * 128 * a + 16 * (fh ^ fsw));
+    for (int b = 0; b < NB; ++b) {
+      zb[b] = zero_bias(ZP ? ((r.z[b] >> zshift[b]) & 15u) : 8u);
+      s2[b] = splat2(__builtin_bit_cast(_Float16, (uint16_t)r.s[b]));
+    }
+    half8_t af[2][4];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) bf[0][b] = *reinterpret_cast<const half8_t*>(wb + 32 * 128 * b + 16 * (fh ^ fsw));
+    for (int a = 0; a < 4; ++a) af[0][a] = *reinterpret_cast<const half8_t*>(xa + 32 * 128 * a + 16 * ((4 * fh) ^ fsw));
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int cur = ks & 1, nx = cur ^ 1;
       if (ks + 1 < BK / 16) {
-        const int slot = 16 * ((2 * (ks + 1) + fh) ^ fsw);
+        const int slot = 16 * ((4 * fh + ks + 1) ^ fsw);
 #pragma unroll
         for (int a = 0; a < 4; ++a) af[nx][a] = *reinterpret_cast<const half8_t*>(xa + 32 * 128 * a + slot);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) bf[nx][b] = *reinterpret_cast<const half8_t*>(wb + 32 * 128 * b + slot);
       }
+      half8_t bf[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) bf[b] = decode_word_scaled(r.w[b][ks], zb[b], kc, s2[b]);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][a], bf[cur][b], acc[a][b], 0, 0, 0);
-      stash_part(nxt, buf ^ 1, ks);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][a], bf[b], acc[a][b], 0, 0, 0);
     }
   };
 
-  StepRegs ra, rb;
-  load_x(0);
+  WRegs ra, rb;
+  load_x(0, 0);
   fetch_w(ra, 0);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) stash_part(ra, 0, q);
   fetch_w(rb, 1);
   __syncthreads();
-
-  // two steps per trip so that the register sets keep static names
   int step = 0;
   for (; step + 1 < nsteps; step += 2) {
-    load_x(step + 1);
+    load_x(step + 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0, ra);
     fetch_w(ra, step + 2);
-    compute(step, rb);
     __syncthreads();
-    load_x(step + 2);
+    load_x(step + 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1, rb);
     fetch_w(rb, step + 3);
-    compute(step + 1, ra);
     __syncthreads();
   }
-  if (step < nsteps) compute(step, rb);
+  if (step < nsteps) compute(0, ra);
 
-  // 32x32 accumulator layout: lane l holds column l % 32 and, in register r,
-  // row 8 * (r / 4) + 4 * (l / 32) + r % 4.  Rows past M fall outside the
-  // buffer and are dropped; columns past N are skipped.
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y + (size_t)m0 * ldy, (uint32_t)rows_m * ldy * 2);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
