@@ -286,28 +286,40 @@ __global__ __launch_bounds__(kPackThreads) void clip_apply_kernel(const u32x4* _
                                                                   u32x4* __restrict__ w_out,
                                                                   int32_t* __restrict__ choice) {
   const int t = threadIdx.x;
-  const int r = t >> 5, l = t & 31, lane = t & 63;
+  const int r = t >> 5, l = t & 31;
   const int n = blockIdx.x * 8 + r;
   const int kw = K >> 3;
   const int G = kw / GW;
   for (int w0 = 0; w0 < kw; w0 += 32) {
     const int j = w0 + l;
     const bool active = j < kw;
-    const int grp = j / GW;
-    int best = 0;
-    if (active && (l % GW) == 0) {
-      double best_v = 0.0;
-      for (int c = 0; c < count; ++c) {
+    const int grp = j / GW, gl = l % GW;
+    // lane gl of the group sums the partials of ratios gl, gl + GW, ... (each
+    // in a fixed order); the group then takes the smallest error, the lowest
+    // ratio index among equal ones
+    double best_v = __builtin_huge_val();
+    int best = 0x7fffffff;
+    if (active) {
+      for (int c = gl; c < count; c += GW) {
         double v = 0.0;
         for (int p = 0; p < parts; ++p) v += (double)part[(((size_t)c * parts + p) * G + grp) * N + n];
-        if (c == 0 || v < best_v) {
+        if (v < best_v) {
           best_v = v;
           best = c;
         }
       }
-      if (choice) choice[(size_t)n * G + grp] = best;
     }
-    best = __shfl(best, lane & ~(GW - 1));
+#pragma unroll
+    for (int off = 1; off < GW; off <<= 1) {
+      const double ov = __shfl_xor(best_v, off);
+      const int oi = __shfl_xor(best, off);
+      if (ov < best_v || (ov == best_v && oi < best)) {
+        best_v = ov;
+        best = oi;
+      }
+    }
+    if (!active) best = 0;
+    if (active && gl == 0 && choice) choice[(size_t)n * G + grp] = best;
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (active) raw = w[(size_t)n * kw + j];
     const half8_t h = as_half8(raw);
