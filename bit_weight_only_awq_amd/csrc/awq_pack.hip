@@ -22,6 +22,34 @@ namespace {
 constexpr int kPackThreads = 256;  // 8 rows x 32 lanes
 constexpr float kRangeFloor = 1e-5f;
 
+// Combine v over the GW consecutive lanes of a group (GW = 4, 8, 16 or 32,
+// aligned); every lane gets the result.  Partners come by DPP lane swaps
+// inside the 16-lane rows (xor 1 and xor 2 within quads, then mirrored
+// halves of 8 lanes, then the mirrored halves of the row) and, for 32-lane
+// groups, one permute across the two rows.  op is min or max, so the order
+// of the combinations does not change the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+template <int GW, class Op>
+__device__ __forceinline__ float group_all(float v, Op op) {
+  if constexpr (GW >= 2) v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  if constexpr (GW >= 4) v = op(v, dpp_mov<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  if constexpr (GW >= 8) v = op(v, dpp_mov<0x141>(v));  // row_half_mirror
+  if constexpr (GW >= 16) v = op(v, dpp_mov<0x140>(v)); // row_mirror
+  if constexpr (GW >= 32) v = op(v, __shfl_xor(v, 16));
+  return v;
+}
+
+struct MinOp {
+  __device__ float operator()(float a, float b) const { return fminf(a, b); }
+};
+struct MaxOp {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
 // Scale and zero point of the group a lane's 8 weights belong to.  A group of
 // g channels is GW = g/8 consecutive lanes of one row, reduced with butterfly
 // shuffles (GW divides 32, so a group never leaves its half-wave, and all
@@ -36,11 +64,8 @@ __device__ __forceinline__ void group_scale_zero(const float (&a)[8], _Float16& 
       mn = fminf(mn, a[c]);
       mx = fmaxf(mx, a[c]);
     }
-#pragma unroll
-    for (int off = 1; off < GW; off <<= 1) {
-      mn = fminf(mn, __shfl_xor(mn, off));
-      mx = fmaxf(mx, __shfl_xor(mx, off));
-    }
+    mn = group_all<GW>(mn, MinOp());
+    mx = group_all<GW>(mx, MaxOp());
     float rng = mx - mn;
     if (rng < kRangeFloor) rng = kRangeFloor;
     s16 = (_Float16)(rng / 15.0f);
@@ -51,8 +76,7 @@ __device__ __forceinline__ void group_scale_zero(const float (&a)[8], _Float16& 
     float amax = fabsf(a[0]);
 #pragma unroll
     for (int c = 1; c < 8; ++c) amax = fmaxf(amax, fabsf(a[c]));
-#pragma unroll
-    for (int off = 1; off < GW; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    amax = group_all<GW>(amax, MaxOp());
     if (amax < kRangeFloor) amax = kRangeFloor;
     s16 = (_Float16)(amax / 7.0f);
     s = (float)s16;
@@ -78,19 +102,15 @@ __device__ __forceinline__ void group_clip_bounds(const float (&a)[8], float r, 
       mn = fminf(mn, a[c]);
       mx = fmaxf(mx, a[c]);
     }
-#pragma unroll
-    for (int off = 1; off < GW; off <<= 1) {
-      mn = fminf(mn, __shfl_xor(mn, off));
-      mx = fmaxf(mx, __shfl_xor(mx, off));
-    }
+    mn = group_all<GW>(mn, MinOp());
+    mx = group_all<GW>(mx, MaxOp());
     lo = r * mn;
     hi = r * mx;
   } else {
     float amax = fabsf(a[0]);
 #pragma unroll
     for (int c = 1; c < 8; ++c) amax = fmaxf(amax, fabsf(a[c]));
-#pragma unroll
-    for (int off = 1; off < GW; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    amax = group_all<GW>(amax, MaxOp());
     hi = r * amax;
     lo = -hi;
   }
@@ -98,67 +118,67 @@ __device__ __forceinline__ void group_clip_bounds(const float (&a)[8], float r, 
 
 // One block quantizes one octet of rows (n0 .. n0+7).  Thread t works on row
 // n0 + (t >> 5); its lane l = t & 31 owns one packed word (8 channels) of each
-// 256-channel pass over the row.  The octet's scales and zero points are
-// staged in LDS and stored as one 16-byte scale vector and one zero-point word
-// per group (row-octet-major layout).
+// 256-channel pass over the row, so wave w holds rows 2w (lanes 0..31) and
+// 2w + 1 (lanes 32..63).  The first lane of each group stores its row's fp16
+// scale into the octet's 16-byte scale vector, and the rows 2w and 2w + 1
+// share one byte of the octet's zero-point word (two nibbles), written by the
+// row-2w lane after one exchange: no LDS, no barriers.
 template <int GW, bool ZP>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restrict__ w, int N, int K,
                                                             uint32_t* __restrict__ qweight,
                                                             uint16_t* __restrict__ scales,
                                                             uint32_t* __restrict__ qzeros) {
-  constexpr int kGroupsPerPass = 32 / GW;
-  __shared__ __attribute__((aligned(16))) uint16_t s_lds[kGroupsPerPass][8];
-  __shared__ uint8_t z_lds[kGroupsPerPass][8];
-
   const int t = threadIdx.x;
   const int r = t >> 5, l = t & 31;
-  const int n0 = blockIdx.x * 8;
-  const int n = n0 + r;
+  const int n = blockIdx.x * 8 + r;
   const int kw = K >> 3;            // packed words per row
-  const int ngroups = kw / GW;      // groups per row
+  const int G = kw / GW;            // groups per row
+  uint16_t* soct = scales + (size_t)blockIdx.x * G * 8;
+  uint8_t* zoct = reinterpret_cast<uint8_t*>(qzeros + (ZP ? (size_t)blockIdx.x * G : 0));
 
-  // the next pass's weights are loaded while this pass is quantized
+  // kDepth passes of weights are in flight per lane: a lane streams its row
+  // with a ring of loads kDepth passes ahead of the one it quantizes
+  constexpr int kDepth = 4;
   const u32x4* wrow = w + (size_t)n * kw;
-  u32x4 next = {0u, 0u, 0u, 0u};
-  if (l < kw) next = wrow[l];
-  for (int w0 = 0; w0 < kw; w0 += 32) {
-    const int j = w0 + l;
-    const bool active = j < kw;
-    const u32x4 raw = next;
-    next = u32x4{0u, 0u, 0u, 0u};
-    if (j + 32 < kw) next = wrow[j + 32];
-    const half8_t h = as_half8(raw);
-
-    float a[8];
+  u32x4 ring[kDepth];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) a[c] = (float)h[c];
-
-    float s, zf;
-    _Float16 s16;
-    group_scale_zero<GW, ZP>(a, s16, s, zf);
-
-    uint32_t word = 0;
+  for (int u = 0; u < kDepth; ++u) {
+    const int j = 32 * u + l;
+    ring[u] = j < kw ? wrow[j] : u32x4{0u, 0u, 0u, 0u};
+  }
+  for (int w0 = 0; w0 < kw; w0 += 32 * kDepth) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) word |= (uint32_t)code_of(a[c], s, zf) << nibble_shift(c);
-    if (active) qweight[(size_t)n * kw + j] = word;
+    for (int u = 0; u < kDepth; ++u) {
+      const int j = w0 + 32 * u + l;
+      if (j - l >= kw) break;  // uniform: no pass left
+      const bool active = j < kw;
+      const u32x4 raw = ring[u];
+      const int jn = j + 32 * kDepth;
+      ring[u] = jn < kw ? wrow[jn] : u32x4{0u, 0u, 0u, 0u};
+      const half8_t h = as_half8(raw);
 
-    if (active && (l % GW) == 0) {
-      s_lds[l / GW][r] = __builtin_bit_cast(uint16_t, s16);
-      z_lds[l / GW][r] = (uint8_t)zf;
-    }
-    __syncthreads();
-    const int gbase = w0 / GW;
-    if (t < kGroupsPerPass && gbase + t < ngroups) {
-      const size_t octet_group = (size_t)blockIdx.x * ngroups + gbase + t;
-      *reinterpret_cast<u32x4*>(scales + octet_group * 8) = *reinterpret_cast<const u32x4*>(&s_lds[t][0]);
+      float a[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) a[c] = (float)h[c];
+
+      float s, zf;
+      _Float16 s16;
+      group_scale_zero<GW, ZP>(a, s16, s, zf);
+
+      uint32_t word = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) word |= (uint32_t)code_of(a[c], s, zf) << nibble_shift(c);
+      if (active) qweight[(size_t)n * kw + j] = word;
+
+      const int grp = j / GW;
+      const bool leader = active && (l % GW) == 0;
+      if (leader) soct[(size_t)grp * 8 + r] = __builtin_bit_cast(uint16_t, s16);
       if constexpr (ZP) {
-        uint32_t zw = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) zw |= (uint32_t)z_lds[t][i] << (4 * i);
-        qzeros[octet_group] = zw;
+        const float zpartner = __shfl_xor(zf, 32);  // row 2w + 1's zero point, same group
+        if (leader && (r & 1) == 0)
+          zoct[(size_t)grp * 4 + (r >> 1)] = (uint8_t)((uint32_t)zf | ((uint32_t)zpartner << 4));
       }
     }
-    __syncthreads();
   }
 }
 
