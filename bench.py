@@ -21,7 +21,7 @@ cpu_baseline = the CPU oracle (decode + fp64 product) on one block, timed on
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--blocks 32]
                        [--legs all|none|<comma list>] [--no-cpu-baseline]
-       python bench.py --leg-only pack|fused|batched|prefill|scale|clip   (one leg, for profiling)
+       python bench.py --leg-only pack|fused|batched|prefill|scale|clip|power   (one leg, for profiling)
        python bench.py --copy-calibration | --summarize DB... [--kernel-filter NAME]
 """
 from __future__ import annotations
@@ -61,7 +61,7 @@ def parse():
     ap.add_argument("--summarize", nargs="+", metavar="DB",
                     help="print a per-kernel summary of rocprofv3 result databases and exit")
     ap.add_argument("--kernel-filter", default=None, help="with --summarize: only kernels whose name contains this")
-    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "prefill", "scale", "clip"],
+    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "prefill", "scale", "clip", "power"],
                     help="run just this leg (no headline, no CPU baseline) and print its JSON; for profiling")
     return ap.parse_args()
 
@@ -380,6 +380,69 @@ def leg_clip_search(torch, awq, workloads, g=128, zp=True, M=512, iters=5):
     return out
 
 
+def _smi_sample():
+    """Socket power (amd-smi) and graphics clock (rocm-smi) of GPU 0, as text."""
+    import subprocess
+
+    out = {}
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p"], capture_output=True, text=True, timeout=20)
+        for line in r.stdout.splitlines():
+            if "SOCKET_POWER" in line:
+                out["socket_power"] = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError) as e:
+        out["socket_power"] = f"unavailable ({e.__class__.__name__})"
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        for line in r.stdout.splitlines():
+            if "sclk" in line:
+                out["sclk"] = line.split(":", 2)[-1].strip()
+                break
+    except (OSError, subprocess.SubprocessError) as e:
+        out["sclk"] = f"unavailable ({e.__class__.__name__})"
+    return out
+
+
+def leg_power(torch, awq, workloads, g=128, zp=True, seconds=2.0):
+    """Power and clock of the prefill GEMM (70B down_proj, M = 2048) under
+    sustained load, with the synthetic activations and with all-zero ones
+    (the same kernel and instruction stream; fewer operand bit flips).  Shows
+    whether the matrix-core kernel runs at the part's power limit."""
+    import threading
+
+    M = 2048
+    name, K, N = workloads.LLAMA70B_MLP[1]
+    W = torch.from_numpy(workloads.weight(N, K, cfg=4, layer=1)).cuda()
+    qw, sc, qz = awq.awq_pack(W, g, zp)
+    del W
+    X = torch.from_numpy(workloads.activations(M, K, cfg=4, layer=1)).cuda()
+    Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    out = {"shape": {"M": M, "K": K, "N": N}, "idle": _smi_sample()}
+    for label, xin in (("synthetic_x", X), ("zero_x", torch.zeros_like(X))):
+        stop = []
+
+        def spin():
+            while not stop:
+                for _ in range(10):
+                    awq.awq_gemm(xin, qw, sc, qz, N, K, g, zp, y=Y)
+                torch.cuda.synchronize()
+
+        th = threading.Thread(target=spin)
+        th.start()
+        time.sleep(seconds)
+        sample = _smi_sample()
+        stop.append(True)
+        th.join()
+        tm = Timer(torch)
+        tm.start()
+        for _ in range(20):
+            awq.awq_gemm(xin, qw, sc, qz, N, K, g, zp, y=Y)
+        ms = tm.stop_ms() / 20
+        out[label] = dict(sample, us=round(ms * 1e3, 1), TFLOPS=round(2 * M * N * K / (ms * 1e-3) / 1e12, 1))
+    return out
+
+
 def cpu_baseline(layers, g, zp, min_seconds=10.0, max_passes=40):
     """The CPU oracle as it stands (unpack + fp64 decode + fp64 product) on the
     seven linears of one block, M = 1."""
@@ -479,12 +542,13 @@ def main():
         return 0
 
     g, zp = 128, True
-    if args.leg_only in ("fused", "batched", "prefill", "scale", "clip"):
+    if args.leg_only in ("fused", "batched", "prefill", "scale", "clip", "power"):
         fn = {"fused": lambda: leg_fused_decode(torch, awq, workloads, g, zp, blocks=args.blocks),
               "batched": lambda: leg_batched_decode(torch, awq, workloads, g, zp),
               "prefill": lambda: leg_prefill(torch, awq, workloads, g, zp),
               "scale": lambda: leg_scale_search(torch, awq, workloads, g, zp),
-              "clip": lambda: leg_clip_search(torch, awq, workloads, g, zp)}[args.leg_only]
+              "clip": lambda: leg_clip_search(torch, awq, workloads, g, zp),
+              "power": lambda: leg_power(torch, awq, workloads, g, zp)}[args.leg_only]
         print(json.dumps({"leg": args.leg_only, "result": fn()}), flush=True)
         return 0
     log(f"building {args.blocks} decode blocks")
