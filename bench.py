@@ -244,7 +244,8 @@ def leg_fused_decode(torch, awq, workloads, g=128, zp=True, blocks=32, replays=2
 
 
 def leg_batched_decode(torch, awq, workloads, g=128, zp=True, blocks=16, iters=20):
-    """M = 4 / 16 / 64 tokens through the 7 linears of `blocks` distinct blocks."""
+    """M = 4 / 16 / 64 tokens (and 1 and 256 for context) through the 7 linears
+    of `blocks` distinct blocks."""
     out = {}
     base = []
     for li, (name, K, N) in enumerate(workloads.LLAMA7B_BLOCK):
@@ -253,7 +254,7 @@ def leg_batched_decode(torch, awq, workloads, g=128, zp=True, blocks=16, iters=2
         base.append((K, N, qw, sc, qz))
     torch.cuda.synchronize()
     reps = [[(K, N, qw.clone(), sc.clone(), qz.clone()) for (K, N, qw, sc, qz) in base] for _ in range(blocks)]
-    for M in (1, 4, 16, 64):
+    for M in (1, 4, 16, 64, 256):
         xs = [torch.from_numpy(workloads.activations(M, K, cfg=3, layer=li)).cuda()
               for li, (_, K, _) in enumerate(workloads.LLAMA7B_BLOCK)]
         ys = [torch.empty((M, N), dtype=torch.float16, device="cuda") for (_, _, N) in workloads.LLAMA7B_BLOCK]

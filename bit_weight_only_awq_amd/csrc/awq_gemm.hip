@@ -363,14 +363,19 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
                                                              const uint16_t* __restrict__ scales,
                                                              const uint32_t* __restrict__ qzeros,
                                                              _Float16* __restrict__ Y, int M, int N, int K, int gshift,
-                                                             int tiles_m, int group_m, int ldy) {
+                                                             int tiles_m, int group_m, int ldy, int splits,
+                                                             int steps_per_split, float* __restrict__ part) {
   constexpr int WN = 32 * NB;  // wave tile width (N)
   constexpr int TBN = 4 * WN;  // workgroup tile width
   __shared__ __attribute__((aligned(1024))) char lx0[TILE_BYTES], lx1[TILE_BYTES];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
-  const int tiles_n = gridDim.x / tiles_m;
+  // with K split over `splits` workgroups per tile: the workgroups of one
+  // slice are consecutive, so an XCD works on tiles of the same K slice
+  const int id = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  const int tiles = gridDim.x / splits;
+  const int split = id / tiles, tile = id - split * tiles;
+  const int tiles_n = tiles / tiles_m;
   const int per_group = group_m * tiles_n, grp0 = tile / per_group, first_m = grp0 * group_m;
   const int gm = min(tiles_m - first_m, group_m), r_in = tile - grp0 * per_group;
   const int tm = first_m + r_in % gm, tn = r_in / gm;
@@ -378,6 +383,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
   const int rows_m = min(BM, M - m0), rows_n = min(TBN, N - n0);
   const int wm = (wave & 1) * 128, wn = (wave >> 1) * WN;
   const int nsteps = (K + BK - 1) / BK;
+  const int s0 = split * steps_per_split, s1 = min(nsteps, s0 + steps_per_split);  // this workgroup's K steps
   const int G = K >> gshift;
   const DecodeConsts kc;
 
@@ -481,12 +487,12 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
   };
 
   WRegs ra, rb;
-  load_x(0, 0);
-  fetch_w(ra, 0);
-  fetch_w(rb, 1);
+  load_x(s0, 0);
+  fetch_w(ra, s0);
+  fetch_w(rb, s0 + 1);
   __syncthreads();
-  int step = 0;
-  for (; step + 1 < nsteps; step += 2) {
+  int step = s0;
+  for (; step + 1 < s1; step += 2) {
     load_x(step + 1, 1);
     __builtin_amdgcn_sched_barrier(0);
     compute(0, ra);
@@ -498,22 +504,94 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
     fetch_w(rb, step + 3);
     __syncthreads();
   }
-  if (step < nsteps) compute(0, ra);
+  if (step < s1) compute(0, ra);
 
-  const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y + (size_t)m0 * ldy, (uint32_t)rows_m * ldy * 2);
+  // 32x32 accumulator layout: lane l holds column l % 32 and, in register r,
+  // row 8 (r / 4) + 4 (l / 32) + r % 4.  Rows past M fall outside the buffer
+  // and are dropped; columns past N are skipped.  With K split, the fp32
+  // partial tile goes to part[split][M][N] (rows of the tile at stride N).
+  if (splits == 1) {
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y + (size_t)m0 * ldy, (uint32_t)rows_m * ldy * 2);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int col = wn + 32 * b + fi;
-      if (col >= rows_n) continue;
+      for (int b = 0; b < NB; ++b) {
+        const int col = wn + 32 * b + fi;
+        if (col >= rows_n) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm + 32 * a + 8 * (r >> 2) + 4 * fh + (r & 3);
-        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)acc[a][b][r]), ry,
-                                              (uint32_t)(row * ldy + n0 + col) * 2, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm + 32 * a + 8 * (r >> 2) + 4 * fh + (r & 3);
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)acc[a][b][r]), ry,
+                                                (uint32_t)(row * ldy + n0 + col) * 2, 0, 0);
+        }
       }
+  } else {
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(part + ((size_t)split * M + m0) * N, (uint32_t)rows_m * N * 4);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int col = wn + 32 * b + fi;
+        if (col >= rows_n) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm + 32 * a + 8 * (r >> 2) + 4 * fh + (r & 3);
+          // through a named float: a bit cast applied to the vector element
+          // itself was compiled into stores of one register for every r
+          const float v = acc[a][b][r];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rp,
+                                                (uint32_t)(row * N + n0 + col) * 4, 0, 0);
+        }
+      }
+  }
+}
+
+// Y[m][n] = fp16(sum over the K slices s = 0, 1, ... of part[s][m][n]), four
+// outputs per thread, the slices added in order.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float4_t* __restrict__ part, int splits,
+                                                            size_t quads, _Float16* __restrict__ Y) {
+  typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < quads; i += (size_t)gridDim.x * 256) {
+    float4_t v = part[i];
+    for (int s = 1; s < splits; ++s) v += part[(size_t)s * quads + i];
+    half4_t h;
+    h[0] = (_Float16)v[0];
+    h[1] = (_Float16)v[1];
+    h[2] = (_Float16)v[2];
+    h[3] = (_Float16)v[3];
+    reinterpret_cast<half4_t*>(Y)[i] = h;
+  }
+}
+
+// K split of the matrix-core kernel, chosen from a simple time model: one
+// 256 x 256 x 64 tile step takes about 1.2 us, the fp32 partials cost a write
+// and a read at about 5 TB/s, and the reduction is one more launch (~2 us).
+// Splitting pays when there are fewer tiles than compute units (M from 65 to
+// a few hundred tokens).
+struct LargePlan {
+  int splits, steps_per_split;
+};
+
+LargePlan plan_large(int M, int N, int K) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int steps = (K + BK - 1) / BK;
+  constexpr int kUnits = 256;
+  LargePlan best{1, steps};
+  // partial tiles are addressed with 32-bit offsets: 256 rows x N fp32 < 2^31
+  if ((size_t)BM * N * 4 >= ((size_t)1 << 31)) return best;
+  double best_t = (double)((tiles + kUnits - 1) / kUnits) * steps * 1.2;
+  for (int s = 2; s <= 16 && steps / s >= 2; ++s) {
+    const int spp = (steps + s - 1) / s;
+    const int sp = (steps + spp - 1) / spp;
+    const double t = (double)((tiles * sp + kUnits - 1) / kUnits) * spp * 1.2 +
+                     (double)sp * M * N * 8 / 5e6 + 2.0;
+    if (t < best_t) {
+      best_t = t;
+      best = {sp, spp};
     }
+  }
+  return best;
 }
 
 int compute_units() {
@@ -528,7 +606,8 @@ int compute_units() {
 
 template <bool ZP, int NB>
 void launch_large_part(const _Float16* X, const uint32_t* qw, const uint16_t* sc, const uint32_t* qz, _Float16* Y, int M,
-                       int N, int K, int gs, int n_base, int ldy, hipStream_t stream) {
+                       int N, int K, int gs, int n_base, int ldy, hipStream_t stream, LargePlan plan = {1, 0},
+                       float* part = nullptr) {
   constexpr int TBN = 128 * NB;
   const int G = K >> gs;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + TBN - 1) / TBN;
@@ -540,12 +619,14 @@ void launch_large_part(const _Float16* X, const uint32_t* qw, const uint16_t* sc
   const uint32_t* qwp = qw + (size_t)n_base * (K >> 3);
   const uint16_t* scp = sc + scale_index(n_base, 0, G);
   const uint32_t* qzp = ZP ? qz + zero_word_index(n_base, 0, G) : qz;
+  const int spp = plan.splits > 1 ? plan.steps_per_split : (K + BK - 1) / BK;
+  const dim3 grid(tiles_m * tiles_n * plan.splits);
   if (K % BK == 0)
-    hipLaunchKernelGGL((gemm_large_kernel<ZP, false, NB>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, X, qwp, scp,
-                       qzp, Y + n_base, M, N, K, gs, tiles_m, group_m, ldy);
+    hipLaunchKernelGGL((gemm_large_kernel<ZP, false, NB>), grid, dim3(512), 0, stream, X, qwp, scp, qzp, Y + n_base, M,
+                       N, K, gs, tiles_m, group_m, ldy, plan.splits, spp, part);
   else
-    hipLaunchKernelGGL((gemm_large_kernel<ZP, true, NB>), dim3(tiles_m * tiles_n), dim3(512), 0, stream, X, qwp, scp,
-                       qzp, Y + n_base, M, N, K, gs, tiles_m, group_m, ldy);
+    hipLaunchKernelGGL((gemm_large_kernel<ZP, true, NB>), grid, dim3(512), 0, stream, X, qwp, scp, qzp, Y + n_base, M,
+                       N, K, gs, tiles_m, group_m, ldy, plan.splits, spp, part);
 }
 
 // 256x256 tiles; when the last wave of tiles over the compute units would run
@@ -553,7 +634,19 @@ void launch_large_part(const _Float16* X, const uint32_t* qw, const uint16_t* sc
 // 256x128 tiles in a second launch, so the tail takes half a tile time.
 template <bool ZP>
 hipError_t launch_large(const _Float16* X, const uint32_t* qw, const uint16_t* sc, const uint32_t* qz, _Float16* Y,
-                        int M, int N, int K, int gs, hipStream_t stream) {
+                        int M, int N, int K, int gs, void* workspace, hipStream_t stream) {
+  const LargePlan plan = plan_large(M, N, K);
+  if (plan.splits > 1) {
+    // partials after the counter region of the skinny kernel, which stays zero
+    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
+    launch_large_part<ZP, 2>(X, qw, sc, qz, Y, M, N, K, gs, 0, N, stream, plan, part);
+    const size_t quads = (size_t)M * N / 4;
+    size_t blocks = (quads + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const float4_t*>(part), plan.splits, quads, Y);
+    return hipGetLastError();
+  }
   const int cus = compute_units();
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const int tiles = tiles_m * tiles_n, rem = tiles % cus;
@@ -585,13 +678,16 @@ hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales,
       default: return launch_skinny<4, 4, 4, 1, ZP>(p, x, qweight, sc, qzeros, Y, M, N, K, gs, workspace, stream);
     }
   }
-  return launch_large<ZP>(static_cast<const _Float16*>(x), qweight, sc, qzeros, Y, M, N, K, gs, stream);
-  return hipGetLastError();
+  return launch_large<ZP>(static_cast<const _Float16*>(x), qweight, sc, qzeros, Y, M, N, K, gs, workspace, stream);
 }
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int M, int N, int K) { return M <= 64 ? skinny_workspace_bytes(plan_skinny(M, N, K)) : 0; }
+size_t gemm_workspace_bytes(int M, int N, int K) {
+  if (M <= 64) return skinny_workspace_bytes(plan_skinny(M, N, K));
+  const LargePlan p = plan_large(M, N, K);
+  return p.splits > 1 ? kCounterBytes + (size_t)p.splits * M * N * 4 : 0;
+}
 
 hipError_t launch_gemm(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* y,
                        int M, int N, int K, int group_size, bool zero_point, void* workspace, hipStream_t stream) {

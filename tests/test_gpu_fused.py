@@ -1,6 +1,7 @@
 """Fused projections: several weights that read the same input packed as one
-weight (q/k/v, gate/up) give bit-identical packed data and outputs to the
-separate layers, and match the oracle."""
+weight (q/k/v, gate/up) give bit-identical packed data to the separate layers,
+outputs bit-identical to theirs for a few tokens (same kernels and plans) and
+within tolerance of the oracle for any number of tokens."""
 from __future__ import annotations
 
 import numpy as np
@@ -32,14 +33,20 @@ def test_fused_pack_and_layers_match_separate(shapes, K, g, zp):
     assert np.array_equal(G.host_f16_bits(fused.scales), np.concatenate([G.host_f16_bits(p.scales) for p in sep]))
     if zp:
         assert np.array_equal(G.host_u32(fused.qzeros), np.concatenate([G.host_u32(p.qzeros) for p in sep]))
+    oq, os_, oz = O.pack(np.concatenate(Ws), g, zp)
+    wdq = O.dequant_packed(oq, os_, oz, sum(shapes), K, g, zp)
     for M in (1, 4, 300):
         X = workloads.activations(M, K, cfg=6, layer=M)
         x = G.dev_f16(X)
         yf = G.host_f16(awq.linear(x, fused))
         ys = np.concatenate([G.host_f16(awq.linear(x, p)) for p in sep], axis=1)
         torch.cuda.synchronize()
-        assert np.array_equal(yf.view(np.uint16), ys.view(np.uint16)), M
         if M <= 4:
-            oq, os_, oz = O.pack(np.concatenate(Ws), g, zp)
-            y_ref, d = O.matmul_ref(X, O.dequant_packed(oq, os_, oz, sum(shapes), K, g, zp))
-            G.assert_within_tolerance(yf, y_ref, d, f"fused M={M}")
+            # same kernels and launch plans per row: bit-identical
+            assert np.array_equal(yf.view(np.uint16), ys.view(np.uint16)), M
+        # larger M may split K differently for the fused and the separate N:
+        # both within tolerance of the exact product
+        rows = np.arange(M) if M <= 4 else np.sort(np.random.default_rng(M).choice(M, 12, replace=False))
+        y_ref, d = O.matmul_ref(X[rows], wdq)
+        G.assert_within_tolerance(yf[rows], y_ref, d, f"fused M={M}")
+        G.assert_within_tolerance(ys[rows], y_ref, d, f"separate M={M}")

@@ -83,7 +83,8 @@ def test_gemm_split_k_workspace_reuse():
     whichever workgroup of a tile finishes last."""
     awq = G.lib()
     g = 128
-    shapes = [(16, 4096, 4096), (64, 4104, 11008), (4, 11008, 4096), (64, 1024, 8192), (3, 4096, 4096)]
+    shapes = [(16, 4096, 4096), (64, 4104, 11008), (4, 11008, 4096), (300, 1024, 8192), (64, 1024, 8192),
+              (3, 4096, 4096)]
     need = max(awq.awq_gemm_workspace_bytes(M, N, K, g) for M, N, K in shapes)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     for M, N, K in shapes:
@@ -122,6 +123,27 @@ def test_gemm_batched_decode_full_size(M, name, K, N):
     W = workloads.weight(N, K, cfg=3, layer=layer)
     X = workloads.activations(M, K, cfg=3, layer=layer)
     check(M, N, K, 128, True, W, X, f"gemm {name} M={M}")
+
+
+@pytest.mark.parametrize("M", [96, 256, 512])
+@pytest.mark.parametrize("name,K,N", [workloads.LLAMA7B_BLOCK[0], workloads.LLAMA7B_BLOCK[4],
+                                      workloads.LLAMA7B_BLOCK[6]])
+def test_gemm_medium_m_full_size(M, name, K, N):
+    """Token counts between the skinny and the full-GPU regimes, where the
+    matrix-core kernel splits K over workgroups (fp32 partials added by a
+    second kernel); the oracle checks a sample of rows."""
+    awq = G.lib()
+    g = 128
+    layer = [n for n, _, _ in workloads.LLAMA7B_BLOCK].index(name)
+    W = workloads.weight(N, K, cfg=3, layer=layer)
+    X = workloads.activations(M, K, cfg=3, layer=layer)
+    packed = O.pack(W, g, True)
+    y = run_gemm(X, packed, N, K, g, True)
+    rows = np.sort(np.random.default_rng(M).choice(M, 16, replace=False))
+    y_ref, d = O.matmul_ref(X[rows], O.dequant_packed(*packed, N, K, g, True))
+    G.assert_within_tolerance(y[rows], y_ref, d, f"gemm {name} M={M}")
+    if M <= 256:
+        assert awq.awq_gemm_workspace_bytes(M, N, K, g) > 0, "expected a K split at this size"
 
 
 @pytest.mark.parametrize("name,K,N", workloads.LLAMA70B_MLP)
