@@ -101,32 +101,44 @@ __host__ __device__ __forceinline__ size_t scale_index(int n, int j, int G) {
 }
 __host__ __device__ __forceinline__ size_t zero_word_index(int n, int j, int G) { return (size_t)(n >> 3) * G + j; }
 
-// Sum R per-lane row partials over the 64 lanes of a wave.  Each halving step
-// exchanges half of the rows a lane still carries with the partner lane
-// (xor 32, 16, ...), so after log2(R) steps lane l carries one row,
-// l / (64 / R), summed over a group of lanes that the remaining xor steps
-// complete.  Returns that row's total; it is valid in every lane of the group.
-template <int R>
-__device__ __forceinline__ float wave_reduce_rows(float (&v)[R], int lane) {
-  int cnt = R;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    if (cnt > 1) {
-      const bool hi = lane & off;
-#pragma unroll
-      for (int i = 0; i < R / 2; ++i) {
-        if (i < cnt / 2) {
-          const float give = hi ? v[i] : v[i + cnt / 2];
-          const float keep = hi ? v[i + cnt / 2] : v[i];
-          v[i] = keep + __shfl_xor(give, off);
-        }
-      }
-      cnt >>= 1;
-    } else {
-      v[0] += __shfl_xor(v[0], off);
-    }
-  }
-  return v[0];
+// Sum four per-lane row partials over the 64 lanes of a wave without LDS.
+// v_permlane32_swap exchanges the upper half-wave of its first operand with
+// the lower half-wave of its second, so adding its two results gives, in
+// lanes 0-31, row a summed over lanes l and l + 32 and, in lanes 32-63, row b
+// summed the same way.  v_permlane16_swap does the same between the odd
+// 16-lane rows of its first operand and the even rows of its second.  After
+// the two exchanges lane group r = lane / 16 carries partials of row r only,
+// and four DPP row rotations (by 8, 4, 2, 1 lanes) complete the sum within
+// the group.  Returns row lane / 16's total, valid in every lane of the group;
+// each lane's order of additions is fixed, so results are reproducible.
+// (The two results are copied to named scalars before the bit casts: a bit
+// cast applied directly to an element of the returned vector has been compiled
+// as a cast of one and the same element for both.)
+__device__ __forceinline__ float swap_sum32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                                  false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float swap_sum16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                                  false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+template <int CTRL>
+__device__ __forceinline__ float row_rotate(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_reduce_quad_rows(const float (&v)[4]) {
+  const float a = swap_sum32(v[0], v[2]);  // lanes 0-31: row 0, lanes 32-63: row 2
+  const float b = swap_sum32(v[1], v[3]);  // lanes 0-31: row 1, lanes 32-63: row 3
+  float s = swap_sum16(a, b);              // lanes 16 r .. 16 r + 15: row r
+  s += row_rotate<0x128>(s);               // row_ror:8
+  s += row_rotate<0x124>(s);               // row_ror:4
+  s += row_rotate<0x122>(s);               // row_ror:2
+  s += row_rotate<0x121>(s);               // row_ror:1
+  return s;
 }
 
 // The hardware dispatches workgroup b of a 1-D grid to XCD (b mod 8).  This

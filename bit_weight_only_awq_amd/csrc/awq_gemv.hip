@@ -16,8 +16,9 @@
 //   * decoding is exact bit arithmetic (q - z as small fp16 integers) followed
 //     by v_dot2_f32_f16 against the fp16 activations; the group scale
 //     multiplies the fp32 chunk sum once, so no decoded weight is rounded;
-//   * row sums are reduced across the wave with a transposing butterfly, then
-//     across waves through LDS in a fixed order: bit-reproducible results.
+//   * row sums are reduced across the wave in registers (two lane-swap
+//     exchanges that leave one row per 16-lane group, then DPP row rotations),
+//     then across waves through LDS in a fixed order: bit-reproducible results.
 #include "awq_device.hpp"
 #include "awq_launch.hpp"
 
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const u32x4* __restrict__
     }
   }
 
-  const float total = wave_reduce_rows<kRows>(acc, lane);
+  const float total = wave_reduce_quad_rows(acc);
   constexpr int kLanesPerRow = 64 / kRows;
   if (NW == 1) {
     if ((lane % kLanesPerRow) == 0) y[n0 + lane / kLanesPerRow] = (_Float16)total;
