@@ -61,6 +61,10 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const u32x4* __restrict__
     u32x4 wv[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) wv[r] = wrow[(size_t)r * row_u4 + c];
+    // every load of the chunk is issued before any decoding: left alone, the
+    // scheduler splits them into rounds around the dot products in the
+    // variant without zero points (two to three load latencies per chunk)
+    __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
