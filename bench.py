@@ -15,13 +15,14 @@ legs   = awq_pack, fused-projection decode (qkv and gate_up as one awq_gemv
          each), batched-decode awq_gemm (M = 4/16/64; GEMV vs GEMM at M = 1),
          prefill awq_gemm (M = 2048, 70B-shaped MLP), activation-aware scale
          search (L(s) for 20 candidates over 512 calibration tokens), weight
-         clipping search (20 ratios, same tokens).
+         clipping search (20 ratios, same tokens), group-size / symmetry sweep
+         (g = 32 / 128 / 256 with and without zero points, M = 1 and 8).
 cpu_baseline = the CPU oracle (decode + fp64 product) on one block, timed on
          the host; a reported reference, not a target.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--blocks 32]
                        [--legs all|none|<comma list>] [--no-cpu-baseline]
-       python bench.py --leg-only pack|fused|batched|prefill|scale|clip|power   (one leg, for profiling)
+       python bench.py --leg-only pack|fused|batched|prefill|scale|clip|sweep|power   (one leg, for profiling)
        python bench.py --copy-calibration | --summarize DB... [--kernel-filter NAME]
 """
 from __future__ import annotations
@@ -61,7 +62,7 @@ def parse():
     ap.add_argument("--summarize", nargs="+", metavar="DB",
                     help="print a per-kernel summary of rocprofv3 result databases and exit")
     ap.add_argument("--kernel-filter", default=None, help="with --summarize: only kernels whose name contains this")
-    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "prefill", "scale", "clip", "power"],
+    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "prefill", "scale", "clip", "sweep", "power"],
                     help="run just this leg (no headline, no CPU baseline) and print its JSON; for profiling")
     return ap.parse_args()
 
@@ -280,6 +281,43 @@ def leg_batched_decode(torch, awq, workloads, g=128, zp=True, blocks=16, iters=2
             out["M1_gemv_vs_gemm"] = {"gemv_us_per_block": round(ms_v * 1e3 / blocks, 2),
                                       "gemm_us_per_block": round(ms * 1e3 / blocks, 2),
                                       "gemv_speedup": round(ms / ms_v, 3)}
+    return out
+
+
+def leg_sweep(torch, awq, workloads, blocks=16, iters=20):
+    """Group-size and symmetry sweep over one Llama-7B block's 7 linears (the
+    weights with per-row mean offsets, so that the zero points matter): for
+    g = 32 / 128 / 256, with and without zero points, one token (awq_gemv) and
+    8 tokens (awq_gemm).  Each step runs `blocks` distinct copies of the packed
+    block, so no launch is served from the Infinity Cache."""
+    Ws = [torch.from_numpy(workloads.weight(N, K, cfg=5, layer=li, row_offset=True)).cuda()
+          for li, (_, K, N) in enumerate(workloads.LLAMA7B_BLOCK)]
+    out = {}
+    for g in (32, 128, 256):
+        for zp in (True, False):
+            base = [(K, N) + tuple(awq.awq_pack(W, g, zp)) for W, (_, K, N) in zip(Ws, workloads.LLAMA7B_BLOCK)]
+            torch.cuda.synchronize()
+            reps = [[(K, N, qw.clone(), sc.clone(), None if qz is None else qz.clone()) for (K, N, qw, sc, qz) in base]
+                    for _ in range(blocks)]
+            for M in (1, 8):
+                xs = [torch.from_numpy(workloads.activations(M, K, cfg=5, layer=li)).cuda()
+                      for li, (_, K, _) in enumerate(workloads.LLAMA7B_BLOCK)]
+                ys = [torch.empty((M, N), dtype=torch.float16, device="cuda") for (_, _, N) in workloads.LLAMA7B_BLOCK]
+                call = awq.awq_gemv if M == 1 else awq.awq_gemm
+
+                def step():
+                    for rep in reps:
+                        for i, (K, N, qw, sc, qz) in enumerate(rep):
+                            call(xs[i], qw, sc, qz, N, K, g, zp, y=ys[i])
+
+                ms, _ = time_graph(torch, step, iters)
+                nbytes = blocks * sum(algorithmic_bytes(M, N, K, g, zp) for (_, K, N) in workloads.LLAMA7B_BLOCK)
+                out[f"g{g}_{'zp' if zp else 'sym'}_M{M}"] = {
+                    "kernel": "awq_gemv" if M == 1 else "awq_gemm", "us_per_block": round(ms * 1e3 / blocks, 2),
+                    "MB_per_block": round(nbytes / blocks / 1e6, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                    "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+            del reps, base
+            torch.cuda.empty_cache()
     return out
 
 
@@ -543,12 +581,13 @@ def main():
         return 0
 
     g, zp = 128, True
-    if args.leg_only in ("fused", "batched", "prefill", "scale", "clip", "power"):
+    if args.leg_only in ("fused", "batched", "prefill", "scale", "clip", "sweep", "power"):
         fn = {"fused": lambda: leg_fused_decode(torch, awq, workloads, g, zp, blocks=args.blocks),
               "batched": lambda: leg_batched_decode(torch, awq, workloads, g, zp),
               "prefill": lambda: leg_prefill(torch, awq, workloads, g, zp),
               "scale": lambda: leg_scale_search(torch, awq, workloads, g, zp),
               "clip": lambda: leg_clip_search(torch, awq, workloads, g, zp),
+              "sweep": lambda: leg_sweep(torch, awq, workloads),
               "power": lambda: leg_power(torch, awq, workloads, g, zp)}[args.leg_only]
         print(json.dumps({"leg": args.leg_only, "result": fn()}), flush=True)
         return 0
@@ -626,7 +665,7 @@ def main():
     }
 
     legs = set(args.legs.split(",")) if args.legs not in ("all", "none") else (
-        {"pack", "fused", "batched", "prefill", "scale", "clip"} if args.legs == "all" else set())
+        {"pack", "fused", "batched", "prefill", "scale", "clip", "sweep"} if args.legs == "all" else set())
     out_legs = {}
     if args.leg_only == "pack":
         print(json.dumps({"leg": "pack", "result": leg_pack(torch, awq, layers, g, zp)}), flush=True)
@@ -651,6 +690,9 @@ def main():
     if "clip" in legs:
         log("leg: clip search")
         out_legs["clip_search"] = leg_clip_search(torch, awq, workloads, g, zp)
+    if "sweep" in legs:
+        log("leg: group-size / symmetry sweep")
+        out_legs["sweep_7b_block"] = leg_sweep(torch, awq, workloads)
     if out_legs:
         result["legs"] = out_legs
     if not args.no_cpu_baseline:
