@@ -16,13 +16,15 @@ legs   = awq_pack, fused-projection decode (qkv and gate_up as one awq_gemv
          prefill awq_gemm (M = 2048, 70B-shaped MLP), activation-aware scale
          search (L(s) for 20 candidates over 512 calibration tokens), weight
          clipping search (20 ratios, same tokens), group-size / symmetry sweep
-         (g = 32 / 128 / 256 with and without zero points, M = 1 and 8).
+         (g = 32 / 128 / 256 with and without zero points, M = 1 and 8),
+         single-token GEMV on the 70B MLP shapes (layers large enough that
+         the launch floor no longer dominates).
 cpu_baseline = the CPU oracle (decode + fp64 product) on one block, timed on
          the host; a reported reference, not a target.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--blocks 32]
                        [--legs all|none|<comma list>] [--no-cpu-baseline]
-       python bench.py --leg-only pack|fused|batched|prefill|scale|clip|sweep|power   (one leg, for profiling)
+       python bench.py --leg-only pack|fused|batched|prefill|scale|clip|sweep|gemv70b|power   (one leg, for profiling)
        python bench.py --copy-calibration | --summarize DB... [--kernel-filter NAME]
 """
 from __future__ import annotations
@@ -62,7 +64,7 @@ def parse():
     ap.add_argument("--summarize", nargs="+", metavar="DB",
                     help="print a per-kernel summary of rocprofv3 result databases and exit")
     ap.add_argument("--kernel-filter", default=None, help="with --summarize: only kernels whose name contains this")
-    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "prefill", "scale", "clip", "sweep", "power"],
+    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "prefill", "scale", "clip", "sweep", "gemv70b", "power"],
                     help="run just this leg (no headline, no CPU baseline) and print its JSON; for profiling")
     return ap.parse_args()
 
@@ -318,6 +320,35 @@ def leg_sweep(torch, awq, workloads, blocks=16, iters=20):
                     "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
             del reps, base
             torch.cuda.empty_cache()
+    return out
+
+
+def leg_gemv_70b(torch, awq, workloads, g=128, zp=True, replays=5):
+    """Single-token awq_gemv on the two 70B-shaped MLP linears (122 MB each):
+    at this size the launch floor that caps the 7B layers is a small part of a
+    launch.  Enough distinct copies of each packed layer to total >= 1 GiB per
+    graph replay, so no launch is served from the Infinity Cache."""
+    out = {}
+    for li, (name, K, N) in enumerate(workloads.LLAMA70B_MLP):
+        W = torch.from_numpy(workloads.weight(N, K, cfg=4, layer=li)).cuda()
+        base = awq.awq_pack(W, g, zp)
+        del W
+        nbytes = algorithmic_bytes(1, N, K, g, zp)
+        copies = max(8, -(-(1 << 30) // nbytes))
+        reps = [tuple(t.clone() for t in base) for _ in range(copies)]
+        x = torch.from_numpy(workloads.activations(1, K, cfg=4, layer=li)).cuda()
+        y = torch.empty((1, N), dtype=torch.float16, device="cuda")
+
+        def step():
+            for qw, sc, qz in reps:
+                awq.awq_gemv(x, qw, sc, qz, N, K, g, zp, y=y)
+
+        ms, _ = time_graph(torch, step, replays)
+        us = ms * 1e3 / copies
+        out[name] = {"K": K, "N": N, "MB": round(nbytes / 1e6, 1), "us": round(us, 2),
+                     "GB/s": round(nbytes / us / 1e3, 1), "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 3)}
+        del reps, base
+        torch.cuda.empty_cache()
     return out
 
 
@@ -581,13 +612,14 @@ def main():
         return 0
 
     g, zp = 128, True
-    if args.leg_only in ("fused", "batched", "prefill", "scale", "clip", "sweep", "power"):
+    if args.leg_only in ("fused", "batched", "prefill", "scale", "clip", "sweep", "gemv70b", "power"):
         fn = {"fused": lambda: leg_fused_decode(torch, awq, workloads, g, zp, blocks=args.blocks),
               "batched": lambda: leg_batched_decode(torch, awq, workloads, g, zp),
               "prefill": lambda: leg_prefill(torch, awq, workloads, g, zp),
               "scale": lambda: leg_scale_search(torch, awq, workloads, g, zp),
               "clip": lambda: leg_clip_search(torch, awq, workloads, g, zp),
               "sweep": lambda: leg_sweep(torch, awq, workloads),
+              "gemv70b": lambda: leg_gemv_70b(torch, awq, workloads, g, zp),
               "power": lambda: leg_power(torch, awq, workloads, g, zp)}[args.leg_only]
         print(json.dumps({"leg": args.leg_only, "result": fn()}), flush=True)
         return 0
@@ -665,7 +697,7 @@ def main():
     }
 
     legs = set(args.legs.split(",")) if args.legs not in ("all", "none") else (
-        {"pack", "fused", "batched", "prefill", "scale", "clip", "sweep"} if args.legs == "all" else set())
+        {"pack", "fused", "batched", "prefill", "scale", "clip", "sweep", "gemv70b"} if args.legs == "all" else set())
     out_legs = {}
     if args.leg_only == "pack":
         print(json.dumps({"leg": "pack", "result": leg_pack(torch, awq, layers, g, zp)}), flush=True)
@@ -693,6 +725,9 @@ def main():
     if "sweep" in legs:
         log("leg: group-size / symmetry sweep")
         out_legs["sweep_7b_block"] = leg_sweep(torch, awq, workloads)
+    if "gemv70b" in legs:
+        log("leg: GEMV on the 70B MLP shapes")
+        out_legs["gemv_70b_mlp"] = leg_gemv_70b(torch, awq, workloads, g, zp)
     if out_legs:
         result["legs"] = out_legs
     if not args.no_cpu_baseline:

@@ -67,6 +67,31 @@ def test_gemv_llama7b_block_full_size(name, K, N):
     check_layer(N, K, 128, True, W, X, f"gemv {name}")
 
 
+@pytest.mark.parametrize("name,K,N", workloads.LLAMA70B_MLP)
+def test_gemv_70b_sampled(name, K, N):
+    """Single-token GEMV on the 70B MLP shapes (K = 28672 loops over chunks:
+    8 waves of 64 lanes cover 512 of its 896 chunks per pass); the oracle
+    checks sampled row octets of the GPU packing and of the output."""
+    awq = G.lib()
+    g = 128
+    layer = 0 if K == 8192 else 1
+    W = workloads.weight(N, K, cfg=4, layer=layer)
+    X = workloads.activations(1, K, cfg=4, layer=layer)
+    w = G.dev_f16(W)
+    qw, sc, qz = awq.awq_pack(w, g, True)
+    del w
+    y = G.host_f16(awq.awq_gemv(G.dev_f16(X), qw, sc, qz, N, K, g, True))
+    rng = np.random.default_rng(5)
+    octets = np.sort(rng.choice(N // 8, size=16, replace=False))
+    rows = (octets[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+    oq, os_, oz = O.pack(W[rows], g, True)
+    assert np.array_equal(G.host_u32(qw)[rows], oq)
+    assert np.array_equal(G.host_f16_bits(sc)[octets], os_)
+    assert np.array_equal(G.host_u32(qz)[octets], oz)
+    y_ref, d = O.matmul_ref(X, O.dequant_packed(oq, os_, oz, len(rows), K, g, True))
+    G.assert_within_tolerance(y[:, rows], y_ref, d, f"gemv {name}")
+
+
 def test_gemv_adversarial_weights():
     W = workloads.adversarial_weight(64, 1024, 32, seed=5)
     # keep the outputs inside fp16 range: the adversarial groups hold |w| up to 6e4
