@@ -18,13 +18,15 @@ legs   = awq_pack, fused-projection decode (qkv and gate_up as one awq_gemv
          clipping search (20 ratios, same tokens), group-size / symmetry sweep
          (g = 32 / 128 / 256 with and without zero points, M = 1 and 8),
          single-token GEMV on the 70B MLP shapes (layers large enough that
-         the launch floor no longer dominates).
+         the launch floor no longer dominates); for context, torch's dense
+         fp16 products on the unquantized weights (decode M = 1/4/16/64 and
+         the prefill shapes) with the W4A16 speedup over them.
 cpu_baseline = the CPU oracle (decode + fp64 product) on one block, timed on
          the host; a reported reference, not a target.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--blocks 32]
                        [--legs all|none|<comma list>] [--no-cpu-baseline]
-       python bench.py --leg-only pack|fused|batched|prefill|scale|clip|sweep|gemv70b|power   (one leg, for profiling)
+       python bench.py --leg-only pack|fused|batched|dense|prefill|scale|clip|sweep|gemv70b|power   (one leg, for profiling)
        python bench.py --copy-calibration | --summarize DB... [--kernel-filter NAME]
 """
 from __future__ import annotations
@@ -64,7 +66,7 @@ def parse():
     ap.add_argument("--summarize", nargs="+", metavar="DB",
                     help="print a per-kernel summary of rocprofv3 result databases and exit")
     ap.add_argument("--kernel-filter", default=None, help="with --summarize: only kernels whose name contains this")
-    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "prefill", "scale", "clip", "sweep", "gemv70b", "power"],
+    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "dense", "prefill", "scale", "clip", "sweep", "gemv70b", "power"],
                     help="run just this leg (no headline, no CPU baseline) and print its JSON; for profiling")
     return ap.parse_args()
 
@@ -286,6 +288,46 @@ def leg_batched_decode(torch, awq, workloads, g=128, zp=True, blocks=16, iters=2
     return out
 
 
+def leg_dense_decode(torch, workloads, blocks=4, iters=20):
+    """Context for the decode legs: torch's dense fp16 matrix product (the
+    vendor library) on the unquantized weights of `blocks` distinct Llama-7B
+    blocks (405 MB each, so no launch is served from the Infinity Cache), M =
+    1 / 4 / 16 / 64, replayed from a HIP graph whose first replay is checked
+    against the same products run eagerly.  A measured ceiling for the pages'
+    "4-bit against FP16" comparison, not a product path."""
+    out = {}
+    Ws = [[torch.from_numpy(workloads.weight(N, K, cfg=3, layer=li)).cuda()
+           for li, (_, K, N) in enumerate(workloads.LLAMA7B_BLOCK)]]
+    for _ in range(blocks - 1):
+        Ws.append([w.clone() for w in Ws[0]])
+    for M in (1, 4, 16, 64):
+        xs = [torch.from_numpy(workloads.activations(M, K, cfg=3, layer=li)).cuda()
+              for li, (_, K, _) in enumerate(workloads.LLAMA7B_BLOCK)]
+        ys = [torch.empty((M, N), dtype=torch.float16, device="cuda") for (_, _, N) in workloads.LLAMA7B_BLOCK]
+
+        def step():
+            for blk in Ws:
+                for i, w in enumerate(blk):
+                    torch.mm(xs[i], w.t(), out=ys[i])
+
+        step()
+        torch.cuda.synchronize()
+        eager = [y.clone() for y in ys]
+        for y in ys:
+            y.zero_()
+        ms, graph = time_graph(torch, step, iters)
+        torch.cuda.synchronize()
+        same = all(torch.equal(a, b) for a, b in zip(eager, ys))
+        nbytes = blocks * sum(2 * K * N + 2 * M * K + 2 * M * N for (_, K, N) in workloads.LLAMA7B_BLOCK)
+        out[f"M{M}"] = {"us_per_block": round(ms * 1e3 / blocks, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+                        "graph_matches_eager": same}
+        del graph
+    del Ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def leg_sweep(torch, awq, workloads, blocks=16, iters=20):
     """Group-size and symmetry sweep over one Llama-7B block's 7 linears (the
     weights with per-row mean offsets, so that the zero points matter): for
@@ -352,18 +394,21 @@ def leg_gemv_70b(torch, awq, workloads, g=128, zp=True, replays=5):
     return out
 
 
-def leg_prefill(torch, awq, workloads, g=128, zp=True, iters=30, warm=20):
+def leg_prefill(torch, awq, workloads, g=128, zp=True, iters=30, warm=20, dense=True):
     """M = 2048 prefill through the two 70B-shaped MLP linears (matrix-core bound).
 
     The kernel runs at the chip's power limit, where the clock takes several
     milliseconds of load to settle: ``warm`` untimed launches (about 20 ms)
-    come before the ``iters`` timed ones."""
+    come before the ``iters`` timed ones.  With ``dense``, torch's fp16 matrix
+    product on the unquantized weights is timed the same way, as context (a
+    measured ceiling from the vendor library, not a product path)."""
     out = {}
     M = 2048
     for li, (name, K, N) in enumerate(workloads.LLAMA70B_MLP):
         W = torch.from_numpy(workloads.weight(N, K, cfg=4, layer=li)).cuda()
         qw, sc, qz = awq.awq_pack(W, g, zp)
-        del W
+        if not dense:
+            del W
         X = torch.from_numpy(workloads.activations(M, K, cfg=4, layer=li)).cuda()
         Y = torch.empty((M, N), dtype=torch.float16, device="cuda")
         for _ in range(warm):
@@ -377,6 +422,20 @@ def leg_prefill(torch, awq, workloads, g=128, zp=True, iters=30, warm=20):
         tf = 2 * M * N * K / (ms * 1e-3) / 1e12
         out[name] = {"M": M, "K": K, "N": N, "us": round(ms * 1e3, 1), "TFLOPS": round(tf, 1),
                      "frac_mfma_fp16": round(tf / FP16_MFMA_PEAK_TFLOPS, 3)}
+        if dense:
+            # context: the vendor library's dense fp16 product on the same
+            # (unquantized) weights and activations, same warm-up
+            for _ in range(warm):
+                torch.mm(X, W.t(), out=Y)
+            torch.cuda.synchronize()
+            tm.start()
+            for _ in range(iters):
+                torch.mm(X, W.t(), out=Y)
+            dms = tm.stop_ms() / iters
+            dtf = 2 * M * N * K / (dms * 1e-3) / 1e12
+            out[name]["dense_fp16_torch_mm"] = {"us": round(dms * 1e3, 1), "TFLOPS": round(dtf, 1),
+                                                "awq_speedup": round(dms / ms, 3)}
+            del W
         del qw, sc, qz, X, Y
         torch.cuda.empty_cache()
     tot_f = sum(2 * M * N * K for (_, K, N) in workloads.LLAMA70B_MLP)
@@ -612,9 +671,10 @@ def main():
         return 0
 
     g, zp = 128, True
-    if args.leg_only in ("fused", "batched", "prefill", "scale", "clip", "sweep", "gemv70b", "power"):
+    if args.leg_only in ("fused", "batched", "dense", "prefill", "scale", "clip", "sweep", "gemv70b", "power"):
         fn = {"fused": lambda: leg_fused_decode(torch, awq, workloads, g, zp, blocks=args.blocks),
               "batched": lambda: leg_batched_decode(torch, awq, workloads, g, zp),
+              "dense": lambda: leg_dense_decode(torch, workloads),
               "prefill": lambda: leg_prefill(torch, awq, workloads, g, zp),
               "scale": lambda: leg_scale_search(torch, awq, workloads, g, zp),
               "clip": lambda: leg_clip_search(torch, awq, workloads, g, zp),
@@ -697,7 +757,7 @@ def main():
     }
 
     legs = set(args.legs.split(",")) if args.legs not in ("all", "none") else (
-        {"pack", "fused", "batched", "prefill", "scale", "clip", "sweep", "gemv70b"} if args.legs == "all" else set())
+        {"pack", "fused", "batched", "dense", "prefill", "scale", "clip", "sweep", "gemv70b"} if args.legs == "all" else set())
     out_legs = {}
     if args.leg_only == "pack":
         print(json.dumps({"leg": "pack", "result": leg_pack(torch, awq, layers, g, zp)}), flush=True)
@@ -713,6 +773,15 @@ def main():
     if "batched" in legs:
         log("leg: batched decode")
         out_legs["batched_decode_gemm"] = leg_batched_decode(torch, awq, workloads, g, zp)
+    if "dense" in legs:
+        log("leg: dense fp16 decode (torch, context)")
+        dense = leg_dense_decode(torch, workloads)
+        bd = out_legs.get("batched_decode_gemm")
+        if bd:
+            for M in (1, 4, 16, 64):
+                ours = bd["M1_gemv_vs_gemm"]["gemv_us_per_block"] if M == 1 else bd[f"M{M}"]["us_per_block"]
+                dense[f"M{M}"]["awq_speedup"] = round(dense[f"M{M}"]["us_per_block"] / ours, 3)
+        out_legs["dense_fp16_decode_context"] = dense
     if "prefill" in legs:
         log("leg: prefill")
         out_legs["prefill_gemm_70b"] = leg_prefill(torch, awq, workloads, g, zp)

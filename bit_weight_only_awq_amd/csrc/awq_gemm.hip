@@ -18,13 +18,15 @@
 //     (deterministic, one launch).
 //
 //   * gemm_large_kernel (M > 64): matrix-core bound.  256 x 256 output tile
-//     (or 256 x 128 for the last wave of tiles) per workgroup of 8 waves
-//     (2 x 4, 128 x 64 each, v_mfma_f32_32x32x16_f16), K in steps of 64.  X
-//     tiles go from HBM straight into LDS (buffer-to-LDS loads); packed
-//     weights are fetched two steps ahead into registers and decoded straight
-//     into MFMA B operands (no LDS on the weight path).  LDS tiles use an XOR
-//     swizzle instead of padding; workgroups are mapped so that each XCD (and
-//     its L2) works on a contiguous band of tiles, in groups of 4 tile rows.
+//     (or 256 x 128 for the last wave of tiles) per workgroup of 4 waves, one
+//     per SIMD, each 256 x 64 (v_mfma_f32_32x32x16_f16, accumulators in the
+//     AGPRs), K in steps of 64.  X tiles go from HBM straight into LDS
+//     (buffer-to-LDS loads); packed weights are fetched two steps ahead into
+//     registers and decoded once per workgroup straight into MFMA B operands
+//     (no LDS on the weight path); the K loop is software-pipelined by hand.
+//     LDS tiles use an XOR swizzle instead of padding; workgroups are mapped
+//     so that each XCD (and its L2) works on a contiguous band of tiles, in
+//     groups of 4 tile rows.
 //
 // MFMA operand placement: a lane's 8 fp16 values of A and of B cover the same
 // 8 reduction indices, so any assignment of channels to (lane group, element)
@@ -346,31 +348,44 @@ constexpr int TILE_BYTES = BM * BK * 2;  // one 256 x 64 fp16 tile in LDS (32 Ki
 // of slots is exactly what one buffer-to-LDS load of 64 lanes x 16 bytes writes.
 __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-// 2 x 4 waves of 128 x (32 NB) outputs (two waves per SIMD); tile width
-// 128 NB.  Only X goes through LDS: tiles go from HBM straight into LDS by
-// buffer-to-LDS loads, double-buffered, one step ahead.  The weights go to the
-// matrix cores without LDS: with the channel-to-slot assignment below, the B
-// fragment of a lane for one 16-channel slice is one packed word of one
-// weight row, so lane (n, h) of a wave loads the 32 channels 64 s + 32 h .. +32
-// of its row as one 16-byte word (four slices) two steps ahead and decodes
-// each word right before its MFMAs.  Both M-halves of the workgroup decode
-// the same rows, in exchange for no weight stores, no weight fragment reads
-// and no barrier on the weights.  Every global access goes through a buffer
+// One wave per SIMD: 4 waves of 256 x (32 NB) outputs (tile width 128 NB),
+// every wave multiplying all 256 rows of the X tile, so each packed weight
+// word is loaded and decoded once per workgroup (1.9 VALU instructions per
+// MFMA; with two M-halves decoding the same words it was 3.7, and at the
+// power limit every VALU instruction per MFMA costs about 3% of throughput).
+// The 256 accumulators per lane sit in the AGPRs.
+//
+// Only X goes through LDS: tiles go from HBM straight into LDS by
+// buffer-to-LDS loads, double-buffered.  The weights go to the matrix cores
+// without LDS: with the channel-to-slot assignment below, the B fragment of a
+// lane for one 16-channel slice is one packed word of one weight row, so lane
+// (n, h) of a wave loads the 32 channels 64 s + 32 h .. +32 of its row as one
+// 16-byte word (four slices) two steps ahead and decodes each word one slice
+// before its MFMAs.  Software-pipelined by hand, as a single wave per SIMD
+// has no other wave to hide latency behind: while the 16 MFMAs of one slice
+// run, the wave reads the next slice's A fragments from LDS and decodes its B
+// fragments (scheduling groups interleave one LDS read and four VALU
+// instructions with every two MFMAs); the step's barrier sits before the last
+// slice, whose MFMAs overlap the next step's first reads, its buffer-to-LDS
+// loads and its first decode.  Every global access goes through a buffer
 // resource based at the tile (rows past M or N read as zero), and the K loop
 // has no branches: loads for steps past the end stay inside the buffers (or
 // return zero) and land where no one reads again.
 //   MFMA slice ks of step s, lane half h, element j  <->  channel 64 s + 32 h + 8 ks + j
 // (A and B use the same assignment, so the product is unchanged.)
 template <bool ZP, bool KTAIL, int NB>
-__global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restrict__ X,
-                                                             const uint32_t* __restrict__ qweight,
-                                                             const uint16_t* __restrict__ scales,
-                                                             const uint32_t* __restrict__ qzeros,
-                                                             _Float16* __restrict__ Y, int M, int N, int K, int gshift,
-                                                             int tiles_m, int group_m, int ldy, int splits,
-                                                             int steps_per_split, float* __restrict__ part) {
-  constexpr int WN = 32 * NB;  // wave tile width (N)
-  constexpr int TBN = 4 * WN;  // workgroup tile width
+__global__ __launch_bounds__(256) void gemm_large_kernel(const _Float16* __restrict__ X,
+                                                         const uint32_t* __restrict__ qweight,
+                                                         const uint16_t* __restrict__ scales,
+                                                         const uint32_t* __restrict__ qzeros,
+                                                         _Float16* __restrict__ Y, int M, int N, int K, int gshift,
+                                                         int tiles_m, int group_m, int ldy, int splits,
+                                                         int steps_per_split, float* __restrict__ part) {
+  constexpr int NW = 4, WMT = BM / 32;        // waves; 32-row MFMA tiles per wave
+  constexpr int WN = 32 * NB, TBN = NW * WN;  // wave and workgroup tile widths
+  constexpr int XROWS = BM / NW;              // X tile rows each wave loads, 8 per 1 KiB load
+  // two arrays, so that the compiler's wait for buffer-to-LDS loads in flight
+  // before an LDS read covers only the loads into the array being read
   __shared__ __attribute__((aligned(1024))) char lx0[TILE_BYTES], lx1[TILE_BYTES];
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -385,7 +400,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
   const int tm = first_m + r_in % gm, tn = r_in / gm;
   const int m0 = tm * BM, n0 = tn * TBN;
   const int rows_m = min(BM, M - m0), rows_n = min(TBN, N - n0);
-  const int wm = (wave & 1) * 128, wn = (wave >> 1) * WN;
+  const int wn = wave * WN;
   const int nsteps = (K + BK - 1) / BK;
   const int s0 = split * steps_per_split, s1 = min(nsteps, s0 + steps_per_split);  // this workgroup's K steps
   const int G = K >> gshift;
@@ -397,20 +412,20 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
   const __amdgpu_buffer_rsrc_t rz = make_rsrc(ZP ? qzeros + zero_word_index(n0, 0, G) : qzeros,
                                               ZP ? (uint32_t)(rows_n >> 3) * G * 4 : 0u);
 
-  // X: as in gemm_large_kernel (wave w fills rows 32 w .. 32 w + 31)
-  int xchunk[4];
-  uint32_t xoff[4];
+  // X: wave w fills tile rows XROWS w .. XROWS (w + 1) - 1
+  int xchunk[XROWS / 8];
+  uint32_t xoff[XROWS / 8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 32 * wave + 8 * j + (lane >> 3);
+  for (int j = 0; j < XROWS / 8; ++j) {
+    const int row = XROWS * wave + 8 * j + (lane >> 3);
     xchunk[j] = swz_chunk(row, lane & 7);
     xoff[j] = (uint32_t)row * K * 2 + xchunk[j] * 16;
   }
   // `buf` is a constant at every call site (the K loop is unrolled by two)
   auto load_x = [&](int step, int buf) {
-    char* dst = (buf ? lx1 : lx0) + wave * 4096;
+    char* dst = (buf ? lx1 : lx0) + wave * XROWS * 128;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < XROWS / 8; ++j) {
       uint32_t off = xoff[j];
       if constexpr (KTAIL) {
         if (step * BK + 8 * xchunk[j] >= K) off = kOutOfRange;
@@ -450,65 +465,98 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
     }
   };
 
-  float16_t acc[4][NB];
+  float16_t acc[WMT][NB];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < WMT; ++a)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
   const int fsw = (fi >> 1) & 7;  // swizzle of the fragment rows (tile row bases are multiples of 32)
-  auto compute = [&](int buf, const WRegs& r) {
-    const char* xa = (buf ? lx1 : lx0) + (wm + fi) * 128;
-    ZeroBias zb[NB];
-    half2_t s2[NB];
+  ZeroBias zb[NB];
+  half2_t s2[NB];
+  auto prep = [&](const WRegs& r) {  // the step's zero points and scales
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       zb[b] = zero_bias(ZP ? ((r.z[b] >> zshift[b]) & 15u) : 8u);
       s2[b] = splat2(__builtin_bit_cast(_Float16, (uint16_t)r.s[b]));
     }
-    half8_t af[2][4];
+  };
+  half8_t af[2][WMT], bf[2][NB];
+  // A fragments of slice ks of the tile in `buf` into af[d]; B fragments of
+  // slice ks of the words in r into bf[d]; the MFMAs of af[d] x bf[d]
+  auto read_a = [&](int buf, int ks, int d) {
+    const char* xa = (buf ? lx1 : lx0) + fi * 128 + 16 * ((4 * fh + ks) ^ fsw);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) af[0][a] = *reinterpret_cast<const half8_t*>(xa + 32 * 128 * a + 16 * ((4 * fh) ^ fsw));
+    for (int a = 0; a < WMT; ++a) af[d][a] = *reinterpret_cast<const half8_t*>(xa + 32 * 128 * a);
+  };
+  auto decode_b = [&](const WRegs& r, int ks, int d) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int cur = ks & 1, nx = cur ^ 1;
-      if (ks + 1 < BK / 16) {
-        const int slot = 16 * ((4 * fh + ks + 1) ^ fsw);
+    for (int b = 0; b < NB; ++b) bf[d][b] = decode_word_scaled(r.w[b][ks], zb[b], kc, s2[b]);
+  };
+  auto mfmas = [&](int d) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) af[nx][a] = *reinterpret_cast<const half8_t*>(xa + 32 * 128 * a + slot);
-      }
-      half8_t bf[NB];
+    for (int a = 0; a < WMT; ++a)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) bf[b] = decode_word_scaled(r.w[b][ks], zb[b], kc, s2[b]);
+      for (int b = 0; b < NB; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[d][a], bf[d][b], acc[a][b], 0, 0, 0);
+  };
+  // the slice's scheduling groups: per 32-row tile, one LDS read, an MFMA,
+  // three VALU instructions, the tile's other MFMAs, one VALU instruction
+  auto interleave = [&]() {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][a], bf[b], acc[a][b], 0, 0, 0);
+    for (int i = 0; i < WMT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, NB - 1 > 0 ? NB - 1 : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
     }
   };
+  // one K step with the tile in buffer c and its words in wc (wnx: the next
+  // step's words).  On entry af[0] / bf[0] hold slice 0; with `handover`, on
+  // exit they hold slice 0 of the next step.
+  auto body = [&](int c, WRegs& wc, const WRegs& wnx, int step, bool handover) {
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+      const int d = ks & 1;
+      read_a(c, ks + 1, d ^ 1);
+      decode_b(wc, ks + 1, d ^ 1);
+      if (ks == 2) fetch_w(wc, step + 2);  // wc fully decoded
+      mfmas(d);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (handover) {
+      // the next tile has landed everywhere and no wave still reads this one
+      __syncthreads();
+      asm volatile("" ::: "memory");
+      load_x(step + 2, c);
+      prep(wnx);
+      read_a(c ^ 1, 0, 0);
+      decode_b(wnx, 0, 0);
+    }
+    mfmas(1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  WRegs ra, rb;
+  WRegs w0, w1;
   load_x(s0, 0);
-  fetch_w(ra, s0);
-  fetch_w(rb, s0 + 1);
+  fetch_w(w0, s0);
+  fetch_w(w1, s0 + 1);
   __syncthreads();
+  load_x(s0 + 1, 1);
+  prep(w0);
+  read_a(0, 0, 0);
+  decode_b(w0, 0, 0);
   int step = s0;
   for (; step + 1 < s1; step += 2) {
-    load_x(step + 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(0, ra);
-    fetch_w(ra, step + 2);
-    __syncthreads();
-    load_x(step + 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1, rb);
-    fetch_w(rb, step + 3);
-    __syncthreads();
+    body(0, w0, w1, step, true);
+    body(1, w1, w0, step + 1, true);
   }
-  if (step < s1) compute(0, ra);
+  if (step < s1) body(0, w0, w1, step, false);
 
   // 32x32 accumulator layout: lane l holds column l % 32 and, in register r,
   // row 8 (r / 4) + 4 (l / 32) + r % 4.  Rows past M fall outside the buffer
@@ -517,14 +565,14 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
   if (splits == 1) {
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(Y + (size_t)m0 * ldy, (uint32_t)rows_m * ldy * 2);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < WMT; ++a)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int col = wn + 32 * b + fi;
         if (col >= rows_n) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = wm + 32 * a + 8 * (r >> 2) + 4 * fh + (r & 3);
+          const int row = 32 * a + 8 * (r >> 2) + 4 * fh + (r & 3);
           __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)acc[a][b][r]), ry,
                                                 (uint32_t)(row * ldy + n0 + col) * 2, 0, 0);
         }
@@ -533,14 +581,14 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(const _Float16* __restr
     const __amdgpu_buffer_rsrc_t rp =
         make_rsrc(part + ((size_t)split * M + m0) * N, (uint32_t)rows_m * N * 4);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < WMT; ++a)
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const int col = wn + 32 * b + fi;
         if (col >= rows_n) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = wm + 32 * a + 8 * (r >> 2) + 4 * fh + (r & 3);
+          const int row = 32 * a + 8 * (r >> 2) + 4 * fh + (r & 3);
           // through a named float: a bit cast applied to the vector element
           // itself was compiled into stores of one register for every r
           const float v = acc[a][b][r];
@@ -626,10 +674,10 @@ void launch_large_part(const _Float16* X, const uint32_t* qw, const uint16_t* sc
   const int spp = plan.splits > 1 ? plan.steps_per_split : (K + BK - 1) / BK;
   const dim3 grid(tiles_m * tiles_n * plan.splits);
   if (K % BK == 0)
-    hipLaunchKernelGGL((gemm_large_kernel<ZP, false, NB>), grid, dim3(512), 0, stream, X, qwp, scp, qzp, Y + n_base, M,
+    hipLaunchKernelGGL((gemm_large_kernel<ZP, false, NB>), grid, dim3(256), 0, stream, X, qwp, scp, qzp, Y + n_base, M,
                        N, K, gs, tiles_m, group_m, ldy, plan.splits, spp, part);
   else
-    hipLaunchKernelGGL((gemm_large_kernel<ZP, true, NB>), grid, dim3(512), 0, stream, X, qwp, scp, qzp, Y + n_base, M,
+    hipLaunchKernelGGL((gemm_large_kernel<ZP, true, NB>), grid, dim3(256), 0, stream, X, qwp, scp, qzp, Y + n_base, M,
                        N, K, gs, tiles_m, group_m, ldy, plan.splits, spp, part);
 }
 
