@@ -84,10 +84,32 @@ __device__ __forceinline__ void group_scale_zero(const float (&a)[8], _Float16& 
   }
 }
 
-// Code of one weight: clamp(rne(a / s) + z, 0, 15), as a float.
-__device__ __forceinline__ float code_of(float a, float s, float zf) {
-  const float v = rintf(a / s) + zf;
-  return fminf(fmaxf(v, 0.0f), 15.0f);
+// Codes of a lane's 8 weights of one group, clamp(rne(a / s) + z, 0, 15) as
+// floats, with a / s the correctly rounded fp32 quotient.  The quotient is
+// first taken as x = a * rcp(s): the reciprocal is within 1 ulp and the
+// product adds half an ulp, so x lies within |x| * 2^-21 of the correctly
+// rounded quotient f.  rint(x) and rne(f) can then differ only if a
+// half-integer lies between x and f, that is within |x| * 2^-21 of x; a lane
+// with any weight within |x| * 2^-20 of a half-integer (about 2^-15 of the
+// weights of a Gaussian group, every weight of a group on an exact half-step
+// grid, every quotient beyond 2^19 in magnitude) divides all 8 weights
+// exactly instead.  Bit-identical to dividing every weight.
+__device__ __forceinline__ void codes_of(const float (&a)[8], float s, float zf, float (&q)[8]) {
+  const float rs = __builtin_amdgcn_rcpf(s);
+  float k[8];
+  bool near_half = false;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float x = a[c] * rs;
+    k[c] = rintf(x);
+    near_half |= fabsf(fabsf(x - k[c]) - 0.5f) <= fabsf(x) * 0x1p-20f;
+  }
+  if (near_half) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) k[c] = rintf(a[c] / s);
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) q[c] = fminf(fmaxf(k[c] + zf, 0.0f), 15.0f);
 }
 
 // Range of the group a lane's 8 weights belong to, shrunk by `r` (weight
@@ -171,9 +193,11 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restr
       _Float16 s16;
       group_scale_zero<GW, ZP>(a, s16, s, zf);
 
+      float q[8];
+      codes_of(a, s, zf, q);
       uint32_t word = 0;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) word |= (uint32_t)code_of(a[c], s, zf) << nibble_shift(c);
+      for (int c = 0; c < 8; ++c) word |= (uint32_t)q[c] << nibble_shift(c);
       if (active) qweight[(size_t)n * kw + j] = word;
 
       const int grp = j / GW;
@@ -247,10 +271,12 @@ __global__ __launch_bounds__(kPackThreads) void scale_error_kernel(const u32x4* 
     group_scale_zero<GW, ZP>(a, s16, s, zf);
 
     // e only needs fp16 accuracy: w' / s by a reciprocal (1 ulp in fp32)
+    float q[8];
+    codes_of(a, s, zf, q);
     half8_t out;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float wq = (code_of(a[c], s, zf) - zf) * s;
+      const float wq = (q[c] - zf) * s;
       out[c] = (_Float16)(wq * __builtin_amdgcn_rcpf(sv[c]) - (float)h[c]);
     }
     if (active) e[(size_t)n * kw + j] = __builtin_bit_cast(u32x4, out);
@@ -293,9 +319,11 @@ __global__ __launch_bounds__(kPackThreads) void clip_error_kernel(const u32x4* _
     float s, zf;
     _Float16 s16;
     group_scale_zero<GW, ZP>(cl, s16, s, zf);
+    float q[8];
+    codes_of(cl, s, zf, q);
     half8_t out;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) out[c] = (_Float16)((code_of(cl[c], s, zf) - zf) * s - a[c]);
+    for (int c = 0; c < 8; ++c) out[c] = (_Float16)((q[c] - zf) * s - a[c]);
     if (active) e[(size_t)n * kw + j] = __builtin_bit_cast(u32x4, out);
   }
 }
