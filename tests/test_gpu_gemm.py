@@ -125,6 +125,15 @@ def test_gemm_batched_decode_full_size(M, name, K, N):
     check(M, N, K, 128, True, W, X, f"gemm {name} M={M}")
 
 
+@pytest.mark.parametrize("M,N,K,g", [(300, 33280, 128, 128), (257, 33280, 160, 32)])
+def test_gemm_half_width_tail_launch(M, N, K, g):
+    """260 tiles of 256 x 256 over 256 compute units: the last 512 columns are
+    computed by the second, half-width (256 x 128 tile) launch, with and
+    without a ragged last K step; every output is checked."""
+    assert G.lib().awq_gemm_workspace_bytes(M, N, K, g) == 0  # no K split at these sizes
+    check(M, N, K, g, True)
+
+
 @pytest.mark.parametrize("M", [96, 256, 512])
 @pytest.mark.parametrize("name,K,N", [workloads.LLAMA7B_BLOCK[0], workloads.LLAMA7B_BLOCK[4],
                                       workloads.LLAMA7B_BLOCK[6]])
