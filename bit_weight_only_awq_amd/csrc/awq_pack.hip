@@ -26,28 +26,38 @@ constexpr float kRangeFloor = 1e-5f;
 // aligned); every lane gets the result.  Partners come by DPP lane swaps
 // inside the 16-lane rows (xor 1 and xor 2 within quads, then mirrored
 // halves of 8 lanes, then the mirrored halves of the row) and, for 32-lane
-// groups, one permute across the two rows.  op is min or max, so the order
-// of the combinations does not change the result.
+// groups, one permute across the two rows.  The min / max is taken on an
+// order-preserving integer image of the (finite) floats: integer min / max
+// needs no NaN canonicalization of the permuted operand, so each step is one
+// DPP-fused instruction.  -0 orders below +0 there, which changes no scale,
+// zero point or code.
+__device__ __forceinline__ int ord_of(float x) {
+  const int i = __builtin_bit_cast(int, x);
+  return i ^ ((i >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float float_of(int o) { return __builtin_bit_cast(float, o ^ ((o >> 31) & 0x7FFFFFFF)); }
+
 template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ int dpp_mov(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
 }
 
 template <int GW, class Op>
 __device__ __forceinline__ float group_all(float v, Op op) {
-  if constexpr (GW >= 2) v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1, 0, 3, 2]
-  if constexpr (GW >= 4) v = op(v, dpp_mov<0x4E>(v));   // quad_perm [2, 3, 0, 1]
-  if constexpr (GW >= 8) v = op(v, dpp_mov<0x141>(v));  // row_half_mirror
-  if constexpr (GW >= 16) v = op(v, dpp_mov<0x140>(v)); // row_mirror
-  if constexpr (GW >= 32) v = op(v, __shfl_xor(v, 16));
-  return v;
+  int o = ord_of(v);
+  if constexpr (GW >= 2) o = op(o, dpp_mov<0xB1>(o));   // quad_perm [1, 0, 3, 2]
+  if constexpr (GW >= 4) o = op(o, dpp_mov<0x4E>(o));   // quad_perm [2, 3, 0, 1]
+  if constexpr (GW >= 8) o = op(o, dpp_mov<0x141>(o));  // row_half_mirror
+  if constexpr (GW >= 16) o = op(o, dpp_mov<0x140>(o)); // row_mirror
+  if constexpr (GW >= 32) o = op(o, __shfl_xor(o, 16));
+  return float_of(o);
 }
 
 struct MinOp {
-  __device__ float operator()(float a, float b) const { return fminf(a, b); }
+  __device__ int operator()(int a, int b) const { return a < b ? a : b; }
 };
 struct MaxOp {
-  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+  __device__ int operator()(int a, int b) const { return a > b ? a : b; }
 };
 
 // Scale and zero point of the group a lane's 8 weights belong to.  A group of
@@ -55,8 +65,10 @@ struct MaxOp {
 // shuffles (GW divides 32, so a group never leaves its half-wave, and all
 // lanes of a group are active or inactive together).  s16 is the fp16 scale,
 // s its fp32 value, zf the zero point as a float.
+// amax is the group's largest magnitude (a bound for every |a[c]|).
 template <int GW, bool ZP>
-__device__ __forceinline__ void group_scale_zero(const float (&a)[8], _Float16& s16, float& s, float& zf) {
+__device__ __forceinline__ void group_scale_zero(const float (&a)[8], _Float16& s16, float& s, float& zf,
+                                                 float& amax) {
   if constexpr (ZP) {
     float mn = a[0], mx = a[0];
 #pragma unroll
@@ -66,6 +78,7 @@ __device__ __forceinline__ void group_scale_zero(const float (&a)[8], _Float16& 
     }
     mn = group_all<GW>(mn, MinOp());
     mx = group_all<GW>(mx, MaxOp());
+    amax = fmaxf(fabsf(mn), fabsf(mx));
     float rng = mx - mn;
     if (rng < kRangeFloor) rng = kRangeFloor;
     s16 = (_Float16)(rng / 15.0f);
@@ -73,12 +86,12 @@ __device__ __forceinline__ void group_scale_zero(const float (&a)[8], _Float16& 
     zf = rintf(-mn / s);
     zf = fminf(fmaxf(zf, 0.0f), 15.0f);
   } else {
-    float amax = fabsf(a[0]);
+    float m = fabsf(a[0]);
 #pragma unroll
-    for (int c = 1; c < 8; ++c) amax = fmaxf(amax, fabsf(a[c]));
-    amax = group_all<GW>(amax, MaxOp());
-    if (amax < kRangeFloor) amax = kRangeFloor;
-    s16 = (_Float16)(amax / 7.0f);
+    for (int c = 1; c < 8; ++c) m = fmaxf(m, fabsf(a[c]));
+    amax = group_all<GW>(m, MaxOp());
+    const float am = amax < kRangeFloor ? kRangeFloor : amax;
+    s16 = (_Float16)(am / 7.0f);
     s = (float)s16;
     zf = 8.0f;
   }
@@ -88,28 +101,45 @@ __device__ __forceinline__ void group_scale_zero(const float (&a)[8], _Float16& 
 // floats, with a / s the correctly rounded fp32 quotient.  The quotient is
 // first taken as x = a * rcp(s): the reciprocal is within 1 ulp and the
 // product adds half an ulp, so x lies within |x| * 2^-21 of the correctly
-// rounded quotient f.  rint(x) and rne(f) can then differ only if a
-// half-integer lies between x and f, that is within |x| * 2^-21 of x; a lane
-// with any weight within |x| * 2^-20 of a half-integer (about 2^-15 of the
-// weights of a Gaussian group, every weight of a group on an exact half-step
-// grid, every quotient beyond 2^19 in magnitude) divides all 8 weights
-// exactly instead.  Bit-identical to dividing every weight.
-__device__ __forceinline__ void codes_of(const float (&a)[8], float s, float zf, float (&q)[8]) {
+// rounded quotient f, and rint(x) and rne(f) can differ only if a
+// half-integer lies within that distance of x.  With m = amax * rcp(s) *
+// 2^-20, at least twice that distance for every weight of the group, a lane
+// keeps rint(x) when all its 8 products lie more than m from a half-integer
+// (|x - rint(x)| < 0.5 - m; about 2^-15 of the weights of a Gaussian group
+// fail it), and divides all 8 weights exactly otherwise (every weight of a
+// group on an exact half-step grid, every group whose quotients pass 2^19).
+// Bit-identical to dividing every weight.
+__device__ __forceinline__ void codes_of(const float (&a)[8], float s, float zf, float amax, float (&q)[8]) {
   const float rs = __builtin_amdgcn_rcpf(s);
+  const float lim = 0.5f - amax * rs * 0x1p-20f;
   float k[8];
-  bool near_half = false;
+  float dmax = 0.0f;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const float x = a[c] * rs;
     k[c] = rintf(x);
-    near_half |= fabsf(fabsf(x - k[c]) - 0.5f) <= fabsf(x) * 0x1p-20f;
+    dmax = fmaxf(dmax, fabsf(x - k[c]));
   }
-  if (near_half) {
+  if (!(dmax < lim)) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) k[c] = rintf(a[c] / s);
   }
 #pragma unroll
   for (int c = 0; c < 8; ++c) q[c] = fminf(fmaxf(k[c] + zf, 0.0f), 15.0f);
+}
+
+// The packed word of 8 codes (small integers held as floats): two codes per
+// byte, byte b holding the codes of channels 2b' and 2b' + 2 in the order of
+// nibble_shift, each byte inserted by one float-to-u8 conversion.
+__device__ __forceinline__ uint32_t pack_word(const float (&q)[8]) {
+  uint32_t w = 0;
+  // nibble_shift: c = 0, 2 -> byte 0; 4, 6 -> byte 1; 1, 3 -> byte 2; 5, 7 -> byte 3
+  // (exact: small integers)
+  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[2], 16.0f, q[0]), 0, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[6], 16.0f, q[4]), 1, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[3], 16.0f, q[1]), 2, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[7], 16.0f, q[5]), 3, w);
+  return w;
 }
 
 // Range of the group a lane's 8 weights belong to, shrunk by `r` (weight
@@ -189,15 +219,13 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restr
 #pragma unroll
       for (int c = 0; c < 8; ++c) a[c] = (float)h[c];
 
-      float s, zf;
+      float s, zf, amax;
       _Float16 s16;
-      group_scale_zero<GW, ZP>(a, s16, s, zf);
+      group_scale_zero<GW, ZP>(a, s16, s, zf, amax);
 
       float q[8];
-      codes_of(a, s, zf, q);
-      uint32_t word = 0;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) word |= (uint32_t)q[c] << nibble_shift(c);
+      codes_of(a, s, zf, amax, q);
+      const uint32_t word = pack_word(q);
       if (active) qweight[(size_t)n * kw + j] = word;
 
       const int grp = j / GW;
@@ -266,13 +294,13 @@ __global__ __launch_bounds__(kPackThreads) void scale_error_kernel(const u32x4* 
 #pragma unroll
     for (int c = 0; c < 8; ++c) a[c] = (float)(_Float16)((float)h[c] * sv[c]);
 
-    float s, zf;
+    float s, zf, amax;
     _Float16 s16;
-    group_scale_zero<GW, ZP>(a, s16, s, zf);
+    group_scale_zero<GW, ZP>(a, s16, s, zf, amax);
 
     // e only needs fp16 accuracy: w' / s by a reciprocal (1 ulp in fp32)
     float q[8];
-    codes_of(a, s, zf, q);
+    codes_of(a, s, zf, amax, q);
     half8_t out;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -316,11 +344,11 @@ __global__ __launch_bounds__(kPackThreads) void clip_error_kernel(const u32x4* _
     float cl[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) cl[c] = (float)(_Float16)fminf(fmaxf(a[c], lo), hi);
-    float s, zf;
+    float s, zf, amax;
     _Float16 s16;
-    group_scale_zero<GW, ZP>(cl, s16, s, zf);
+    group_scale_zero<GW, ZP>(cl, s16, s, zf, amax);
     float q[8];
-    codes_of(cl, s, zf, q);
+    codes_of(cl, s, zf, amax, q);
     half8_t out;
 #pragma unroll
     for (int c = 0; c < 8; ++c) out[c] = (_Float16)((q[c] - zf) * s - a[c]);
