@@ -107,10 +107,13 @@ __host__ __device__ __forceinline__ size_t zero_word_index(int n, int j, int G) 
 // lanes 0-31, row a summed over lanes l and l + 32 and, in lanes 32-63, row b
 // summed the same way.  v_permlane16_swap does the same between the odd
 // 16-lane rows of its first operand and the even rows of its second.  After
-// the two exchanges lane group r = lane / 16 carries partials of row r only,
-// and four DPP row rotations (by 8, 4, 2, 1 lanes) complete the sum within
-// the group.  Returns row lane / 16's total, valid in every lane of the group;
-// each lane's order of additions is fixed, so results are reproducible.
+// the two exchanges lane group r = lane / 16 carries partials of row r only;
+// a DPP rotation by 8 adds the partial 8 lanes away (the same pair in either
+// rotation direction), and a mirror within 8 lanes and two quad swaps finish
+// the sum.  Returns row lane / 16's total in lanes with lane % 8 == 0 (the
+// others hold it in another order of additions).  The order is fixed, and the
+// eight-row version below adds every row in exactly the same order, so a row
+// gets the same bits from either.
 // (The two results are copied to named scalars before the bit casts: a bit
 // cast applied directly to an element of the returned vector has been compiled
 // as a cast of one and the same element for both.)
@@ -130,15 +133,35 @@ template <int CTRL>
 __device__ __forceinline__ float row_rotate(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
+// the sum over each 8-lane half-row of a 16-lane row
+__device__ __forceinline__ float octet_sum(float u) {
+  u += row_rotate<0x141>(u);  // row_half_mirror
+  u += row_rotate<0x4E>(u);   // quad_perm [2, 3, 0, 1]
+  u += row_rotate<0xB1>(u);   // quad_perm [1, 0, 3, 2]
+  return u;
+}
 __device__ __forceinline__ float wave_reduce_quad_rows(const float (&v)[4]) {
   const float a = swap_sum32(v[0], v[2]);  // lanes 0-31: row 0, lanes 32-63: row 2
   const float b = swap_sum32(v[1], v[3]);  // lanes 0-31: row 1, lanes 32-63: row 3
-  float s = swap_sum16(a, b);              // lanes 16 r .. 16 r + 15: row r
-  s += row_rotate<0x128>(s);               // row_ror:8
-  s += row_rotate<0x124>(s);               // row_ror:4
-  s += row_rotate<0x122>(s);               // row_ror:2
-  s += row_rotate<0x121>(s);               // row_ror:1
-  return s;
+  const float s = swap_sum16(a, b);        // lanes 16 r .. 16 r + 15: row r
+  return octet_sum(s + row_rotate<0x128>(s));  // row_ror:8
+}
+
+// The same for eight rows: the same two levels of lane-half swaps leave rows
+// r and r + 4 in 16-lane group r; after the rotation by 8 a lane select puts
+// row r in lanes 0-7 of the group and row r + 4 in lanes 8-15, and the same
+// 8-lane sum completes both.  Returns the total of row
+// (lane / 16) + 4 ((lane / 8) mod 2) in lanes with lane % 8 == 0.
+__device__ __forceinline__ float wave_reduce_oct_rows(const float (&v)[8]) {
+  const float a0 = swap_sum32(v[0], v[2]);  // lanes 0-31: row 0, 32-63: row 2
+  const float a1 = swap_sum32(v[1], v[3]);
+  const float a2 = swap_sum32(v[4], v[6]);  // lanes 0-31: row 4, 32-63: row 6
+  const float a3 = swap_sum32(v[5], v[7]);
+  const float s0 = swap_sum16(a0, a1);      // 16-lane group r: row r
+  const float s1 = swap_sum16(a2, a3);      // 16-lane group r: row r + 4
+  const float t0 = s0 + row_rotate<0x128>(s0);
+  const float t1 = s1 + row_rotate<0x128>(s1);
+  return octet_sum((__lane_id() & 8) ? t1 : t0);
 }
 
 // The hardware dispatches workgroup b of a 1-D grid to XCD (b mod 8).  This

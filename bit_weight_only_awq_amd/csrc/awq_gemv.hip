@@ -4,20 +4,21 @@
 // 使用指南", section WQLinear 内核全景: single-token generation, batch 1).  At
 // batch 1 every packed weight byte is used exactly once, so the kernel is a
 // stream over HBM.  Design for gfx950:
-//   * one workgroup per quad of output rows; a lane owns 32-channel chunks of
-//     all 4 rows and loads them as 128-bit words, so every weight load of a
-//     wave reads 1 KiB of one row contiguously;
-//   * the 4 rows share the lane's activations; the quad's 4 scales arrive in
-//     one 64-bit load and its zero points in one 32-bit load, and with the
-//     row-octet-major scale/zero layout consecutive lanes read consecutive
-//     groups, so these side loads stay coalesced;
+//   * one workgroup per quad (or, on layers large enough to fill the chip
+//     with half as many workgroups, per octet) of output rows; a lane owns
+//     32-channel chunks of all its rows and loads them as 128-bit words, so
+//     every weight load of a wave reads 1 KiB of one row contiguously;
+//   * the rows share the lane's activations; their scales arrive in one 64-bit
+//     (quad) or 128-bit (octet) load and their zero points in one 32-bit
+//     load, and with the row-octet-major scale/zero layout consecutive lanes
+//     read consecutive groups, so these side loads stay coalesced;
 //   * side loads are issued before the weight loads, so row 0 is decoded as
 //     soon as its weights land while rows 1-3 are still in flight;
 //   * decoding is exact bit arithmetic (q - z as small fp16 integers) followed
 //     by v_dot2_f32_f16 against the fp16 activations; the group scale
 //     multiplies the fp32 chunk sum once, so no decoded weight is rounded;
-//   * row sums are reduced across the wave in registers (two lane-swap
-//     exchanges that leave one row per 16-lane group, then DPP row rotations),
+//   * row sums are reduced across the wave in registers (lane-swap exchanges
+//     that leave one row per 16- or 8-lane group, then DPP lane rotations),
 //     then across waves through LDS in a fixed order: bit-reproducible results.
 #include "awq_device.hpp"
 #include "awq_launch.hpp"
@@ -25,49 +26,58 @@
 namespace awq {
 namespace {
 
-constexpr int kRows = 4;
-
-template <int NW, bool ZP>
+template <int NW, bool ZP, int ROWS>
 __global__ __launch_bounds__(NW * 64) void gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ qweight,
                                                        const uint16_t* __restrict__ scales,
                                                        const uint32_t* __restrict__ qzeros,
                                                        _Float16* __restrict__ y, int N, int K, int gshift) {
+  static_assert(ROWS == 4 || ROWS == 8, "row quads or octets");
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  __shared__ float red[NW][kRows];
+  __shared__ float red[NW][ROWS];
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int n0 = blockIdx.x * kRows;
+  const int n0 = blockIdx.x * ROWS;
   const int chunks = K >> 5;                // 32-channel chunks per row
   const int G = K >> gshift;
   const size_t row_u4 = (size_t)(K >> 5);   // a row is K/2 bytes = K/32 128-bit words
-  const int sub = n0 & 7;                   // 0 or 4: position of the quad in its octet
+  const int sub = n0 & 7;                   // quads: 0 or 4, the position of the quad in its octet
 
   const u32x4* wrow = qweight + (size_t)n0 * row_u4;
-  const uint16_t* squad = scales + scale_index(n0, 0, G);
+  const uint16_t* sq = scales + scale_index(n0, 0, G);
   const uint32_t* zoct = qzeros + (ZP ? zero_word_index(n0, 0, G) : 0);
   const DecodeConsts kc;
 
-  float acc[kRows];
+  float acc[ROWS];
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) acc[r] = 0.0f;
+  for (int r = 0; r < ROWS; ++r) acc[r] = 0.0f;
 
   for (int c = t; c < chunks; c += NW * 64) {
     const int grp = (c << 5) >> gshift;
-    const u32x2 sv = *reinterpret_cast<const u32x2*>(squad + (size_t)grp * 8);
-    const uint32_t zw = ZP ? (zoct[grp] >> (4 * sub)) : 0x88888888u;
+    // the rows' scales: 8 (16 bytes, an octet) or 4 (8 bytes) consecutive fp16
+    uint32_t sw[ROWS / 2];
+    if constexpr (ROWS == 8) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sq + (size_t)grp * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sw[i] = v[i];
+    } else {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(sq + (size_t)grp * 8);
+      sw[0] = v[0];
+      sw[1] = v[1];
+    }
+    const uint32_t zw = ZP ? (zoct[grp] >> (ROWS == 8 ? 0 : 4 * sub)) : 0x88888888u;
     u32x4 xv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) xv[i] = x[(size_t)c * 4 + i];
-    u32x4 wv[kRows];
+    u32x4 wv[ROWS];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) wv[r] = wrow[(size_t)r * row_u4 + c];
+    for (int r = 0; r < ROWS; ++r) wv[r] = wrow[(size_t)r * row_u4 + c];
     // every load of the chunk is issued before any decoding: left alone, the
     // scheduler splits them into rounds around the dot products in the
     // variant without zero points (two to three load latencies per chunk)
     __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
+    for (int r = 0; r < ROWS; ++r) {
       const ZeroBias b = zero_bias((zw >> (4 * r)) & 15u);
       float part0 = 0.0f, part1 = 0.0f;
 #pragma unroll
@@ -79,21 +89,30 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const u32x4* __restrict__
         part0 = __builtin_amdgcn_fdot2(d[2], as_half2(xv[wi][2]), part0, false);
         part1 = __builtin_amdgcn_fdot2(d[3], as_half2(xv[wi][3]), part1, false);
       }
-      const uint32_t sbits = (sv[r >> 1] >> (16 * (r & 1))) & 0xFFFFu;
+      const uint32_t sbits = (sw[r >> 1] >> (16 * (r & 1))) & 0xFFFFu;
       const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
       acc[r] += (part0 + part1) * s;
     }
   }
 
-  const float total = wave_reduce_quad_rows(acc);
-  constexpr int kLanesPerRow = 64 / kRows;
+  float total;
+  int row;  // the row whose total this lane holds
+  if constexpr (ROWS == 8) {
+    total = wave_reduce_oct_rows(acc);
+    row = (lane >> 4) + 4 * ((lane >> 3) & 1);
+  } else {
+    total = wave_reduce_quad_rows(acc);
+    row = lane >> 4;
+  }
+  // quads: lanes 0, 16, 32, 48; octets: every eighth lane
+  const bool writer = (lane % (64 / ROWS)) == 0;
   if (NW == 1) {
-    if ((lane % kLanesPerRow) == 0) y[n0 + lane / kLanesPerRow] = (_Float16)total;
+    if (writer) y[n0 + row] = (_Float16)total;
     return;
   }
-  if ((lane % kLanesPerRow) == 0) red[wave][lane / kLanesPerRow] = total;
+  if (writer) red[wave][row] = total;
   __syncthreads();
-  if (t < kRows) {
+  if (t < ROWS) {
     float sum = red[0][t];
 #pragma unroll
     for (int w = 1; w < NW; ++w) sum += red[w][t];
@@ -103,22 +122,19 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const u32x4* __restrict__
 
 int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 128 ? 7 : 8; }
 
-template <bool ZP>
-hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* y,
-                     int N, int K, int group_size, hipStream_t stream) {
-  // one 32-channel chunk per lane where K allows it (K = 4096: 2 waves; K = 11008: 6 waves)
+bool gemv_uses_octets(int N, int K) {
   const int chunks = K >> 5;
-  int nw = (chunks + 63) / 64;
-  if (nw > 8) nw = 8;
-  const dim3 grid(N / kRows);
-  const u32x4* xv = static_cast<const u32x4*>(x);
-  const u32x4* wv = reinterpret_cast<const u32x4*>(qweight);
-  const uint16_t* sc = static_cast<const uint16_t*>(scales);
-  _Float16* yv = static_cast<_Float16*>(y);
-  const int gs = log2_group(group_size);
-#define AWQ_GEMV_CASE(W)                                                                                  \
-  case W:                                                                                                 \
-    hipLaunchKernelGGL((gemv_kernel<W, ZP>), grid, dim3(W * 64), 0, stream, xv, wv, sc, qzeros, yv, N, K, gs); \
+  const int nw = chunks > 8 * 64 ? 8 : (chunks + 63) / 64;
+  return (long)(N / 8) * nw >= 16 * 256;
+}
+
+template <bool ZP, int ROWS>
+hipError_t launch_rows(const u32x4* xv, const u32x4* wv, const uint16_t* sc, const uint32_t* qzeros, _Float16* yv,
+                       int N, int K, int gs, int nw, hipStream_t stream) {
+  const dim3 grid(N / ROWS);
+#define AWQ_GEMV_CASE(W)                                                                                    \
+  case W:                                                                                                   \
+    hipLaunchKernelGGL((gemv_kernel<W, ZP, ROWS>), grid, dim3(W * 64), 0, stream, xv, wv, sc, qzeros, yv, N, K, gs); \
     break;
   switch (nw) {
     AWQ_GEMV_CASE(1)
@@ -133,6 +149,27 @@ hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales,
   }
 #undef AWQ_GEMV_CASE
   return hipGetLastError();
+}
+
+template <bool ZP>
+hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* y,
+                     int N, int K, int group_size, hipStream_t stream) {
+  // one 32-channel chunk per lane where K allows it (K = 4096: 2 waves; K = 11008: 6 waves)
+  const int chunks = K >> 5;
+  int nw = (chunks + 63) / 64;
+  if (nw > 8) nw = 8;
+  const u32x4* xv = static_cast<const u32x4*>(x);
+  const u32x4* wv = reinterpret_cast<const u32x4*>(qweight);
+  const uint16_t* sc = static_cast<const uint16_t*>(scales);
+  _Float16* yv = static_cast<_Float16*>(y);
+  const int gs = log2_group(group_size);
+  // row octets halve the activation loads per weight byte, but take half as
+  // many workgroups: they pay once the octets alone give ~16 waves per compute
+  // unit (the 70B MLP layers: 9% faster), quads stay faster below (the 7B
+  // layers: 2-15%)
+  if (gemv_uses_octets(N, K))
+    return launch_rows<ZP, 8>(xv, wv, sc, qzeros, yv, N, K, gs, nw, stream);
+  return launch_rows<ZP, 4>(xv, wv, sc, qzeros, yv, N, K, gs, nw, stream);
 }
 
 }  // namespace

@@ -59,6 +59,16 @@ def test_gemv_ragged_and_minimal_shapes(N, K, g):
     check_layer(N, K, g, False)
 
 
+@pytest.mark.parametrize("N,K,g,zp", [(32768, 2048, 128, True), (16384, 2080, 32, False)])
+def test_gemv_row_octets_full(N, K, g, zp):
+    """Layers wide enough that the GEMV works on row octets instead of quads
+    (8 rows per workgroup, the octet's scales in one 16-byte load, the
+    eight-row register reduction), one with a ragged chunk count; every
+    output is checked."""
+    W = workloads.weight(N, K, cfg=5, layer=N + K, row_offset=True)
+    check_layer(N, K, g, zp, W=W)
+
+
 @pytest.mark.parametrize("name,K,N", workloads.LLAMA7B_BLOCK)
 def test_gemv_llama7b_block_full_size(name, K, N):
     layer = [n for n, _, _ in workloads.LLAMA7B_BLOCK].index(name)
