@@ -59,7 +59,8 @@ def test_gemv_ragged_and_minimal_shapes(N, K, g):
     check_layer(N, K, g, False)
 
 
-@pytest.mark.parametrize("N,K,g,zp", [(32768, 2048, 128, True), (16384, 2080, 32, False)])
+@pytest.mark.parametrize("N,K,g,zp", [(32768, 2048, 128, True), (16384, 2080, 32, False), (32768, 2048, 64, True),
+                                      (32768, 2048, 256, False)])
 def test_gemv_row_octets_full(N, K, g, zp):
     """Layers wide enough that the GEMV works on row octets instead of quads
     (8 rows per workgroup, the octet's scales in one 16-byte load, the
