@@ -336,8 +336,7 @@ hipError_t launch_skinny(const SkinnyPlan& p, const void* x, const uint32_t* qw,
 // --------------------------------------------------------------------------
 // Large M: matrix-core bound.
 // --------------------------------------------------------------------------
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int TILE_BYTES = BM * BK * 2;  // one 256 x 64 fp16 tile in LDS (32 KiB)
+constexpr int BM = 256, BN = 256, BK = 64;  // the full tile; 128-row tiles where 256-row ones are too few
 
 // LDS layout of a 256 x 64 fp16 tile: row r occupies bytes 128 r .. 128 r + 127,
 // and its 16-byte chunk c (channels 8 c .. 8 c + 7) sits in slot
@@ -373,7 +372,7 @@ __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((
 // return zero) and land where no one reads again.
 //   MFMA slice ks of step s, lane half h, element j  <->  channel 64 s + 32 h + 8 ks + j
 // (A and B use the same assignment, so the product is unchanged.)
-template <bool ZP, bool KTAIL, int NB>
+template <bool ZP, bool KTAIL, int NB, int TBM>
 __global__ __launch_bounds__(256) void gemm_large_kernel(const _Float16* __restrict__ X,
                                                          const uint32_t* __restrict__ qweight,
                                                          const uint16_t* __restrict__ scales,
@@ -381,9 +380,10 @@ __global__ __launch_bounds__(256) void gemm_large_kernel(const _Float16* __restr
                                                          _Float16* __restrict__ Y, int M, int N, int K, int gshift,
                                                          int tiles_m, int group_m, int ldy, int splits,
                                                          int steps_per_split, float* __restrict__ part) {
-  constexpr int NW = 4, WMT = BM / 32;        // waves; 32-row MFMA tiles per wave
+  constexpr int NW = 4, WMT = TBM / 32;       // waves; 32-row MFMA tiles per wave
   constexpr int WN = 32 * NB, TBN = NW * WN;  // wave and workgroup tile widths
-  constexpr int XROWS = BM / NW;              // X tile rows each wave loads, 8 per 1 KiB load
+  constexpr int XROWS = TBM / NW;             // X tile rows each wave loads, 8 per 1 KiB load
+  constexpr int TILE_BYTES = TBM * BK * 2;    // one TBM x 64 fp16 tile in LDS
   // two arrays, so that the compiler's wait for buffer-to-LDS loads in flight
   // before an LDS read covers only the loads into the array being read
   __shared__ __attribute__((aligned(1024))) char lx0[TILE_BYTES], lx1[TILE_BYTES];
@@ -398,8 +398,8 @@ __global__ __launch_bounds__(256) void gemm_large_kernel(const _Float16* __restr
   const int per_group = group_m * tiles_n, grp0 = tile / per_group, first_m = grp0 * group_m;
   const int gm = min(tiles_m - first_m, group_m), r_in = tile - grp0 * per_group;
   const int tm = first_m + r_in % gm, tn = r_in / gm;
-  const int m0 = tm * BM, n0 = tn * TBN;
-  const int rows_m = min(BM, M - m0), rows_n = min(TBN, N - n0);
+  const int m0 = tm * TBM, n0 = tn * TBN;
+  const int rows_m = min(TBM, M - m0), rows_n = min(TBN, N - n0);
   const int wn = wave * WN;
   const int nsteps = (K + BK - 1) / BK;
   const int s0 = split * steps_per_split, s1 = min(nsteps, s0 + steps_per_split);  // this workgroup's K steps
@@ -622,25 +622,46 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float4_t* __re
 // Splitting pays when there are fewer tiles than compute units (M from 65 to
 // a few hundred tokens).
 struct LargePlan {
-  int splits, steps_per_split;
+  int tbm, splits, steps_per_split;
 };
 
+// Tile height and K split of the matrix-core kernel, from a small time model:
+// waves of workgroups over the compute units times the steps each takes (a
+// 256 x 256 x 64 tile step ~1.2 us, a 128-row one ~0.70 us: half the matrix
+// work, twice the weight decode per product; a last wave at most half full
+// runs as half-width tiles without a K split and costs ~0.6 of a wave with
+// 256-row tiles, ~0.85 with 128-row ones), plus, with K split, the fp32
+// partials written and read at ~5 TB/s and the reduction launch.  128-row
+// tiles win where 256-row ones are too few to fill the chip without a K split
+// (4096-wide layers up to a few thousand tokens: 10-12% faster there).
 LargePlan plan_large(int M, int N, int K) {
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int steps = (K + BK - 1) / BK;
   constexpr int kUnits = 256;
-  LargePlan best{1, steps};
-  // partial tiles are addressed with 32-bit offsets: 256 rows x N fp32 < 2^31
-  if ((size_t)BM * N * 4 >= ((size_t)1 << 31)) return best;
-  double best_t = (double)((tiles + kUnits - 1) / kUnits) * steps * 1.2;
-  for (int s = 2; s <= 16 && steps / s >= 2; ++s) {
-    const int spp = (steps + s - 1) / s;
-    const int sp = (steps + spp - 1) / spp;
-    const double t = (double)((tiles * sp + kUnits - 1) / kUnits) * spp * 1.2 +
-                     (double)sp * M * N * 8 / 5e6 + 2.0;
-    if (t < best_t) {
-      best_t = t;
-      best = {sp, spp};
+  LargePlan best{BM, 1, steps};
+  double best_t = 1e300;
+  for (int tbm : {BM, BM / 2}) {
+    const double step_us = tbm == BM ? 1.2 : 0.70, half_tail = tbm == BM ? 0.6 : 0.85;
+    auto waves = [&](int wgs, bool split) {
+      const int full = wgs / kUnits, rem = wgs % kUnits;
+      if (rem == 0) return (double)full;
+      return full + (!split && full > 0 && 2 * rem <= kUnits ? half_tail : 1.0);
+    };
+    const int tiles = ((M + tbm - 1) / tbm) * ((N + BN - 1) / BN);
+    const double t1 = waves(tiles, false) * steps * step_us;
+    if (t1 < best_t) {
+      best_t = t1;
+      best = {tbm, 1, steps};
+    }
+    // partial tiles are addressed with 32-bit offsets: tile rows x N fp32 < 2^31
+    if ((size_t)tbm * N * 4 >= ((size_t)1 << 31)) continue;
+    for (int s = 2; s <= 16 && steps / s >= 2; ++s) {
+      const int spp = (steps + s - 1) / s;
+      const int sp = (steps + spp - 1) / spp;
+      const double t = waves(tiles * sp, true) * spp * step_us + (double)sp * M * N * 8 / 5e6 + 2.0;
+      if (t < best_t) {
+        best_t = t;
+        best = {tbm, sp, spp};
+      }
     }
   }
   return best;
@@ -656,13 +677,13 @@ int compute_units() {
   return cus;
 }
 
-template <bool ZP, int NB>
+template <bool ZP, int NB, int TBM>
 void launch_large_part(const _Float16* X, const uint32_t* qw, const uint16_t* sc, const uint32_t* qz, _Float16* Y, int M,
-                       int N, int K, int gs, int n_base, int ldy, hipStream_t stream, LargePlan plan = {1, 0},
+                       int N, int K, int gs, int n_base, int ldy, hipStream_t stream, LargePlan plan,
                        float* part = nullptr) {
   constexpr int TBN = 128 * NB;
   const int G = K >> gs;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + TBN - 1) / TBN;
+  const int tiles_m = (M + TBM - 1) / TBM, tiles_n = (N + TBN - 1) / TBN;
   // tiles are ordered in groups of 4 tile rows (all tile columns of a group
   // before the next group), so the 32-tile band that one XCD works on spans
   // 4 row bands of X and 8 column bands of W instead of all row bands: about
@@ -674,24 +695,23 @@ void launch_large_part(const _Float16* X, const uint32_t* qw, const uint16_t* sc
   const int spp = plan.splits > 1 ? plan.steps_per_split : (K + BK - 1) / BK;
   const dim3 grid(tiles_m * tiles_n * plan.splits);
   if (K % BK == 0)
-    hipLaunchKernelGGL((gemm_large_kernel<ZP, false, NB>), grid, dim3(256), 0, stream, X, qwp, scp, qzp, Y + n_base, M,
-                       N, K, gs, tiles_m, group_m, ldy, plan.splits, spp, part);
+    hipLaunchKernelGGL((gemm_large_kernel<ZP, false, NB, TBM>), grid, dim3(256), 0, stream, X, qwp, scp, qzp,
+                       Y + n_base, M, N, K, gs, tiles_m, group_m, ldy, plan.splits, spp, part);
   else
-    hipLaunchKernelGGL((gemm_large_kernel<ZP, true, NB>), grid, dim3(256), 0, stream, X, qwp, scp, qzp, Y + n_base, M,
-                       N, K, gs, tiles_m, group_m, ldy, plan.splits, spp, part);
+    hipLaunchKernelGGL((gemm_large_kernel<ZP, true, NB, TBM>), grid, dim3(256), 0, stream, X, qwp, scp, qzp,
+                       Y + n_base, M, N, K, gs, tiles_m, group_m, ldy, plan.splits, spp, part);
 }
 
-// 256x256 tiles; when the last wave of tiles over the compute units would run
-// at most half full, the N columns of that wave are computed instead as
-// 256x128 tiles in a second launch, so the tail takes half a tile time.
-template <bool ZP>
-hipError_t launch_large(const _Float16* X, const uint32_t* qw, const uint16_t* sc, const uint32_t* qz, _Float16* Y,
-                        int M, int N, int K, int gs, void* workspace, hipStream_t stream) {
-  const LargePlan plan = plan_large(M, N, K);
+// TBM x 256 tiles; when the last wave of tiles over the compute units would
+// run at most half full, the N columns of that wave are computed instead as
+// TBM x 128 tiles in a second launch, so the tail takes half a tile time.
+template <bool ZP, int TBM>
+hipError_t launch_large_tbm(const _Float16* X, const uint32_t* qw, const uint16_t* sc, const uint32_t* qz, _Float16* Y,
+                            int M, int N, int K, int gs, void* workspace, const LargePlan& plan, hipStream_t stream) {
   if (plan.splits > 1) {
     // partials after the counter region of the skinny kernel, which stays zero
     float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
-    launch_large_part<ZP, 2>(X, qw, sc, qz, Y, M, N, K, gs, 0, N, stream, plan, part);
+    launch_large_part<ZP, 2, TBM>(X, qw, sc, qz, Y, M, N, K, gs, 0, N, stream, plan, part);
     const size_t quads = (size_t)M * N / 4;
     size_t blocks = (quads + 255) / 256;
     if (blocks > 4096) blocks = 4096;
@@ -700,7 +720,7 @@ hipError_t launch_large(const _Float16* X, const uint32_t* qw, const uint16_t* s
     return hipGetLastError();
   }
   const int cus = compute_units();
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int tiles_m = (M + TBM - 1) / TBM, tiles_n = (N + BN - 1) / BN;
   const int tiles = tiles_m * tiles_n, rem = tiles % cus;
   int tail_n = 0;  // 256-wide N tiles moved to the half-width launch
   if (tiles > cus && rem > 0 && 2 * rem <= cus) {
@@ -708,9 +728,17 @@ hipError_t launch_large(const _Float16* X, const uint32_t* qw, const uint16_t* s
     if (tail_n >= tiles_n) tail_n = 0;
   }
   const int n_main = (tiles_n - tail_n) * BN;
-  if (n_main > 0) launch_large_part<ZP, 2>(X, qw, sc, qz, Y, M, tail_n ? n_main : N, K, gs, 0, N, stream);
-  if (tail_n) launch_large_part<ZP, 1>(X, qw, sc, qz, Y, M, N - n_main, K, gs, n_main, N, stream);
+  if (n_main > 0) launch_large_part<ZP, 2, TBM>(X, qw, sc, qz, Y, M, tail_n ? n_main : N, K, gs, 0, N, stream, plan);
+  if (tail_n) launch_large_part<ZP, 1, TBM>(X, qw, sc, qz, Y, M, N - n_main, K, gs, n_main, N, stream, plan);
   return hipGetLastError();
+}
+
+template <bool ZP>
+hipError_t launch_large(const _Float16* X, const uint32_t* qw, const uint16_t* sc, const uint32_t* qz, _Float16* Y,
+                        int M, int N, int K, int gs, void* workspace, hipStream_t stream) {
+  const LargePlan plan = plan_large(M, N, K);
+  return plan.tbm == BM ? launch_large_tbm<ZP, BM>(X, qw, sc, qz, Y, M, N, K, gs, workspace, plan, stream)
+                        : launch_large_tbm<ZP, BM / 2>(X, qw, sc, qz, Y, M, N, K, gs, workspace, plan, stream);
 }
 
 template <bool ZP>

@@ -48,9 +48,10 @@ def test_gemm_launch_plans_through_workspace_sizes(lib):
     """The GEMM launch plans, seen through the workspace they need: on a
     4096 x 4096 layer, up to 8 tokens run as 16-row tiles without a K split
     (no workspace); 16 and 64 tokens split K across workgroups (512 KiB of
-    counters plus fp32 partial tiles); the large-M kernel splits K only while
-    its 256 x 256 tiles are fewer than the compute units: on 4096 x 4096 up to
-    M = 2048 (128 tiles), on the 70B MLP shape not at M = 2048 (896 tiles)."""
+    counters plus fp32 partial tiles); the matrix-core kernel splits K only
+    while its tiles (256 or 128 rows x 256) are too few for the compute units:
+    on 4096 x 4096 up to M = 1024, not at M = 2048 (256 tiles of 128 rows) nor
+    on the 70B MLP shapes at M = 2048 (896 and 256 tiles of 256 rows)."""
     ws = awq.awq_gemm_workspace_bytes
     counters = 512 * 1024
     for M in (1, 2, 4, 5, 8):
@@ -58,11 +59,13 @@ def test_gemm_launch_plans_through_workspace_sizes(lib):
     for M in (16, 64):
         need = ws(M, 4096, 4096, 128)
         assert need > counters and (need - counters) % (16 * 16 * 4) == 0, M
-    for M in (96, 256, 1024, 2048):
+    for M in (96, 256, 512, 1024):
         need = ws(M, 4096, 4096, 128)
         assert need > counters and (need - counters) % (M * 4096 * 4) == 0, M  # whole [splits][M][N] fp32 slices
+    assert ws(2048, 4096, 4096, 128) == 0
+    assert ws(4096, 4096, 4096, 128) == 0
     assert ws(2048, 28672, 8192, 128) == 0
-    assert ws(4096, 4096, 4096, 128) == 0  # 256 tiles: a full wave
+    assert ws(2048, 8192, 28672, 128) == 0
 
 
 # Fake, 16-byte aligned device addresses: validation must reject every call

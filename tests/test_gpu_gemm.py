@@ -134,13 +134,15 @@ def test_gemm_half_width_tail_launch(M, N, K, g):
     check(M, N, K, g, True)
 
 
-@pytest.mark.parametrize("M", [96, 256, 512])
+@pytest.mark.parametrize("M", [96, 256, 512, 1000, 2048])
 @pytest.mark.parametrize("name,K,N", [workloads.LLAMA7B_BLOCK[0], workloads.LLAMA7B_BLOCK[4],
                                       workloads.LLAMA7B_BLOCK[6]])
 def test_gemm_medium_m_full_size(M, name, K, N):
-    """Token counts between the skinny and the full-GPU regimes, where the
-    matrix-core kernel splits K over workgroups (fp32 partials added by a
-    second kernel); the oracle checks a sample of rows."""
+    """Token counts between the skinny and the full-GPU regimes on the 7B
+    shapes: the matrix-core kernel on 128- or 256-row tiles, splitting K over
+    workgroups (fp32 partials added by a second kernel) while the tiles are
+    too few, with a ragged last row tile at M = 1000; the oracle checks a
+    sample of rows."""
     awq = G.lib()
     g = 128
     layer = [n for n, _, _ in workloads.LLAMA7B_BLOCK].index(name)
