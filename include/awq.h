@@ -126,9 +126,10 @@ int awq_gemv(const void* x, const uint32_t* qweight, const void* scales, const u
  * the buffer is first used (e.g. allocated zero-filled); every call returns
  * it to zero, so one buffer serves any number of calls of any shape in
  * stream order.  Calls that may run concurrently (different streams) need
- * separate workspaces.  For larger M with few output tiles (M up to a few
- * hundred), K is split as well: the fp32 partial products follow the counter
- * region and a second kernel adds them in a fixed order.
+ * separate workspaces.  For larger M with few output tiles (M up to about a
+ * thousand on 4096-wide layers), K is split as well: the fp32 partial
+ * products follow the counter region and a second kernel adds them in a
+ * fixed order.
  */
 int awq_gemm(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros,
              void* y, int32_t M, int32_t N, int32_t K, int32_t group_size, int32_t zero_point,
