@@ -347,12 +347,13 @@ constexpr int BM = 256, BN = 256, BK = 64;  // the full tile; 128-row tiles wher
 // of slots is exactly what one buffer-to-LDS load of 64 lanes x 16 bytes writes.
 __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-// One wave per SIMD: 4 waves of 256 x (32 NB) outputs (tile width 128 NB),
-// every wave multiplying all 256 rows of the X tile, so each packed weight
-// word is loaded and decoded once per workgroup (1.9 VALU instructions per
-// MFMA; with two M-halves decoding the same words it was 3.7, and at the
-// power limit every VALU instruction per MFMA costs about 3% of throughput).
-// The 256 accumulators per lane sit in the AGPRs.
+// One wave per SIMD: 4 waves of TBM x (32 NB) outputs (tile TBM x 128 NB, TBM
+// = 256, or 128 where 256-row tiles are too few), every wave multiplying all
+// TBM rows of the X tile, so each packed weight word is loaded and decoded
+// once per workgroup (1.9 VALU instructions per MFMA at TBM = 256; with two
+// M-halves decoding the same words it was 3.7, and at the power limit every
+// VALU instruction per MFMA costs about 3% of throughput).  The TBM accumulators
+// per lane sit in the AGPRs.
 //
 // Only X goes through LDS: tiles go from HBM straight into LDS by
 // buffer-to-LDS loads, double-buffered.  The weights go to the matrix cores
@@ -616,11 +617,6 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float4_t* __re
   }
 }
 
-// K split of the matrix-core kernel, chosen from a simple time model: one
-// 256 x 256 x 64 tile step takes about 1.2 us, the fp32 partials cost a write
-// and a read at about 5 TB/s, and the reduction is one more launch (~2 us).
-// Splitting pays when there are fewer tiles than compute units (M from 65 to
-// a few hundred tokens).
 struct LargePlan {
   int tbm, splits, steps_per_split;
 };
