@@ -125,13 +125,21 @@ def test_gemm_batched_decode_full_size(M, name, K, N):
     check(M, N, K, 128, True, W, X, f"gemm {name} M={M}")
 
 
-@pytest.mark.parametrize("M,N,K,g", [(300, 33280, 128, 128), (257, 33280, 160, 32)])
-def test_gemm_half_width_tail_launch(M, N, K, g):
-    """260 tiles of 256 x 256 over 256 compute units: the last 512 columns are
-    computed by the second, half-width (256 x 128 tile) launch, with and
-    without a ragged last K step; every output is checked."""
-    assert G.lib().awq_gemm_workspace_bytes(M, N, K, g) == 0  # no K split at these sizes
-    check(M, N, K, g, True)
+# Launch paths of the matrix-core kernel, one shape each (all outputs
+# checked; N ragged by 8 rows): 256- or 128-row tiles as the launch plan
+# picks them, with the last wave of tiles run by the second, half-width
+# launch or not, with K split or not, with a ragged last K step or not.
+@pytest.mark.parametrize("M,N,K,g,split,what", [
+    (261, 44280, 128, 128, False, "256-row tiles, half-width tail"),
+    (261, 44280, 96, 32, False, "256-row tiles, half-width tail, ragged K"),
+    (135, 33528, 96, 32, False, "256-row tiles, one wave, ragged K"),
+    (513, 44280, 128, 128, False, "128-row tiles, half-width tail"),
+    (513, 44280, 96, 32, False, "128-row tiles, half-width tail, ragged K"),
+    (65, 512, 544, 32, True, "128-row tiles, K split, ragged K"),
+])
+def test_gemm_large_launch_paths(M, N, K, g, split, what):
+    assert (G.lib().awq_gemm_workspace_bytes(M, N, K, g) > 0) == split, what
+    check(M, N, K, g, True, what=f"{what}: M={M} N={N} K={K} g={g}")
 
 
 @pytest.mark.parametrize("M", [96, 256, 512, 1000, 2048])
