@@ -449,12 +449,15 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
 template <bool ZP>
 hipError_t launch_pack_zp(const void* w, int N, int K, int group_size, uint32_t* qweight, void* scales,
                           uint32_t* qzeros, hipStream_t stream) {
-  // K is cut into slices of whole 4-pass rings (128 words, 1024 channels)
-  // until the grid has about 8192 blocks: one block per row octet streams a
-  // row with too few loads in flight (a 4096-row layer: 243 us per Llama-7B
-  // block of 7 linears, against 206-212 us with the slices; finer slices or
-  // more blocks change nothing)
-  constexpr int kTargetBlocks = 8192, kRingWords = 128;
+  // K is cut into slices of whole 2-pass rings (64 words, 512 channels, a
+  // multiple of every group) until the grid has about 8192 blocks: one block
+  // per row octet streams a row with too few loads in flight (243 us per
+  // Llama-7B block of 7 linears with the first quantizer, against 206-212 us
+  // with slices of 1024 channels).  With the current quantizer (150-155 us
+  // per block) 512-channel slices are 3-5% faster than 1024-channel ones;
+  // fewer slices (1024-4096 target blocks) are 5-18% slower, twice the target
+  // blocks slower at g = 256.
+  constexpr int kTargetBlocks = 8192, kRingWords = 64;
   const int kw = K >> 3, octets = N / 8;
   const int rings = (kw + kRingWords - 1) / kRingWords;
   int slices = (kTargetBlocks + octets - 1) / octets;
