@@ -6,7 +6,8 @@
 // rounding of the product with the group scale) and multiplied on the gfx950
 // fp16 matrix cores with fp32 accumulation.  Two kernels:
 //
-//   * gemm_skinny_kernel (M <= 64): bound by the weight stream (and, from
+//   * gemm_skinny_kernel (M <= 64, but 33-64 tokens on layers with N >= 8192
+//     go to the matrix-core kernel): bound by the weight stream (and, from
 //     ~16 tokens on, by the activation loads).  A workgroup owns NT tiles of
 //     16 output rows, all (<= 4) tiles of 16 tokens and one slice of K; its
 //     lanes load packed weights straight into MFMA B-operand registers (one
@@ -17,7 +18,8 @@
 //     workspace and the last workgroup of each tile adds them in slice order
 //     (deterministic, one launch).
 //
-//   * gemm_large_kernel (M > 64): matrix-core bound.  256 x 256 output tile
+//   * gemm_large_kernel (M > 64, and 33-64 tokens on layers with N >= 8192
+//     on 64-row tiles): matrix-core bound.  256 x 256 output tile
 //     (or 256 x 128 for the last wave of tiles) per workgroup of 4 waves, one
 //     per SIMD, each 256 x 64 (v_mfma_f32_32x32x16_f16, accumulators in the
 //     AGPRs), K in steps of 64.  X tiles go from HBM straight into LDS
@@ -729,9 +731,29 @@ hipError_t launch_large_tbm(const _Float16* X, const uint32_t* qw, const uint16_
   return hipGetLastError();
 }
 
+// 33-64 tokens on wide layers (N >= 8192): the matrix-core kernel on 64-row
+// tiles, K split to about 128 workgroups.  Its waves share each activation
+// tile through LDS, where the skinny kernel's waves each load their own from
+// L2 (4096 -> 11008 at 64 tokens: 22.5 us against 31.9 us, at 48 tokens 21.6
+// against 23.3); on narrower layers the skinny kernel stays faster.
+bool gemm_uses_mid(int M, int N) { return M > 32 && M <= 64 && N >= 8192; }
+
+LargePlan plan_mid(int M, int N, int K) {
+  (void)M;
+  const int steps = (K + BK - 1) / BK;
+  const int tiles = (N + BN - 1) / BN;
+  int s = (128 + tiles - 1) / tiles;
+  if (s > steps / 2) s = steps / 2;
+  if (s < 1) s = 1;
+  const int spp = (steps + s - 1) / s;
+  return LargePlan{64, (steps + spp - 1) / spp, spp};
+}
+
 template <bool ZP>
 hipError_t launch_large(const _Float16* X, const uint32_t* qw, const uint16_t* sc, const uint32_t* qz, _Float16* Y,
                         int M, int N, int K, int gs, void* workspace, hipStream_t stream) {
+  if (gemm_uses_mid(M, N))
+    return launch_large_tbm<ZP, 64>(X, qw, sc, qz, Y, M, N, K, gs, workspace, plan_mid(M, N, K), stream);
   const LargePlan plan = plan_large(M, N, K);
   return plan.tbm == BM ? launch_large_tbm<ZP, BM>(X, qw, sc, qz, Y, M, N, K, gs, workspace, plan, stream)
                         : launch_large_tbm<ZP, BM / 2>(X, qw, sc, qz, Y, M, N, K, gs, workspace, plan, stream);
@@ -743,7 +765,7 @@ hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales,
   const uint16_t* sc = static_cast<const uint16_t*>(scales);
   _Float16* Y = static_cast<_Float16*>(y);
   const int gs = log2_group(group_size);
-  if (M <= 64) {
+  if (M <= 64 && !gemm_uses_mid(M, N)) {
     const SkinnyPlan p = plan_skinny(M, N, K);
     switch (p.mt) {
       case 1:
@@ -760,8 +782,8 @@ hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales,
 }  // namespace
 
 size_t gemm_workspace_bytes(int M, int N, int K) {
-  if (M <= 64) return skinny_workspace_bytes(plan_skinny(M, N, K));
-  const LargePlan p = plan_large(M, N, K);
+  if (M <= 64 && !gemm_uses_mid(M, N)) return skinny_workspace_bytes(plan_skinny(M, N, K));
+  const LargePlan p = gemm_uses_mid(M, N) ? plan_mid(M, N, K) : plan_large(M, N, K);
   return p.splits > 1 ? kCounterBytes + (size_t)p.splits * M * N * 4 : 0;
 }
 

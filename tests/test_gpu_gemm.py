@@ -142,6 +142,17 @@ def test_gemm_large_launch_paths(M, N, K, g, split, what):
     check(M, N, K, g, True, what=f"{what}: M={M} N={N} K={K} g={g}")
 
 
+@pytest.mark.parametrize("M,N,K,g", [(48, 8200, 544, 32), (64, 8192, 1024, 128), (33, 16384, 256, 64)])
+def test_gemm_mid_tokens_wide_layers(M, N, K, g):
+    """33-64 tokens on layers with N >= 8192 run on the matrix-core kernel's
+    64-row tiles with K split (ragged last tile and K step in the first case);
+    every output is checked."""
+    slices = G.lib().awq_gemm_workspace_bytes(M, N, K, g) - 512 * 1024  # past the tile counters
+    assert slices > 0 and slices % (M * N * 4) == 0  # whole fp32 [M][N] partial slices
+    check(M, N, K, g, True)
+    check(M, N, K, g, False)
+
+
 @pytest.mark.parametrize("M", [96, 256, 512, 1000, 2048])
 @pytest.mark.parametrize("name,K,N", [workloads.LLAMA7B_BLOCK[0], workloads.LLAMA7B_BLOCK[4],
                                       workloads.LLAMA7B_BLOCK[6]])
