@@ -16,10 +16,12 @@
 
 #pragma clang fp contract(off)
 
+
 namespace awq {
 namespace {
 
 constexpr int kPackThreads = 256;  // 8 rows x 32 lanes
+constexpr int kPackWords = 2;      // packed words (8 channels each) per lane and pass of pack_kernel
 constexpr float kRangeFloor = 1e-5f;
 
 // Combine v over the GW consecutive lanes of a group (GW = 4, 8, 16 or 32,
@@ -60,19 +62,20 @@ struct MaxOp {
   __device__ int operator()(int a, int b) const { return a > b ? a : b; }
 };
 
-// Scale and zero point of the group a lane's 8 weights belong to.  A group of
-// g channels is GW = g/8 consecutive lanes of one row, reduced with butterfly
-// shuffles (GW divides 32, so a group never leaves its half-wave, and all
-// lanes of a group are active or inactive together).  s16 is the fp16 scale,
+// Scale and zero point of the group a lane's NV weights (one or two packed
+// words) belong to.  A group of g channels is GW = g / NV consecutive lanes of
+// one row, reduced with butterfly shuffles (GW divides 32, so a group never
+// leaves its half-wave, and all lanes of a group are active or inactive
+// together).  s16 is the fp16 scale,
 // s its fp32 value, zf the zero point as a float.
 // amax is the group's largest magnitude (a bound for every |a[c]|).
-template <int GW, bool ZP>
-__device__ __forceinline__ void group_scale_zero(const float (&a)[8], _Float16& s16, float& s, float& zf,
+template <int GW, bool ZP, int NV>
+__device__ __forceinline__ void group_scale_zero(const float (&a)[NV], _Float16& s16, float& s, float& zf,
                                                  float& amax) {
   if constexpr (ZP) {
     float mn = a[0], mx = a[0];
 #pragma unroll
-    for (int c = 1; c < 8; ++c) {
+    for (int c = 1; c < NV; ++c) {
       mn = fminf(mn, a[c]);
       mx = fmaxf(mx, a[c]);
     }
@@ -88,7 +91,7 @@ __device__ __forceinline__ void group_scale_zero(const float (&a)[8], _Float16& 
   } else {
     float m = fabsf(a[0]);
 #pragma unroll
-    for (int c = 1; c < 8; ++c) m = fmaxf(m, fabsf(a[c]));
+    for (int c = 1; c < NV; ++c) m = fmaxf(m, fabsf(a[c]));
     amax = group_all<GW>(m, MaxOp());
     const float am = amax < kRangeFloor ? kRangeFloor : amax;
     s16 = (_Float16)(am / 7.0f);
@@ -170,65 +173,86 @@ __device__ __forceinline__ void group_clip_bounds(const float (&a)[8], float r, 
 
 // One block quantizes one octet of rows (n0 .. n0+7) over one slice of K
 // (blockIdx.y: packed words [chunk_words * y, + chunk_words), a multiple of a
-// 256-channel pass, so slices end on group boundaries; several slices per row
+// 512-channel pass, so slices end on group boundaries; several slices per row
 // keep enough blocks in flight when the rows are few).  Thread t works on row
-// n0 + (t >> 5); its lane l = t & 31 owns one packed word (8 channels) of each
-// 256-channel pass over the slice, so wave w holds rows 2w (lanes 0..31) and
-// 2w + 1 (lanes 32..63).  The first lane of each group stores its row's fp16
-// scale into the octet's 16-byte scale vector, and the rows 2w and 2w + 1
-// share one byte of the octet's zero-point word (two nibbles), written by the
-// row-2w lane after one exchange: no LDS, no barriers.
+// n0 + (t >> 5); its lane l = t & 31 owns two consecutive packed words (16
+// channels, always in one group) of each 512-channel pass over the slice, so
+// wave w holds rows 2w (lanes 0..31) and 2w + 1 (lanes 32..63) and a group
+// of g channels is GW = g / 16 consecutive lanes: the group statistics and
+// the scale and zero point, computed alike by every lane of a group, are
+// shared by 16 weights per lane (with one word per lane, 9-12% slower with
+// zero points: the group reductions and the two divisions of the scale and
+// zero point are per wave instruction, whatever a lane holds).  The first lane of each group stores its
+// row's fp16 scale into the octet's 16-byte scale vector, and the rows 2w and
+// 2w + 1 share one byte of the octet's zero-point word (two nibbles), written
+// by the row-2w lane after one exchange: no LDS, no barriers.
 template <int GW, bool ZP>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restrict__ w, int N, int K,
                                                             int chunk_words, uint32_t* __restrict__ qweight,
                                                             uint16_t* __restrict__ scales,
                                                             uint32_t* __restrict__ qzeros) {
+  constexpr int WPL = kPackWords;
+  typedef uint32_t wordsT __attribute__((ext_vector_type(WPL)));
+  constexpr int kPass = 32 * WPL;   // words per row and pass
   const int t = threadIdx.x;
   const int r = t >> 5, l = t & 31;
   const int n = blockIdx.x * 8 + r;
   const int kw = K >> 3;            // packed words per row
-  const int G = kw / GW;            // groups per row
+  const int G = kw / (WPL * GW);    // groups per row
   uint16_t* soct = scales + (size_t)blockIdx.x * G * 8;
   uint8_t* zoct = reinterpret_cast<uint8_t*>(qzeros + (ZP ? (size_t)blockIdx.x * G : 0));
 
   const int j_begin = blockIdx.y * chunk_words;
-  const int j_end = min(kw, j_begin + chunk_words);
+  const int j_end = min(kw, j_begin + chunk_words);  // multiples of WPL: no lane's words straddle j_end
 
-  // kDepth passes of weights are in flight per lane: a lane streams its slice
-  // with a ring of loads kDepth passes ahead of the one it quantizes
-  constexpr int kDepth = 4;
+  // the next pass's weights are loaded while this one is quantized (deeper
+  // rings, 2-4 passes ahead, were 1-4% slower: the grid alone keeps enough
+  // loads in flight)
+  constexpr int kDepth = 1;
   const u32x4* wrow = w + (size_t)n * kw;
-  u32x4 ring[kDepth];
+  u32x4 ring[kDepth][WPL];
 #pragma unroll
   for (int u = 0; u < kDepth; ++u) {
-    const int j = j_begin + 32 * u + l;
-    ring[u] = j < j_end ? wrow[j] : u32x4{0u, 0u, 0u, 0u};
+    const int j = j_begin + kPass * u + WPL * l;
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) ring[u][i] = j < j_end ? wrow[j + i] : u32x4{0u, 0u, 0u, 0u};
   }
-  for (int w0 = j_begin; w0 < j_end; w0 += 32 * kDepth) {
+  for (int w0 = j_begin; w0 < j_end; w0 += kPass * kDepth) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
-      const int j = w0 + 32 * u + l;
-      if (j - l >= j_end) break;  // uniform: no pass left
+      if (w0 + kPass * u >= j_end) break;  // uniform: no pass left
+      const int j = w0 + kPass * u + WPL * l;
       const bool active = j < j_end;
-      const u32x4 raw = ring[u];
-      const int jn = j + 32 * kDepth;
-      ring[u] = jn < j_end ? wrow[jn] : u32x4{0u, 0u, 0u, 0u};
-      const half8_t h = as_half8(raw);
-
-      float a[8];
+      u32x4 raw[WPL];
+      const int jn = j + kPass * kDepth;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) a[c] = (float)h[c];
+      for (int i = 0; i < WPL; ++i) {
+        raw[i] = ring[u][i];
+        ring[u][i] = jn < j_end ? wrow[jn + i] : u32x4{0u, 0u, 0u, 0u};
+      }
+
+      float a[8 * WPL], aw[WPL][8];
+#pragma unroll
+      for (int i = 0; i < WPL; ++i) {
+        const half8_t h = as_half8(raw[i]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) aw[i][c] = a[8 * i + c] = (float)h[c];
+      }
 
       float s, zf, amax;
       _Float16 s16;
       group_scale_zero<GW, ZP>(a, s16, s, zf, amax);
 
-      float q[8];
-      codes_of(a, s, zf, amax, q);
-      const uint32_t word = pack_word(q);
-      if (active) qweight[(size_t)n * kw + j] = word;
+      wordsT out;
+#pragma unroll
+      for (int i = 0; i < WPL; ++i) {
+        float q[8];
+        codes_of(aw[i], s, zf, amax, q);
+        out[i] = pack_word(q);
+      }
+      if (active) *reinterpret_cast<wordsT*>(qweight + (size_t)n * kw + j) = out;
 
-      const int grp = j / GW;
+      const int grp = j / (WPL * GW);
       const bool leader = active && (l % GW) == 0;
       if (leader) soct[(size_t)grp * 8 + r] = __builtin_bit_cast(uint16_t, s16);
       if constexpr (ZP) {
@@ -449,15 +473,15 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
 template <bool ZP>
 hipError_t launch_pack_zp(const void* w, int N, int K, int group_size, uint32_t* qweight, void* scales,
                           uint32_t* qzeros, hipStream_t stream) {
-  // K is cut into slices of whole 2-pass rings (64 words, 512 channels, a
-  // multiple of every group) until the grid has about 8192 blocks: one block
-  // per row octet streams a row with too few loads in flight (243 us per
-  // Llama-7B block of 7 linears with the first quantizer, against 206-212 us
-  // with slices of 1024 channels).  With the current quantizer (150-155 us
-  // per block) 512-channel slices are 3-5% faster than 1024-channel ones;
-  // fewer slices (1024-4096 target blocks) are 5-18% slower, twice the target
-  // blocks slower at g = 256.
-  constexpr int kTargetBlocks = 8192, kRingWords = 64;
+  // K is cut into slices of whole 512-channel passes (64 words, a multiple of
+  // every group) until the grid has about 8192 blocks: one block per row
+  // octet streams a row with too few loads in flight (243 us per Llama-7B
+  // block of 7 linears with the first quantizer, against 206-212 us with
+  // slices of 1024 channels).  With one word per lane (150-155 us per block)
+  // 512-channel slices were 3-5% faster than 1024-channel ones and fewer
+  // slices (1024-4096 target blocks) 5-18% slower; with two words per lane
+  // a 4096-channel row is 8 one-pass slices.
+  constexpr int kTargetBlocks = 8192, kRingWords = 32 * kPackWords;
   const int kw = K >> 3, octets = N / 8;
   const int rings = (kw + kRingWords - 1) / kRingWords;
   int slices = (kTargetBlocks + octets - 1) / octets;
@@ -468,10 +492,10 @@ hipError_t launch_pack_zp(const void* w, int N, int K, int group_size, uint32_t*
   const u32x4* wv = static_cast<const u32x4*>(w);
   uint16_t* sc = static_cast<uint16_t*>(scales);
   switch (group_size) {
-    case 32: hipLaunchKernelGGL((pack_kernel<4, ZP>), grid, block, 0, stream, wv, N, K, chunk, qweight, sc, qzeros); break;
-    case 64: hipLaunchKernelGGL((pack_kernel<8, ZP>), grid, block, 0, stream, wv, N, K, chunk, qweight, sc, qzeros); break;
-    case 128: hipLaunchKernelGGL((pack_kernel<16, ZP>), grid, block, 0, stream, wv, N, K, chunk, qweight, sc, qzeros); break;
-    case 256: hipLaunchKernelGGL((pack_kernel<32, ZP>), grid, block, 0, stream, wv, N, K, chunk, qweight, sc, qzeros); break;
+    case 32: hipLaunchKernelGGL((pack_kernel<4 / kPackWords, ZP>), grid, block, 0, stream, wv, N, K, chunk, qweight, sc, qzeros); break;
+    case 64: hipLaunchKernelGGL((pack_kernel<8 / kPackWords, ZP>), grid, block, 0, stream, wv, N, K, chunk, qweight, sc, qzeros); break;
+    case 128: hipLaunchKernelGGL((pack_kernel<16 / kPackWords, ZP>), grid, block, 0, stream, wv, N, K, chunk, qweight, sc, qzeros); break;
+    case 256: hipLaunchKernelGGL((pack_kernel<32 / kPackWords, ZP>), grid, block, 0, stream, wv, N, K, chunk, qweight, sc, qzeros); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
