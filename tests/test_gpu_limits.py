@@ -61,7 +61,7 @@ def test_max_n_pack_gemv_gemm():
     cols = (cols[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
     cols = np.concatenate([cols, np.arange(N - 8, N)])  # the last octet
     wdq = O.dequant_packed(oq[cols], os_[cols[::8] // 8], oz[cols[::8] // 8], len(cols), K, g, True)
-    for M, fn in ((1, "gemv"), (5, "gemm"), (300, "gemm")):
+    for M, fn in ((1, "gemv"), (5, "gemm"), (48, "gemm"), (300, "gemm")):
         X = workloads.activations(M, K, cfg=8, layer=M + 1)
         y = G.host_f16((awq.awq_gemv if fn == "gemv" else awq.awq_gemm)(G.dev_f16(X), qw, sc, qz, N, K, g, True))
         rows = np.arange(M) if M < 8 else np.sort(np.random.default_rng(M).choice(M, 8, replace=False))
