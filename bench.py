@@ -139,7 +139,7 @@ def per_layer_launch_times(torch, awq, layers, reps, g, zp, replays=20):
 
 def hbm_traffic(step_launches):
     """Measured HBM bytes per GEMV launch from the committed counter summary,
-    if it was taken on the current kernel source; else None."""
+    if it was taken on the current kernel source and build flags; else None."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "gemv_llama7b_decode_traffic.txt")
@@ -157,7 +157,7 @@ def hbm_traffic(step_launches):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     if h.hexdigest() != rec["sources_sha256"]:
-        return None, "kernel source changed since the counters were taken"
+        return None, "kernel source or build flags changed since the counters were taken"
     return int(rec["hbm_bytes_per_launch"]), rec["note"]
 
 
