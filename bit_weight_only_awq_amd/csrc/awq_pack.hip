@@ -148,12 +148,12 @@ __device__ __forceinline__ uint32_t pack_word(const float (&q)[8]) {
 // Range of the group a lane's 8 weights belong to, shrunk by `r` (weight
 // clipping): [r * min, r * max] with a zero point, [-r * amax, r * amax]
 // without (fp32 products).
-template <int GW, bool ZP>
-__device__ __forceinline__ void group_clip_bounds(const float (&a)[8], float r, float& lo, float& hi) {
+template <int GW, bool ZP, int NV>
+__device__ __forceinline__ void group_clip_bounds(const float (&a)[NV], float r, float& lo, float& hi) {
   if constexpr (ZP) {
     float mn = a[0], mx = a[0];
 #pragma unroll
-    for (int c = 1; c < 8; ++c) {
+    for (int c = 1; c < NV; ++c) {
       mn = fminf(mn, a[c]);
       mx = fmaxf(mx, a[c]);
     }
@@ -164,7 +164,7 @@ __device__ __forceinline__ void group_clip_bounds(const float (&a)[8], float r, 
   } else {
     float amax = fabsf(a[0]);
 #pragma unroll
-    for (int c = 1; c < 8; ++c) amax = fmaxf(amax, fabsf(a[c]));
+    for (int c = 1; c < NV; ++c) amax = fmaxf(amax, fabsf(a[c]));
     amax = group_all<GW>(amax, MaxOp());
     hi = r * amax;
     lo = -hi;
@@ -279,6 +279,7 @@ template <int GW, bool ZP>
 __global__ __launch_bounds__(kPackThreads) void scale_error_kernel(const u32x4* __restrict__ w,
                                                                    const float* __restrict__ s_all, int N, int K,
                                                                    u32x4* __restrict__ e_all) {
+  constexpr int WPL = kPackWords;  // lane l of a row owns words 2l, 2l + 1 of each 64-word pass
   const int t = threadIdx.x;
   const int r = t >> 5, l = t & 31;
   const int n = blockIdx.x * 8 + r;
@@ -288,50 +289,57 @@ __global__ __launch_bounds__(kPackThreads) void scale_error_kernel(const u32x4* 
 
   // the next pass's weights and scales are loaded while this pass is processed
   const u32x4* wrow = w + (size_t)n * kw;
-  u32x4 nraw = {0u, 0u, 0u, 0u};
-  float4_t ns0 = {1.f, 1.f, 1.f, 1.f}, ns1 = {1.f, 1.f, 1.f, 1.f};
+  u32x4 nraw[WPL];
+  float4_t ns[2 * WPL];
   auto fetch = [&](int j) {
-    nraw = u32x4{0u, 0u, 0u, 0u};
-    ns0 = float4_t{1.f, 1.f, 1.f, 1.f};
-    ns1 = ns0;
-    if (j < kw) {
-      nraw = wrow[j];
-      ns0 = *reinterpret_cast<const float4_t*>(sc + 8 * j);
-      ns1 = *reinterpret_cast<const float4_t*>(sc + 8 * j + 4);
-    }
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) nraw[i] = j < kw ? wrow[j + i] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 2 * WPL; ++i)
+      ns[i] = j < kw ? *reinterpret_cast<const float4_t*>(sc + 8 * j + 4 * i) : float4_t{1.f, 1.f, 1.f, 1.f};
   };
-  fetch(l);
-  for (int w0 = 0; w0 < kw; w0 += 32) {
-    const int j = w0 + l;
+  fetch(WPL * l);
+  for (int w0 = 0; w0 < kw; w0 += 32 * WPL) {
+    const int j = w0 + WPL * l;  // kw is a multiple of 4: a lane's words are all in or all out
     const bool active = j < kw;
-    const u32x4 raw = nraw;
-    const float4_t s0 = ns0, s1 = ns1;
-    fetch(j + 32);
-    const half8_t h = as_half8(raw);
-    float sv[8];
+    u32x4 raw[WPL];
+    float sv[8 * WPL];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      sv[c] = s0[c];
-      sv[c + 4] = s1[c];
+    for (int i = 0; i < WPL; ++i) raw[i] = nraw[i];
+#pragma unroll
+    for (int i = 0; i < 2 * WPL; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sv[4 * i + c] = ns[i][c];
+    fetch(j + 32 * WPL);
+    float hv[8 * WPL], a[8 * WPL];
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) {
+      const half8_t h = as_half8(raw[i]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) hv[8 * i + c] = (float)h[c];
     }
-    float a[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) a[c] = (float)(_Float16)((float)h[c] * sv[c]);
+    for (int c = 0; c < 8 * WPL; ++c) a[c] = (float)(_Float16)(hv[c] * sv[c]);
 
     float s, zf, amax;
     _Float16 s16;
     group_scale_zero<GW, ZP>(a, s16, s, zf, amax);
 
     // e only needs fp16 accuracy: w' / s by a reciprocal (1 ulp in fp32)
-    float q[8];
-    codes_of(a, s, zf, amax, q);
-    half8_t out;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float wq = (q[c] - zf) * s;
-      out[c] = (_Float16)(wq * __builtin_amdgcn_rcpf(sv[c]) - (float)h[c]);
+    for (int i = 0; i < WPL; ++i) {
+      float ai[8], q[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ai[c] = a[8 * i + c];
+      codes_of(ai, s, zf, amax, q);
+      half8_t out;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float wq = (q[c] - zf) * s;
+        out[c] = (_Float16)(wq * __builtin_amdgcn_rcpf(sv[8 * i + c]) - hv[8 * i + c]);
+      }
+      if (active) e[(size_t)n * kw + j + i] = __builtin_bit_cast(u32x4, out);
     }
-    if (active) e[(size_t)n * kw + j] = __builtin_bit_cast(u32x4, out);
   }
 }
 
@@ -344,6 +352,7 @@ __global__ __launch_bounds__(kPackThreads) void scale_error_kernel(const u32x4* 
 template <int GW, bool ZP>
 __global__ __launch_bounds__(kPackThreads) void clip_error_kernel(const u32x4* __restrict__ w, ClipRatios ratios,
                                                                   int N, int K, u32x4* __restrict__ e_all) {
+  constexpr int WPL = kPackWords;  // lane l of a row owns words 2l, 2l + 1 of each 64-word pass
   const int t = threadIdx.x;
   const int r = t >> 5, l = t & 31;
   const int n = blockIdx.x * 8 + r;
@@ -351,32 +360,40 @@ __global__ __launch_bounds__(kPackThreads) void clip_error_kernel(const u32x4* _
   const float ratio = ratios.v[blockIdx.y];
   u32x4* e = e_all + (size_t)blockIdx.y * N * kw;
   const u32x4* wrow = w + (size_t)n * kw;
-  u32x4 next = {0u, 0u, 0u, 0u};
-  if (l < kw) next = wrow[l];
-  for (int w0 = 0; w0 < kw; w0 += 32) {
-    const int j = w0 + l;
-    const bool active = j < kw;
-    const u32x4 raw = next;
-    next = u32x4{0u, 0u, 0u, 0u};
-    if (j + 32 < kw) next = wrow[j + 32];
-    const half8_t h = as_half8(raw);
-    float a[8];
+  u32x4 next[WPL];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) a[c] = (float)h[c];
+  for (int i = 0; i < WPL; ++i) next[i] = WPL * l < kw ? wrow[WPL * l + i] : u32x4{0u, 0u, 0u, 0u};
+  for (int w0 = 0; w0 < kw; w0 += 32 * WPL) {
+    const int j = w0 + WPL * l;  // kw is a multiple of 4: a lane's words are all in or all out
+    const bool active = j < kw;
+    const int jn = j + 32 * WPL;
+    float a[8 * WPL];
+#pragma unroll
+    for (int i = 0; i < WPL; ++i) {
+      const half8_t h = as_half8(next[i]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) a[8 * i + c] = (float)h[c];
+      next[i] = jn < kw ? wrow[jn + i] : u32x4{0u, 0u, 0u, 0u};
+    }
     float lo, hi;
     group_clip_bounds<GW, ZP>(a, ratio, lo, hi);
-    float cl[8];
+    float cl[8 * WPL];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) cl[c] = (float)(_Float16)fminf(fmaxf(a[c], lo), hi);
+    for (int c = 0; c < 8 * WPL; ++c) cl[c] = (float)(_Float16)fminf(fmaxf(a[c], lo), hi);
     float s, zf, amax;
     _Float16 s16;
     group_scale_zero<GW, ZP>(cl, s16, s, zf, amax);
-    float q[8];
-    codes_of(cl, s, zf, amax, q);
-    half8_t out;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) out[c] = (_Float16)((q[c] - zf) * s - a[c]);
-    if (active) e[(size_t)n * kw + j] = __builtin_bit_cast(u32x4, out);
+    for (int i = 0; i < WPL; ++i) {
+      float ci[8], q[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ci[c] = cl[8 * i + c];
+      codes_of(ci, s, zf, amax, q);
+      half8_t out;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) out[c] = (_Float16)((q[c] - zf) * s - a[8 * i + c]);
+      if (active) e[(size_t)n * kw + j + i] = __builtin_bit_cast(u32x4, out);
+    }
   }
 }
 
@@ -510,10 +527,10 @@ hipError_t launch_scale_error_zp(const void* w, const float* s, int count, int N
   const u32x4* wv = static_cast<const u32x4*>(w);
   u32x4* ev = static_cast<u32x4*>(e);
   switch (group_size) {
-    case 32: hipLaunchKernelGGL((scale_error_kernel<4, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
-    case 64: hipLaunchKernelGGL((scale_error_kernel<8, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
-    case 128: hipLaunchKernelGGL((scale_error_kernel<16, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
-    case 256: hipLaunchKernelGGL((scale_error_kernel<32, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
+    case 32: hipLaunchKernelGGL((scale_error_kernel<4 / kPackWords, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
+    case 64: hipLaunchKernelGGL((scale_error_kernel<8 / kPackWords, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
+    case 128: hipLaunchKernelGGL((scale_error_kernel<16 / kPackWords, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
+    case 256: hipLaunchKernelGGL((scale_error_kernel<32 / kPackWords, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -527,7 +544,8 @@ hipError_t launch_clip_zp(const void* w, const ClipRatios& ratios, int count, in
 #define AWQ_CLIP_CASE(G_, GW_)                                                                                   \
   case G_:                                                                                                     \
     if (!apply)                                                                                                \
-      hipLaunchKernelGGL((clip_error_kernel<GW_, ZP>), dim3(N / 8, count), block, 0, stream, wv, ratios, N, K,   \
+      hipLaunchKernelGGL((clip_error_kernel<GW_ / kPackWords, ZP>), dim3(N / 8, count), block, 0, stream, wv,     \
+                         ratios, N, K,                                                                         \
                          static_cast<u32x4*>(e));                                                              \
     else                                                                                                       \
       hipLaunchKernelGGL((clip_apply_kernel<GW_, ZP>), dim3(N / 8), block, 0, stream, wv, part, parts, N, K,     \
