@@ -491,14 +491,14 @@ template <bool ZP>
 hipError_t launch_pack_zp(const void* w, int N, int K, int group_size, uint32_t* qweight, void* scales,
                           uint32_t* qzeros, hipStream_t stream) {
   // K is cut into slices of whole 512-channel passes (64 words, a multiple of
-  // every group) until the grid has about 8192 blocks: one block per row
-  // octet streams a row with too few loads in flight (243 us per Llama-7B
-  // block of 7 linears with the first quantizer, against 206-212 us with
-  // slices of 1024 channels).  With one word per lane (150-155 us per block)
-  // 512-channel slices were 3-5% faster than 1024-channel ones and fewer
-  // slices (1024-4096 target blocks) 5-18% slower; with two words per lane
-  // a 4096-channel row is 8 one-pass slices.
-  constexpr int kTargetBlocks = 8192, kRingWords = 32 * kPackWords;
+  // every group) until the grid has about 16384 blocks, which on the Llama-7B
+  // layers makes every slice a single pass: one block per row octet streams
+  // a row with too few loads in flight (243 us per Llama-7B block of 7
+  // linears with the first quantizer, against 206-212 us with slices of 1024
+  // channels).  With two words per lane, 16384 target blocks are 3-6% faster
+  // than 8192 (a 4096-row layer then already has one-pass slices, the
+  // 11008-row ones had two) and 2048 are 7% slower.
+  constexpr int kTargetBlocks = 16384, kRingWords = 32 * kPackWords;
   const int kw = K >> 3, octets = N / 8;
   const int rings = (kw + kRingWords - 1) / kRingWords;
   int slices = (kTargetBlocks + octets - 1) / octets;
