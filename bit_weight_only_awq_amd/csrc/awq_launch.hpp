@@ -50,7 +50,8 @@ struct ClipRatios {
 // e[c][n][k] = fp16(Dq(Q(clip_c(w)))[n][k] - w[n][k]) for each ratio c.
 hipError_t launch_clip_error(const void* w, const ClipRatios& ratios, int count, int N, int K, int group_size,
                              bool zero_point, void* e, hipStream_t stream);
-// Per group: the ratio with the smallest summed partial error; clipped weights to w_out.
+// Per group: the ratio with the smallest summed partial error to choice[n][j]
+// (device, [N][K / group_size], always written), then the clipped weights to w_out.
 hipError_t launch_clip_apply(const void* w, const float* part, int parts, const ClipRatios& ratios, int count, int N,
                              int K, int group_size, bool zero_point, void* w_out, int32_t* choice, hipStream_t stream);
 // Clip search: errors of every ratio, then choice and clipped weights.

@@ -397,17 +397,36 @@ __global__ __launch_bounds__(kPackThreads) void clip_error_kernel(const u32x4* _
   }
 }
 
-// Chooses each group's clipping ratio and writes the clipped weights.  The
-// error of group (n, j) under ratio c is the sum, in a fixed order, of the
-// per-tile partials part[c][tm][h][j][n] (tile rows tm, half h of a tile's
-// rows); the group keeps the first ratio with the smallest error, is clamped
-// to its range shrunk by that ratio, and `choice[n][j]` (if given) records it.
+// The clipping ratio of each weight group (n, j): the error of the group under
+// ratio c is the sum, in a fixed order (fp64), of the per-tile partials
+// part[c][tm][h][j][n] (tile rows tm, half h of a tile's rows), and the group
+// keeps the first ratio with the smallest error.  One thread per group,
+// consecutive threads on consecutive rows n, so the partial reads coalesce.
+__global__ __launch_bounds__(256) void clip_choose_kernel(const float* __restrict__ part, int parts, int G, int N,
+                                                          int count, int32_t* __restrict__ choice) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)G * N) return;
+  const int grp = (int)(idx / N), n = (int)(idx - (size_t)grp * N);
+  double best_v = __builtin_huge_val();
+  int best = 0;
+  for (int c = 0; c < count; ++c) {
+    double v = 0.0;
+    for (int p = 0; p < parts; ++p) v += (double)part[(((size_t)c * parts + p) * G + grp) * N + n];
+    if (v < best_v) {
+      best_v = v;
+      best = c;
+    }
+  }
+  choice[(size_t)n * G + grp] = best;
+}
+
+// Writes the clipped weights: every group clamped to its range shrunk by its
+// chosen ratio choice[n][j].
 template <int GW, bool ZP>
-__global__ __launch_bounds__(kPackThreads) void clip_apply_kernel(const u32x4* __restrict__ w,
-                                                                  const float* __restrict__ part, int parts, int N,
-                                                                  int K, ClipRatios ratios, int count,
-                                                                  u32x4* __restrict__ w_out,
-                                                                  int32_t* __restrict__ choice) {
+__global__ __launch_bounds__(kPackThreads) void clip_apply_kernel(const u32x4* __restrict__ w, int N, int K,
+                                                                  ClipRatios ratios,
+                                                                  const int32_t* __restrict__ choice,
+                                                                  u32x4* __restrict__ w_out) {
   const int t = threadIdx.x;
   const int r = t >> 5, l = t & 31;
   const int n = blockIdx.x * 8 + r;
@@ -416,33 +435,8 @@ __global__ __launch_bounds__(kPackThreads) void clip_apply_kernel(const u32x4* _
   for (int w0 = 0; w0 < kw; w0 += 32) {
     const int j = w0 + l;
     const bool active = j < kw;
-    const int grp = j / GW, gl = l % GW;
-    // lane gl of the group sums the partials of ratios gl, gl + GW, ... (each
-    // in a fixed order); the group then takes the smallest error, the lowest
-    // ratio index among equal ones
-    double best_v = __builtin_huge_val();
-    int best = 0x7fffffff;
-    if (active) {
-      for (int c = gl; c < count; c += GW) {
-        double v = 0.0;
-        for (int p = 0; p < parts; ++p) v += (double)part[(((size_t)c * parts + p) * G + grp) * N + n];
-        if (v < best_v) {
-          best_v = v;
-          best = c;
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 1; off < GW; off <<= 1) {
-      const double ov = __shfl_xor(best_v, off);
-      const int oi = __shfl_xor(best, off);
-      if (ov < best_v || (ov == best_v && oi < best)) {
-        best_v = ov;
-        best = oi;
-      }
-    }
-    if (!active) best = 0;
-    if (active && gl == 0 && choice) choice[(size_t)n * G + grp] = best;
+    const int grp = j / GW;
+    const int best = active ? choice[(size_t)n * G + grp] : 0;
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (active) raw = w[(size_t)n * kw + j];
     const half8_t h = as_half8(raw);
@@ -538,7 +532,7 @@ hipError_t launch_scale_error_zp(const void* w, const float* s, int count, int N
 
 template <bool ZP>
 hipError_t launch_clip_zp(const void* w, const ClipRatios& ratios, int count, int N, int K, int group_size, void* e,
-                          const float* part, int parts, void* w_out, int32_t* choice, bool apply, hipStream_t stream) {
+                          const int32_t* choice, void* w_out, bool apply, hipStream_t stream) {
   const u32x4* wv = static_cast<const u32x4*>(w);
   const dim3 block(kPackThreads);
 #define AWQ_CLIP_CASE(G_, GW_)                                                                                   \
@@ -548,8 +542,8 @@ hipError_t launch_clip_zp(const void* w, const ClipRatios& ratios, int count, in
                          ratios, N, K,                                                                         \
                          static_cast<u32x4*>(e));                                                              \
     else                                                                                                       \
-      hipLaunchKernelGGL((clip_apply_kernel<GW_, ZP>), dim3(N / 8), block, 0, stream, wv, part, parts, N, K,     \
-                         ratios, count, static_cast<u32x4*>(w_out), choice);                                   \
+      hipLaunchKernelGGL((clip_apply_kernel<GW_, ZP>), dim3(N / 8), block, 0, stream, wv, N, K, ratios, choice,  \
+                         static_cast<u32x4*>(w_out));                                                          \
     break;
   switch (group_size) {
     AWQ_CLIP_CASE(32, 4)
@@ -566,18 +560,20 @@ hipError_t launch_clip_zp(const void* w, const ClipRatios& ratios, int count, in
 
 hipError_t launch_clip_error(const void* w, const ClipRatios& ratios, int count, int N, int K, int group_size,
                              bool zero_point, void* e, hipStream_t stream) {
-  return zero_point ? launch_clip_zp<true>(w, ratios, count, N, K, group_size, e, nullptr, 0, nullptr, nullptr, false,
-                                           stream)
-                    : launch_clip_zp<false>(w, ratios, count, N, K, group_size, e, nullptr, 0, nullptr, nullptr, false,
-                                            stream);
+  return zero_point ? launch_clip_zp<true>(w, ratios, count, N, K, group_size, e, nullptr, nullptr, false, stream)
+                    : launch_clip_zp<false>(w, ratios, count, N, K, group_size, e, nullptr, nullptr, false, stream);
 }
 
 hipError_t launch_clip_apply(const void* w, const float* part, int parts, const ClipRatios& ratios, int count, int N,
                              int K, int group_size, bool zero_point, void* w_out, int32_t* choice, hipStream_t stream) {
-  return zero_point ? launch_clip_zp<true>(w, ratios, count, N, K, group_size, nullptr, part, parts, w_out, choice,
-                                           true, stream)
-                    : launch_clip_zp<false>(w, ratios, count, N, K, group_size, nullptr, part, parts, w_out, choice,
-                                            true, stream);
+  const int G = K / group_size;
+  const size_t groups = (size_t)G * N;
+  hipLaunchKernelGGL(clip_choose_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream, part, parts, G,
+                     N, count, choice);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return zero_point ? launch_clip_zp<true>(w, ratios, count, N, K, group_size, nullptr, choice, w_out, true, stream)
+                    : launch_clip_zp<false>(w, ratios, count, N, K, group_size, nullptr, choice, w_out, true, stream);
 }
 
 hipError_t launch_scale_error(const void* w, const float* s, int count, int N, int K, int group_size, bool zero_point,

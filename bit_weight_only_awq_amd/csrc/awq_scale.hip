@@ -383,7 +383,10 @@ hipError_t launch_clip_search(const void* x, const void* w, int M, int N, int K,
   err = launch_sumsq(static_cast<const _Float16*>(x), e, M, N, K, T, tiles_m, dim3(tiles_m * tiles_n, count), nullptr,
                      log2_group(group_size), gpart, true, stream);
   if (err != hipSuccess) return err;
-  return launch_clip_apply(w, gpart, tiles_m * 2, r, count, N, K, group_size, zero_point, w_out, choice, stream);
+  // without a caller's choice buffer the choices go to the start of the
+  // workspace: the weight errors there are dead once the product has run
+  int32_t* ch = choice ? choice : reinterpret_cast<int32_t*>(ws);
+  return launch_clip_apply(w, gpart, tiles_m * 2, r, count, N, K, group_size, zero_point, w_out, ch, stream);
 }
 
 }  // namespace awq
