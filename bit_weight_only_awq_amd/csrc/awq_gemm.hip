@@ -19,10 +19,12 @@
 //     (deterministic, one launch).
 //
 //   * gemm_large_kernel (M > 64, and 33-64 tokens on layers with N >= 8192
-//     on 64-row tiles): matrix-core bound.  256 x 256 output tile
-//     (or 256 x 128 for the last wave of tiles) per workgroup of 4 waves, one
-//     per SIMD, each 256 x 64 (v_mfma_f32_32x32x16_f16, accumulators in the
-//     AGPRs), K in steps of 64.  X tiles go from HBM straight into LDS
+//     on 64-row tiles): matrix-core bound.  TBM x 256 output tile per
+//     workgroup of 4 waves, one per SIMD, each TBM x 64
+//     (v_mfma_f32_32x32x16_f16, accumulators in the AGPRs), K in steps of 64;
+//     TBM = 256, or 128 / 64 where 256-row tiles are too few to fill the chip
+//     (then with K split across workgroups and a reduction launch), and
+//     TBM x 128 tiles for a last wave of tiles that would run half empty.  X tiles go from HBM straight into LDS
 //     (buffer-to-LDS loads); packed weights are fetched two steps ahead into
 //     registers and decoded once per workgroup straight into MFMA B operands
 //     (no LDS on the weight path); the K loop is software-pipelined by hand.
