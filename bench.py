@@ -602,8 +602,9 @@ def cpu_baseline(layers, g, zp, min_seconds=10.0, max_passes=40):
 
 def summarize(db_paths, name_filter=None):
     """Per-kernel summary of rocprofv3 SQLite databases (kernel-trace and/or
-    --pmc runs): dispatch count, duration statistics and, when present, the
-    per-dispatch average of each collected counter.  Prints text."""
+    --pmc runs): dispatch count, duration statistics (mean, median, minimum,
+    10th and 90th percentiles) and, when present, the per-dispatch average of
+    each collected counter.  Prints text."""
     import sqlite3
     import statistics
 
@@ -625,10 +626,12 @@ def summarize(db_paths, name_filter=None):
         except sqlite3.Error:
             pass
         for (name, grid, wg), ds in sorted(by.items(), key=lambda kv: -sum(d for _, d in kv[1])):
-            durs = [d for _, d in ds]
+            durs = sorted(d for _, d in ds)
+            p10 = durs[int(0.1 * (len(durs) - 1))]
+            p90 = durs[int(0.9 * (len(durs) - 1))]
             line = (f"{name[:90]:90s} grid={grid:8d} wg={wg:4d} n={len(durs):5d} "
                     f"avg_us={statistics.mean(durs) / 1e3:9.3f} med_us={statistics.median(durs) / 1e3:9.3f} "
-                    f"min_us={min(durs) / 1e3:9.3f}")
+                    f"min_us={durs[0] / 1e3:9.3f} p10_us={p10 / 1e3:9.3f} p90_us={p90 / 1e3:9.3f}")
             cnt = {}
             for kid, _ in ds:
                 for c, v in pmc.get(kid, {}).items():
