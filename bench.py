@@ -20,13 +20,15 @@ legs   = awq_pack, fused-projection decode (qkv and gate_up as one awq_gemv
          single-token GEMV on the 70B MLP shapes (layers large enough that
          the launch floor no longer dominates); for context, torch's dense
          fp16 products on the unquantized weights (decode M = 1/4/16/64 and
-         the prefill shapes) with the W4A16 speedup over them.
+         the prefill shapes) with the W4A16 speedup over them, and measured
+         HBM ceilings (torch's 1 GiB copy and 1 GiB fp16 sum).
 cpu_baseline = the CPU oracle (decode + fp64 product) on one block, timed on
          the host; a reported reference, not a target.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--blocks 32]
                        [--legs all|none|<comma list>] [--no-cpu-baseline]
-       python bench.py --leg-only pack|fused|batched|dense|prefill|scale|clip|sweep|gemv70b|power   (one leg, for profiling)
+       python bench.py --leg-only pack|fused|batched|dense|prefill|scale|clip|sweep|gemv70b|power|ceiling
+                       (one leg, for profiling)
        python bench.py --copy-calibration | --summarize DB... [--kernel-filter NAME]
 """
 from __future__ import annotations
@@ -66,7 +68,8 @@ def parse():
     ap.add_argument("--summarize", nargs="+", metavar="DB",
                     help="print a per-kernel summary of rocprofv3 result databases and exit")
     ap.add_argument("--kernel-filter", default=None, help="with --summarize: only kernels whose name contains this")
-    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "dense", "prefill", "scale", "clip", "sweep", "gemv70b", "power"],
+    ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "dense", "prefill", "scale", "clip", "sweep", "gemv70b", "power",
+                             "ceiling"],
                     help="run just this leg (no headline, no CPU baseline) and print its JSON; for profiling")
     return ap.parse_args()
 
@@ -533,6 +536,30 @@ def _smi_sample():
     return out
 
 
+def leg_ceiling(torch, iters=20):
+    """Measured HBM ceilings, for context only (never a roofline denominator):
+    torch's device copy of 1 GiB (1 GiB read + 1 GiB written) and torch's sum
+    over 1 GiB of fp16 (1 GiB read), each as GB/s of HBM bytes moved."""
+    n = 1 << 30
+    src = torch.empty(n // 2, dtype=torch.float16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, nbytes in (("copy_1GiB", lambda: dst.copy_(src), 2 * n), ("sum_1GiB_fp16", lambda: src.sum(), n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        tm.start()
+        for _ in range(iters):
+            fn()
+        ms = tm.stop_ms() / iters
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"us": round(ms * 1e3, 1), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 3)}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def leg_power(torch, awq, workloads, g=128, zp=True, seconds=2.0):
     """Power and clock of the prefill GEMM (70B down_proj, M = 2048) under
     sustained load, with the synthetic activations and with all-zero ones
@@ -674,7 +701,8 @@ def main():
         return 0
 
     g, zp = 128, True
-    if args.leg_only in ("fused", "batched", "dense", "prefill", "scale", "clip", "sweep", "gemv70b", "power"):
+    if args.leg_only in ("fused", "batched", "dense", "prefill", "scale", "clip", "sweep", "gemv70b", "power",
+                         "ceiling"):
         fn = {"fused": lambda: leg_fused_decode(torch, awq, workloads, g, zp, blocks=args.blocks),
               "batched": lambda: leg_batched_decode(torch, awq, workloads, g, zp),
               "dense": lambda: leg_dense_decode(torch, workloads),
@@ -683,7 +711,8 @@ def main():
               "clip": lambda: leg_clip_search(torch, awq, workloads, g, zp),
               "sweep": lambda: leg_sweep(torch, awq, workloads),
               "gemv70b": lambda: leg_gemv_70b(torch, awq, workloads, g, zp),
-              "power": lambda: leg_power(torch, awq, workloads, g, zp)}[args.leg_only]
+              "power": lambda: leg_power(torch, awq, workloads, g, zp),
+              "ceiling": lambda: leg_ceiling(torch)}[args.leg_only]
         print(json.dumps({"leg": args.leg_only, "result": fn()}), flush=True)
         return 0
     log(f"building {args.blocks} decode blocks")
@@ -760,7 +789,8 @@ def main():
     }
 
     legs = set(args.legs.split(",")) if args.legs not in ("all", "none") else (
-        {"pack", "fused", "batched", "dense", "prefill", "scale", "clip", "sweep", "gemv70b"} if args.legs == "all" else set())
+        {"pack", "fused", "batched", "dense", "prefill", "scale", "clip", "sweep", "gemv70b", "ceiling"}
+        if args.legs == "all" else set())
     out_legs = {}
     if args.leg_only == "pack":
         print(json.dumps({"leg": "pack", "result": leg_pack(torch, awq, layers, g, zp)}), flush=True)
@@ -800,6 +830,9 @@ def main():
     if "gemv70b" in legs:
         log("leg: GEMV on the 70B MLP shapes")
         out_legs["gemv_70b_mlp"] = leg_gemv_70b(torch, awq, workloads, g, zp)
+    if "ceiling" in legs:
+        log("leg: HBM ceilings (torch copy and sum, context)")
+        out_legs["hbm_ceiling_context"] = leg_ceiling(torch)
     if out_legs:
         result["legs"] = out_legs
     if not args.no_cpu_baseline:
