@@ -126,10 +126,14 @@ __global__ __launch_bounds__(WM * WN * 64) void sumsq_gemm_kernel(const _Float16
   __shared__ __attribute__((aligned(1024))) char lx0[OP], lx1[OP], le0[OP], le1[OP];
   __shared__ double wsum[NW];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int tile = blockIdx.x;
+  // (tile, candidate) from the workgroup's place in an XCD-contiguous order:
+  // the row tiles of one column band of a candidate's E run on one XCD and
+  // share its L2, so E is fetched once per XCD rather than once per row tile
+  const int lin = xcd_contiguous_tile(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
+  const int tile = lin % gridDim.x, cand = lin / gridDim.x;
   const int tm = tile % tiles_m, tn = tile / tiles_m;
   const int m0 = tm * T, n0 = tn * T;
-  const _Float16* E = E_all + (size_t)blockIdx.y * N * K;
+  const _Float16* E = E_all + (size_t)cand * N * K;
   const int rows_m = min(T, M - m0), rows_n = min(T, N - n0);
   const int nsteps = (K + TK - 1) / TK;
 
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(WM * WN * 64) void sumsq_gemm_kernel(const _Float16
 
   // per-group flush (GROUPED): squares per column over this wave's rows
   const int G = K >> gshift;
-  float* gout = GROUPED ? gpart + (((size_t)blockIdx.y * tiles_m + tm) * WM + (wave % WM)) * G * N : nullptr;
+  float* gout = GROUPED ? gpart + (((size_t)cand * tiles_m + tm) * WM + (wave % WM)) * G * N : nullptr;
   auto flush = [&](int grp) {
 #pragma unroll
     for (int b = 0; b < AN; ++b) {
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(WM * WN * 64) void sumsq_gemm_kernel(const _Float16
     double v = wsum[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) v += wsum[w];
-    partial[(size_t)blockIdx.y * gridDim.x + tile] = v;
+    partial[(size_t)cand * gridDim.x + tile] = v;
   }
 }
 
