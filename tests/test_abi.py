@@ -49,7 +49,8 @@ def test_gemm_launch_plans_through_workspace_sizes(lib):
     4096 x 4096 layer, up to 8 tokens run as 16-row tiles without a K split
     (no workspace); 16 and 64 tokens split K across workgroups (512 KiB of
     counters plus fp32 partial tiles), 33-64 tokens on layers with N >= 8192
-    run on the matrix-core kernel's 64-row tiles; the matrix-core kernel splits K only
+    and 49-64 tokens on layers with K >= 8192 run on the matrix-core kernel's
+    64-row tiles; the matrix-core kernel splits K only
     while its tiles (256 or 128 rows x 256) are too few for the compute units:
     on 4096 x 4096 up to M = 1024, not at M = 2048 (256 tiles of 128 rows) nor
     on the 70B MLP shapes at M = 2048 (896 and 256 tiles of 256 rows)."""
@@ -66,6 +67,10 @@ def test_gemm_launch_plans_through_workspace_sizes(lib):
         assert need > counters and (need - counters) % (M * 11008 * 4) == 0, M
     need = ws(32, 11008, 4096, 128)
     assert (need - counters) % (16 * 16 * 4) == 0  # 32 tokens: still the skinny kernel's partial tiles
+    # 49-64 tokens on layers with K >= 8192 (11008 -> 4096) take the 64-row tiles too
+    for M in (49, 64):
+        need = ws(M, 4096, 11008, 128)
+        assert need > counters and (need - counters) % (M * 4096 * 4) == 0, M
     for M in (96, 256, 512, 1024):
         need = ws(M, 4096, 4096, 128)
         assert need > counters and (need - counters) % (M * 4096 * 4) == 0, M  # whole [splits][M][N] fp32 slices
