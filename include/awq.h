@@ -119,8 +119,8 @@ int awq_gemv(const void* x, const uint32_t* qweight, const void* scales, const u
  * workspace: device scratch of at least awq_gemm_workspace_bytes(M, N, K,
  * group_size) bytes, 16-byte aligned, owned by the caller (may be NULL when
  * that size is 0).  For small M (<= 64, except 33-64 tokens on layers with
- * N >= 8192, which take the matrix-core path below) the K dimension is split
- * across workgroups: the workspace then starts with a 512 KiB region of 32-bit
+ * N >= 8192 and 49-64 tokens on layers with K >= 8192, which take the
+ * matrix-core path below) the K dimension is split across workgroups: the workspace then starts with a 512 KiB region of 32-bit
  * per-tile counters, followed by fp32 partial tiles, and the last workgroup
  * of a tile to finish adds the partials in a fixed order (the result does not
  * depend on which one finishes last).  The counter region must be ZERO when
@@ -128,8 +128,8 @@ int awq_gemv(const void* x, const uint32_t* qweight, const void* scales, const u
  * it to zero, so one buffer serves any number of calls of any shape in
  * stream order.  Calls that may run concurrently (different streams) need
  * separate workspaces.  For larger M with few output tiles (M up to about a
- * thousand on 4096-wide layers, and 33-64 tokens on layers with N >= 8192),
- * K is split as well: fp32 partial products [slices][M][N] follow the
+ * thousand on 4096-wide layers, and the 33-64 token cases above), K is
+ * split as well: fp32 partial products [slices][M][N] follow the
  * counter region and a second kernel adds them in a fixed order.
  */
 int awq_gemm(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros,
