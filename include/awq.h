@@ -120,8 +120,9 @@ int awq_gemv(const void* x, const uint32_t* qweight, const void* scales, const u
  * group_size) bytes, 16-byte aligned, owned by the caller (may be NULL when
  * that size is 0).  For small M (<= 64, except 33-64 tokens on layers with
  * N >= 8192 and 49-64 tokens on layers with K >= 8192, which take the
- * matrix-core path below) the K dimension is split across workgroups: the workspace then starts with a 512 KiB region of 32-bit
- * per-tile counters, followed by fp32 partial tiles, and the last workgroup
+ * matrix-core path below) the K dimension is split across workgroups: the
+ * workspace then starts with a 512 KiB region of 32-bit per-tile counters,
+ * followed by fp32 partial tiles, and the last workgroup
  * of a tile to finish adds the partials in a fixed order (the result does not
  * depend on which one finishes last).  The counter region must be ZERO when
  * the buffer is first used (e.g. allocated zero-filled); every call returns
