@@ -122,11 +122,16 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const u32x4* __restrict__
 
 int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 128 ? 7 : 8; }
 
-bool gemv_uses_octets(int N, int K) {
+// Waves per workgroup: one 32-channel chunk per lane where K allows it
+// (K = 4096: 2 waves; K = 11008: 6); past 512 chunks 12 waves, so that on
+// K = 28672 (896 chunks) most lanes take one chunk instead of two (2% faster
+// than 8 waves; 7 or 14 waves are slower).
+int gemv_waves(int K) {
   const int chunks = K >> 5;
-  const int nw = chunks > 8 * 64 ? 8 : (chunks + 63) / 64;
-  return (long)(N / 8) * nw >= 16 * 256;
+  return chunks > 8 * 64 ? 12 : (chunks + 63) / 64;
 }
+
+bool gemv_uses_octets(int N, int K) { return (long)(N / 8) * gemv_waves(K) >= 16 * 256; }
 
 template <bool ZP, int ROWS>
 hipError_t launch_rows(const u32x4* xv, const u32x4* wv, const uint16_t* sc, const uint32_t* qzeros, _Float16* yv,
@@ -145,6 +150,7 @@ hipError_t launch_rows(const u32x4* xv, const u32x4* wv, const uint16_t* sc, con
     AWQ_GEMV_CASE(6)
     AWQ_GEMV_CASE(7)
     AWQ_GEMV_CASE(8)
+    AWQ_GEMV_CASE(12)
     default: return hipErrorInvalidValue;
   }
 #undef AWQ_GEMV_CASE
@@ -154,10 +160,7 @@ hipError_t launch_rows(const u32x4* xv, const u32x4* wv, const uint16_t* sc, con
 template <bool ZP>
 hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* y,
                      int N, int K, int group_size, hipStream_t stream) {
-  // one 32-channel chunk per lane where K allows it (K = 4096: 2 waves; K = 11008: 6 waves)
-  const int chunks = K >> 5;
-  int nw = (chunks + 63) / 64;
-  if (nw > 8) nw = 8;
+  const int nw = gemv_waves(K);
   const u32x4* xv = static_cast<const u32x4*>(x);
   const u32x4* wv = reinterpret_cast<const u32x4*>(qweight);
   const uint16_t* sc = static_cast<const uint16_t*>(scales);
