@@ -53,8 +53,11 @@ def test_gemv_group_sizes_and_symmetry(g, zp):
 
 
 @pytest.mark.parametrize("N,K,g", [(8, 32, 32), (8, 96, 32), (16, 160, 32), (8, 2304, 256), (40, 11008, 128),
-                                   (24, 4128, 32), (8, 32768, 256)])
+                                   (24, 4128, 32), (8, 32768, 256), (16, 16416, 32), (24, 24608, 32)])
 def test_gemv_ragged_and_minimal_shapes(N, K, g):
+    """Minimal and ragged shapes; K = 16416 and 24608 are just past 512 and 768
+    32-channel chunks, so the 12-wave workgroups run with most lanes idle, or
+    with one chunk for most lanes and a second for a few."""
     check_layer(N, K, g, True)
     check_layer(N, K, g, False)
 
