@@ -22,14 +22,17 @@ legs   = awq_pack, fused-projection decode (qkv and gate_up as one awq_gemv
          fp16 products on the unquantized weights (decode M = 1/4/16/64 and
          the prefill shapes) with the W4A16 speedup over them, and measured
          HBM ceilings (torch's 1 GiB copy and 1 GiB fp16 sum).
-cpu_baseline = the CPU oracle (decode + fp64 product) on one block, timed on
-         the host; a reported reference, not a target.
+cpu_baseline = the CPU oracle on one block, timed on the host (quantize + pack;
+         decode + fp64 product, which is its value; a 70B prefill sample): a
+         reported reference, not a target.  The same oracle results check the
+         run (self_check): the GPU packing bit for bit, and the last timed
+         replay's outputs within 1e-3 * sum |x w'|.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--blocks 32]
-                       [--legs all|none|<comma list>] [--no-cpu-baseline]
+                       [--legs all|none|<comma list>] [--no-cpu-baseline] [--no-layer-timing]
        python bench.py --leg-only pack|fused|batched|dense|prefill|scale|clip|sweep|gemv70b|power|ceiling
                        (one leg, for profiling)
-       python bench.py --copy-calibration | --summarize DB... [--kernel-filter NAME]
+       python bench.py --copy-calibration | --summarize DB... [--kernel-filter NAME] [--last N]
 """
 from __future__ import annotations
 
@@ -68,6 +71,11 @@ def parse():
     ap.add_argument("--summarize", nargs="+", metavar="DB",
                     help="print a per-kernel summary of rocprofv3 result databases and exit")
     ap.add_argument("--kernel-filter", default=None, help="with --summarize: only kernels whose name contains this")
+    ap.add_argument("--last", type=int, default=None,
+                    help="with --summarize: only the last N matching dispatches (e.g. the timed replays)")
+    ap.add_argument("--no-layer-timing", action="store_true",
+                    help="skip the per-layer timing graphs after the timed steps (so that a kernel trace ends "
+                         "with the timed replays)")
     ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "dense", "prefill", "scale", "clip", "sweep", "gemv70b", "power",
                              "ceiling"],
                     help="run just this leg (no headline, no CPU baseline) and print its JSON; for profiling")
@@ -193,7 +201,9 @@ def time_graph(torch, fn, iters, warm=3):
         fn()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    # capture on the warm-up stream: awq_gemm's split-K workspace is per
+    # stream and is not created under capture
+    with torch.cuda.graph(graph, stream=s):
         fn()
     for _ in range(warm):
         graph.replay()
@@ -599,9 +609,36 @@ def leg_power(torch, awq, workloads, g=128, zp=True, seconds=2.0):
     return out
 
 
-def cpu_baseline(layers, g, zp, min_seconds=10.0, max_passes=40):
-    """The CPU oracle as it stands (unpack + fp64 decode + fp64 product) on the
-    seven linears of one block, M = 1."""
+def _cpu_model():
+    """Host CPU model name from lscpu (text), or 'unknown'."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        for line in r.stdout.splitlines():
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    return "unknown"
+
+
+def cpu_baseline(layers, g, zp, timed=None, min_seconds=8.0, max_passes=40, pack_runs=2):
+    """The CPU oracle as it stands on the seven linears of one block, M = 1:
+    (i) quantize + pack, best of ``pack_runs``; (ii) unpack + fp64 decode +
+    fp64 product, repeated for at least ``min_seconds`` (this is ``value``);
+    and a prefill sample on a 70B-shaped layer (quantize + pack once, decode,
+    fp64 product for 64 of the 2048 tokens).
+
+    With ``timed`` (the GPU's packed block and the outputs of the timed decode
+    graph), the oracle's results also check the run: the GPU packing of all
+    seven layers must be bit-identical to the oracle's, and the last timed
+    replay's outputs of block 0 must be within 1e-3 * sum |x w'| of the fp64
+    product (every block's outputs bit-identical to block 0's, since the
+    blocks hold copies of the same weights)."""
+    import numpy as np
+
+    import workloads
     from oracle import awq_oracle as O
 
     try:
@@ -610,24 +647,79 @@ def cpu_baseline(layers, g, zp, min_seconds=10.0, max_passes=40):
         blas_threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover - threadpoolctl missing
         blas_threads = 1
-    packed = [O.pack(L["W"], g, zp) for L in layers]
+    weights = sum(L["N"] * L["K"] for L in layers)
+    pack_s = []
+    packed = None
+    for _ in range(pack_runs):
+        t0 = time.perf_counter()
+        packed = [O.pack(L["W"], g, zp) for L in layers]
+        pack_s.append(time.perf_counter() - t0)
+    pack_bytes = sum(2 * L["N"] * L["K"] + algorithmic_bytes(0, L["N"], L["K"], g, zp) for L in layers)
+
     t0 = time.perf_counter()
     nbytes = 0
     passes = 0
+    refs = []
     while passes < max_passes and (passes == 0 or time.perf_counter() - t0 < min_seconds):
         for L, (qw, sc, qz) in zip(layers, packed):
             wdq = O.dequant_packed(qw, sc, qz, L["N"], L["K"], g, zp)
-            O.matmul_ref(L["X"], wdq)
+            yd = O.matmul_ref(L["X"], wdq)
+            if passes == 0:
+                refs.append(yd)
             nbytes += algorithmic_bytes(1, L["N"], L["K"], g, zp)
         passes += 1
     dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": f"{passes} passes over one Llama-7B block (7 linears, M=1, g=128, zero_point): oracle unpack + "
-                      "fp64 decode + fp64 matmul (numpy; the product runs on the BLAS threads, the decode on one core)"}
+
+    # prefill sample: the 70B-shaped up projection, 64 of the 2048 tokens
+    _, Kp, Np = workloads.LLAMA70B_MLP[0]
+    Mp = 64
+    Wp = workloads.weight(Np, Kp, cfg=4, layer=0)
+    Xp = workloads.activations(2048, Kp, cfg=4, layer=0)[:Mp]
+    t1 = time.perf_counter()
+    pp = O.pack(Wp, g, zp)
+    t_pack = time.perf_counter() - t1
+    t1 = time.perf_counter()
+    O.matmul_ref(Xp, O.dequant_packed(*pp, Np, Kp, g, zp))
+    t_prod = time.perf_counter() - t1
+    del Wp, pp
+
+    out = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads, "kind": "oracle",
+           "seconds": round(dt, 2),
+           "sample": f"{passes} passes over one Llama-7B block (7 linears, M=1, g=128, zero_point): oracle unpack + "
+                     "fp64 decode + fp64 matmul (numpy; the product runs on the BLAS threads, the decode on one "
+                     "core); value = algorithmic bytes / time",
+           "host_cpu_count": os.cpu_count(), "cpu_model": _cpu_model(), "blas_threads": blas_threads,
+           "quantize_pack": {"what": "oracle pack (quantize + store) of the same 7 linears, one core",
+                             "seconds_best": round(min(pack_s), 3), "runs": pack_runs,
+                             "Mweights_per_s": round(weights / min(pack_s) / 1e6, 2),
+                             "GB/s": round(pack_bytes / min(pack_s) / 1e9, 4)},
+           "decode_matmul": {"seconds_per_block": round(dt / passes, 3), "passes": passes},
+           "prefill_sample": {"what": f"70B up_proj {Kp}->{Np}: oracle pack once, then decode + fp64 product "
+                                      f"of {Mp} of the 2048 prefill tokens",
+                              "pack_s": round(t_pack, 2), "decode_product_s": round(t_prod, 2),
+                              "GFLOP/s_product_incl_decode": round(2.0 * Mp * Np * Kp / t_prod / 1e9, 2)}}
+    check = None
+    if timed is not None:
+        pack_ok = True
+        for L, (qw, sc, qz) in zip(layers, packed):
+            pack_ok &= bool(np.array_equal(L["qw"].cpu().numpy().view(np.uint32), qw))
+            pack_ok &= bool(np.array_equal(L["sc"].cpu().numpy().view(np.uint16), sc))
+            if zp:
+                pack_ok &= bool(np.array_equal(L["qz"].cpu().numpy().view(np.uint32), qz))
+        worst = 0.0
+        for y, (y_ref, d) in zip(timed["y_block0"], refs):
+            r = O.tolerance_ratio(y.cpu().numpy().astype(np.float64), y_ref, d)
+            worst = max(worst, float(np.max(r)))
+        check = {"pack_bit_exact": pack_ok, "pack_layers": len(layers),
+                 "gemv_worst_err_over_D": worst, "tolerance": 1e-3,
+                 "blocks_identical": timed["blocks_identical"],
+                 "what": "oracle packing of the block vs the GPU's, bit for bit; the timed graph's last outputs "
+                         "(block 0, 7 layers) vs the fp64 product, |y - y_ref| <= 1e-3 * sum |x w'|",
+                 "pass": bool(pack_ok and worst <= 1e-3 and timed["blocks_identical"])}
+    return out, check
 
 
-def summarize(db_paths, name_filter=None):
+def summarize(db_paths, name_filter=None, last=None):
     """Per-kernel summary of rocprofv3 SQLite databases (kernel-trace and/or
     --pmc runs): dispatch count, duration statistics (mean, median, minimum,
     10th and 90th percentiles) and, when present, the per-dispatch average of
@@ -639,11 +731,15 @@ def summarize(db_paths, name_filter=None):
     for db in db_paths:
         con = sqlite3.connect(db)
         lines.append(f"# {db}")
-        rows = list(con.execute("select dispatch_id, name, duration, grid_x, workgroup_x from kernels"))
+        rows = list(con.execute("select dispatch_id, name, duration, grid_x, workgroup_x from kernels "
+                                "order by dispatch_id"))
+        if name_filter:
+            rows = [r for r in rows if name_filter in r[1]]
+        if last:
+            rows = rows[-last:]  # e.g. only the timed replays at the end of the run
+            lines.append(f"# the last {len(rows)} matching dispatches")
         by = {}
         for kid, name, dur, grid, wg in rows:
-            if name_filter and name_filter not in name:
-                continue
             by.setdefault((name, grid, wg), []).append((kid, dur))
         pmc = {}
         try:
@@ -672,7 +768,7 @@ def summarize(db_paths, name_filter=None):
 def main():
     args = parse()
     if args.summarize:
-        print(summarize(args.summarize, args.kernel_filter))
+        print(summarize(args.summarize, args.kernel_filter, args.last))
         return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1",
@@ -733,7 +829,7 @@ def main():
         step()
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    with torch.cuda.graph(graph, stream=s):
         step()
     for _ in range(args.warmup):
         graph.replay()
@@ -755,14 +851,19 @@ def main():
     avg_us = ms_per_step * 1e3 / launches
     bytes_per_launch = step_bytes / launches
     achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
-    log("timing each layer shape")
-    per_layer = per_layer_launch_times(torch, awq, layers, reps, g, zp)
+    # outputs of the last timed replay, for the oracle check in the CPU baseline
+    timed = {"y_block0": [R["y"].clone() for R in reps[0]],
+             "blocks_identical": all(torch.equal(R["y"], R0["y"]) for rep in reps[1:]
+                                     for R, R0 in zip(rep, reps[0]))}
     layer_stats = {}
-    for L in layers:
-        mu = per_layer[L["name"]]
-        b = algorithmic_bytes(1, L["N"], L["K"], g, zp)
-        layer_stats[L["name"]] = {"K": L["K"], "N": L["N"], "us": round(mu, 3),
-                                  "GB/s": round(b / (mu * 1e-6) / 1e9, 1)}
+    if not args.no_layer_timing:
+        log("timing each layer shape")
+        per_layer = per_layer_launch_times(torch, awq, layers, reps, g, zp)
+        for L in layers:
+            mu = per_layer[L["name"]]
+            b = algorithmic_bytes(1, L["N"], L["K"], g, zp)
+            layer_stats[L["name"]] = {"K": L["K"], "N": L["N"], "us": round(mu, 3),
+                                      "GB/s": round(b / (mu * 1e-6) / 1e9, 1)}
     traffic, traffic_note = hbm_traffic(launches)
 
     result = {
@@ -836,9 +937,10 @@ def main():
     if out_legs:
         result["legs"] = out_legs
     if not args.no_cpu_baseline:
-        log("cpu baseline (oracle)")
-        cb = cpu_baseline(layers, g, zp)
+        log("cpu baseline (oracle) and oracle check of the timed run")
+        cb, check = cpu_baseline(layers, g, zp, timed)
         result["cpu_baseline"] = cb
+        result["self_check"] = check
     print(json.dumps(result), flush=True)
     return 0
 

@@ -173,25 +173,38 @@ def awq_gemv(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, qzero
     return y
 
 
-_WORKSPACES = {}
-_RETIRED_WORKSPACES = []
+_WORKSPACES = {}          # (device index, stream handle) -> zero-initialised uint8 tensor
+_RETIRED_WORKSPACES = []  # replaced buffers, kept alive for graphs that captured their address
 
 
-def gemm_workspace(nbytes: int, device) -> torch.Tensor:
-    """The zero-initialised awq_gemm workspace of ``device`` (at least
-    ``nbytes``), kept for later calls.  awq_gemm returns the workspace's
-    counters to zero, so calls in stream order share it, including calls
-    captured into a HIP graph.  It is one buffer per device: calls that may
-    run concurrently on different streams must each pass a workspace of their
-    own (``torch.zeros(awq_gemm_workspace_bytes(...), dtype=torch.uint8)``)."""
-    device = torch.device(device)
-    key = device.index if device.index is not None else torch.cuda.current_device()
+def gemm_workspace(nbytes: int, device=None, stream=None) -> torch.Tensor:
+    """The zero-initialised awq_gemm workspace of (``device``, ``stream``), at
+    least ``nbytes`` long, kept for later calls on that stream.  awq_gemm
+    returns the workspace's counters to zero, so calls in one stream's order
+    share it, including calls captured into a HIP graph on that stream.
+    Calls on different streams get different buffers, since overlapping
+    calls on one buffer would break its per-tile counters.
+
+    Under graph capture the buffer is not created or grown (its zero fill
+    would only be recorded into the graph): call once eagerly on the
+    capture stream first, or pass ``workspace=`` explicitly."""
+    device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if stream is None:
+        stream = torch.cuda.current_stream(idx)
+    key = (idx, stream.cuda_stream)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(
+                f"awq_gemm needs a {nbytes}-byte split-K workspace on stream {stream.cuda_stream:#x} of cuda:{idx}, "
+                "and none of that size exists; a workspace cannot be created during graph capture. Make one "
+                "eager call of the largest shape on the capture stream before capturing, or pass workspace= "
+                "(a zero-filled uint8 tensor of awq_gemm_workspace_bytes(...) bytes)")
         if ws is not None:
-            # a captured graph may still hold the old buffer's address: keep it alive
             _RETIRED_WORKSPACES.append(ws)
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):  # zero fill ordered before this stream's next call
+            ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=torch.device("cuda", idx))
         _WORKSPACES[key] = ws
     return ws
 

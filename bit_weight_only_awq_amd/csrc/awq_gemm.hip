@@ -374,8 +374,8 @@ __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((
 // slice, whose MFMAs overlap the next step's first reads, its buffer-to-LDS
 // loads and its first decode.  Every global access goes through a buffer
 // resource based at the tile (rows past M or N read as zero), and the K loop
-// has no branches: loads for steps past the end stay inside the buffers (or
-// return zero) and land where no one reads again.
+// has no branches: loads for steps past the end carry an out-of-range lane
+// offset (they return zero) and land where no one reads again.
 //   MFMA slice ks of step s, lane half h, element j  <->  channel 64 s + 32 h + 8 ks + j
 // (A and B use the same assignment, so the product is unchanged.)
 template <bool ZP, bool KTAIL, int NB, int TBM>
@@ -432,7 +432,10 @@ __global__ __launch_bounds__(256) void gemm_large_kernel(const _Float16* __restr
     char* dst = (buf ? lx1 : lx0) + wave * XROWS * 128;
 #pragma unroll
     for (int j = 0; j < XROWS / 8; ++j) {
-      uint32_t off = xoff[j];
+      // the step goes into the instruction's scalar offset, which the
+      // hardware leaves out of the range check: a prefetch past the last
+      // step must carry the out-of-range lane offset instead
+      uint32_t off = step < nsteps ? xoff[j] : kOutOfRange;
       if constexpr (KTAIL) {
         if (step * BK + 8 * xchunk[j] >= K) off = kOutOfRange;
       }
@@ -459,7 +462,9 @@ __global__ __launch_bounds__(256) void gemm_large_kernel(const _Float16* __restr
   };
   auto fetch_w = [&](WRegs& r, int step) {
     const int k0 = step * BK + 32 * fh;
-    const bool kin = !KTAIL || k0 < K;
+    // past the last step the weight row offset would run off the buffer
+    // through the scalar offset, which is not range-checked (see load_x)
+    const bool kin = step < nsteps && (!KTAIL || k0 < K);
     const int grp = k0 >> gshift;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {

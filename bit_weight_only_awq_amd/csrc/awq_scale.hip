@@ -158,7 +158,9 @@ __global__ __launch_bounds__(WM * WN * 64) void sumsq_gemm_kernel(const _Float16
     char* de = (buf ? le1 : le0) + wave * 4096;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t o = off[j];
+      // the step sits in the scalar offset, outside the hardware's range
+      // check: a prefetch past the last step takes the out-of-range lane offset
+      uint32_t o = step < nsteps ? off[j] : kOutOfRange;
       if constexpr (KTAIL) {  // channels past K of the last step load as zero
         if (step * TK + 8 * chunk[j] >= K) o = kOutOfRange;
       }
@@ -227,8 +229,8 @@ __global__ __launch_bounds__(WM * WN * 64) void sumsq_gemm_kernel(const _Float16
 
   // Two steps per trip; the scheduling barriers keep each step's loads ahead
   // of the multiplies that hide their latency.  Loads of a step past the end
-  // stay inside the resources (or read zero) and land in a buffer no one
-  // reads again.
+  // read zero (out-of-range lane offset) and land in a buffer no one reads
+  // again.
   load(0, 0);
   __syncthreads();
   int step = 0;

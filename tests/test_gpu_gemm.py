@@ -101,6 +101,34 @@ def test_gemm_split_k_workspace_reuse():
     G.assert_within_tolerance(G.host_f16(ys[-1]), y_ref, d, "reused workspace")
 
 
+def test_gemm_split_k_back_to_back_new_data():
+    """Split-K calls of one shape in a row on one workspace, each with new
+    activations (the k_proj / v_proj case of batched decode): a last
+    workgroup that read a stale partial or a stale counter would give the
+    previous call's bytes.  Each output must equal the same call on a freshly
+    zeroed workspace and meet the oracle's tolerance."""
+    awq = G.lib()
+    g = 128
+    for M, N, K in [(16, 4096, 4096), (56, 1032, 8192), (7, 264, 4096)]:
+        need = awq.awq_gemm_workspace_bytes(M, N, K, g)
+        assert need > 0
+        ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        W = workloads.weight(N, K, cfg=3, layer=7 * M)
+        packed = O.pack(W, g, True)
+        qw, sc, qz = G.upload_packed(*packed)
+        wdq = O.dequant_packed(*packed, N, K, g, True)
+        for call in range(4):
+            X = workloads.activations(M, K, cfg=3, layer=100 * M + call)
+            x = G.dev_f16(X)
+            y = awq.awq_gemm(x, qw, sc, qz, N, K, g, True, workspace=ws)
+            fresh = awq.awq_gemm(x, qw, sc, qz, N, K, g, True,
+                                 workspace=torch.zeros(need, dtype=torch.uint8, device="cuda"))
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), fresh.view(torch.int16)), f"M={M} N={N} K={K} call {call}"
+            y_ref, d = O.matmul_ref(X, wdq)
+            G.assert_within_tolerance(G.host_f16(y), y_ref, d, f"back-to-back M={M} N={N} K={K} call {call}")
+
+
 @pytest.mark.parametrize("M", [4, 200])
 @pytest.mark.parametrize("zp", [True, False])
 def test_gemm_one_hot_reproduces_decoded_weights(M, zp):
@@ -142,17 +170,22 @@ def test_gemm_large_launch_paths(M, N, K, g, split, what):
     check(M, N, K, g, True, what=f"{what}: M={M} N={N} K={K} g={g}")
 
 
-@pytest.mark.parametrize("M,N,K,g", [(48, 8200, 544, 32), (64, 8192, 1024, 128), (33, 16384, 256, 64),
-                                     (56, 1032, 8224, 32), (64, 4096, 11008, 128)])
-def test_gemm_mid_tokens_wide_layers(M, N, K, g):
+@pytest.mark.parametrize("M,N,K,g,split", [(48, 8200, 544, 32, True), (64, 8192, 1024, 128, True),
+                                           (33, 16384, 256, 64, False), (56, 1032, 8224, 32, True),
+                                           (64, 4096, 11008, 128, True)])
+def test_gemm_mid_tokens_wide_layers(M, N, K, g, split):
     """33-64 tokens on layers with N >= 8192, and 49-64 tokens on layers with
     K >= 8192, run on the matrix-core kernel's 64-row tiles: 64 x 128 with K
     split, or 64 x 256 without where the tiles alone fill the chip (the third
     case); ragged last tile and K step in the first and fourth cases; every
     output is checked."""
     need = G.lib().awq_gemm_workspace_bytes(M, N, K, g)
-    # no K split (enough tiles already), or whole fp32 [M][N] partial slices past the tile counters
-    assert need == 0 or (need > 512 * 1024 and (need - 512 * 1024) % (M * N * 4) == 0)
+    # each case pins whether K is split; a split needs whole fp32 [M][N]
+    # partial slices past the 512 KiB of tile counters
+    if split:
+        assert need > 512 * 1024 and (need - 512 * 1024) % (M * N * 4) == 0
+    else:
+        assert need == 0
     check(M, N, K, g, True)
     check(M, N, K, g, False)
 

@@ -35,7 +35,8 @@ def test_graph_replays_match_eager(M, N, K, fn):
         f(x, qw, sc, qz, N, K, g, True, y=y)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    # captured on the warm-up stream, whose split-K workspace now exists
+    with torch.cuda.graph(graph, stream=s):
         f(x, qw, sc, qz, N, K, g, True, y=y)
     # other eager work between replays, sharing the split-K workspace
     W2 = workloads.weight(2048, 4096, cfg=9, layer=99)
