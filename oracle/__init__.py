@@ -18,6 +18,10 @@ from .awq_oracle import (  # noqa: F401
     pack_scales,
     quantize,
     recon_loss,
+    scale_candidates,
+    scale_weights,
+    search_scale,
+    weight_scale,
     tolerance_ratio,
     unpack,
     unpack_qweight,

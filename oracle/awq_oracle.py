@@ -51,6 +51,10 @@ of the repository):
    give no candidate family; the reading taken is s = a^alpha with
    a_k = max(mean_m |x_mk|, 1e-4) and alpha on a grid in [0, 1); the search
    keeps the candidate with the smallest L(s) (the first one on ties).
+   With ``duo_scaling`` ([P5] "自定义校准策略 (校准参数全景)": scale weights and
+   activations) the candidate also divides by a weight statistic of the same
+   channel: s = a^alpha / b^(1 - alpha), b_k = max(mean_n |w_nk|, 1e-4), the
+   plainest reading that uses both (alpha = 1 is the activation-only a).
 9. Weight clipping ([P5] "自定义校准策略" (校准参数全景), ``apply_clip``: clip the weights to
    further reduce the effect of outliers on the quantization error).  The pages
    give no rule; the reading taken: each group tries ratios r in (0, 1]; its
@@ -288,14 +292,21 @@ def recon_loss(W16: np.ndarray, X: np.ndarray, s: np.ndarray, g: int, zero_point
     s = np.asarray(s, dtype=F32)
     if s.shape != (K,) or not np.all(s > 0):
         raise ValueError("s must be a positive vector of length K")
-    Ws16 = (W16.astype(F32) * s[None, :]).astype(F32).astype(np.float16)
-    Wq = fake_quant(Ws16, g, zero_point)
+    Wq = fake_quant(scale_weights(W16, s), g, zero_point)
     Xs = np.asarray(X, dtype=np.float64) / s.astype(np.float64)[None, :]
     ref = np.asarray(X, dtype=np.float64) @ W16.astype(np.float64).T
     return float(np.linalg.norm(Xs @ Wq.T - ref))
 
 
+def scale_weights(W16: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """fp16(W * s): each weight times its input channel's scale, an fp32
+    product rounded once to fp16 (reading 7: Q takes fp16 weights)."""
+    s = np.asarray(s, dtype=F32)
+    return (W16.astype(F32) * s[None, :]).astype(F32).astype(np.float16)
+
+
 ACT_FLOOR = 1e-4
+WEIGHT_FLOOR = 1e-4
 
 
 def activation_scale(X16: np.ndarray) -> np.ndarray:
@@ -307,17 +318,31 @@ def activation_scale(X16: np.ndarray) -> np.ndarray:
     return np.maximum(np.abs(X).mean(axis=0), ACT_FLOOR)
 
 
-def scale_candidates(X16: np.ndarray, alphas) -> np.ndarray:
-    """Candidate scales s_c = a^alpha_c (reading 8), as fp32 [len(alphas), K];
-    alpha = 0 gives exactly 1."""
+def weight_scale(W16: np.ndarray) -> np.ndarray:
+    """Per-input-channel weight statistic of duo scaling (reading 8),
+    b_k = max(mean_n |w_nk|, 1e-4), fp64."""
+    W = np.asarray(W16, dtype=np.float64)
+    if W.ndim != 2 or W.shape[0] < 1:
+        raise ValueError("W must be [N, K] with N >= 1")
+    return np.maximum(np.abs(W).mean(axis=0), WEIGHT_FLOOR)
+
+
+def scale_candidates(X16: np.ndarray, alphas, W16: np.ndarray | None = None) -> np.ndarray:
+    """Candidate scales (reading 8) as fp32 [len(alphas), K]: s_c = a^alpha_c
+    (alpha = 0 gives exactly 1), or with ``W16`` (duo scaling)
+    s_c = a^alpha_c / b^(1 - alpha_c), computed in fp64 and rounded to fp32."""
     a = activation_scale(X16)
-    return np.stack([np.power(a, float(al)).astype(F32) for al in alphas])
+    if W16 is None:
+        return np.stack([np.power(a, float(al)).astype(F32) for al in alphas])
+    b = weight_scale(W16)
+    return np.stack([(np.power(a, float(al)) / np.power(b, 1.0 - float(al))).astype(F32) for al in alphas])
 
 
-def search_scale(W16: np.ndarray, X16: np.ndarray, g: int, zero_point: bool, alphas):
-    """Evaluate L(s_c) (reading 7) for every candidate of reading 8 and return
-    (index of the smallest loss, the candidates, the losses)."""
-    S = scale_candidates(X16, alphas)
+def search_scale(W16: np.ndarray, X16: np.ndarray, g: int, zero_point: bool, alphas, duo: bool = False):
+    """Evaluate L(s_c) (reading 7) for every candidate of reading 8 (duo
+    scaling with ``duo``) and return (index of the smallest loss, the
+    candidates, the losses)."""
+    S = scale_candidates(X16, alphas, W16 if duo else None)
     losses = [recon_loss(W16, X16, s, g, zero_point) for s in S]
     return int(np.argmin(losses)), S, losses
 

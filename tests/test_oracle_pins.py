@@ -336,6 +336,62 @@ def check_scale_candidates():
     assert np.array_equal(S[1], np.sqrt(np.array([2.0, 1.0, 1e-4, 0.5])).astype(np.float32))
 
 
+def check_duo_candidates():
+    # a = [2, 1, 1e-4 (floor), 0.5] as above; b = mean |w| per channel = [0.5, 1, 2, 1e-4 (floor)]
+    X = np.array([[1, -2, 0, 0.5], [3, 0, 0, -0.5]], np.float16)
+    W = np.array([[0.5, 1, 2, 0], [0.5, -1, -2, 0]], np.float16)
+    assert np.array_equal(O.weight_scale(W), np.array([0.5, 1.0, 2.0, 1e-4]))
+    S = O.scale_candidates(X, [0.0, 0.5, 1.0], W)
+    assert S.dtype == np.float32 and S.shape == (3, 4)
+    # alpha = 0: 1 / b; alpha = 1: a (the activation-only candidate); alpha = 1/2: sqrt(a / b)
+    assert np.array_equal(S[0], np.array([2.0, 1.0, 0.5, 1e4], np.float32))
+    assert np.array_equal(S[2], np.array([2.0, 1.0, 1e-4, 0.5], np.float32))
+    np.testing.assert_allclose(S[1], [2.0, 1.0, math.sqrt(5e-5), math.sqrt(5e3)], rtol=2.4e-7)
+    # weights twice as large halve the alpha = 0 candidate exactly (the floored
+    # all-zero channel keeps its floor)
+    S2 = O.scale_candidates(X, [0.0], (W.astype(np.float32) * 2).astype(np.float16))[0]
+    assert np.array_equal(S2[:3], S[0][:3] / 2) and S2[3] == S[0][3]
+
+
+def check_weight_scale_brute_force():
+    W = workloads.weight(37, 24, cfg=96, layer=3, row_offset=True)
+    W[:, 5] = 0  # an all-zero channel takes the floor
+    b = O.weight_scale(W)
+    for k in range(24):
+        want = max(math.fsum(abs(float(v)) for v in W[:, k]) / 37, 1e-4)
+        assert abs(b[k] - want) <= 1e-15 * want, k
+    assert b[5] == 1e-4
+
+
+def check_scale_weights():
+    W = np.array([[0.5, 3, -1.5, 1.0], [0.25, -2, 0, 1.0]], np.float16)
+    s = np.array([2.0, 0.5, 3.0, 1.0 / 3.0], np.float32)
+    got = O.scale_weights(W, s)
+    assert got.dtype == np.float16
+    # products exact in fp16, except 1 * fp32(1/3) = 0.33333334 whose nearest fp16 is 0x3555 (0.333251953125)
+    want = np.array([[1.0, 1.5, -4.5, 0.333251953125], [0.5, -1.0, 0.0, 0.333251953125]], np.float16)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+    assert got.view(np.uint16)[0, 3] == 0x3555
+    # a power-of-two scale >= 1 per channel scales exactly
+    Wr = workloads.weight(8, 64, cfg=96, layer=4)
+    e = np.random.default_rng(3).integers(0, 4, size=64)  # no scale into the fp16 subnormals
+    assert np.array_equal(O.scale_weights(Wr, np.exp2(e).astype(np.float32)).astype(np.float64),
+                          Wr.astype(np.float64) * np.exp2(e)[None, :])
+
+
+def check_duo_search():
+    W = workloads.weight(64, 256, cfg=96, layer=1)
+    X = workloads.activations(64, 256, cfg=96, layer=1)
+    alphas = [i / 10 for i in range(10)]
+    best, S, losses = O.search_scale(W, X, 64, True, alphas, duo=True)
+    assert np.array_equal(S, O.scale_candidates(X, alphas, W))
+    for i in (0, 3, 9):
+        assert losses[i] == O.recon_loss(W, X, S[i], 64, True)
+    assert losses[best] == min(losses) and all(losses[best] < losses[i] for i in range(best))
+    rtn = O.recon_loss(W, X, np.ones(256, np.float32), 64, True)
+    assert losses[best] < 0.8 * rtn, "duo scaling must beat plain rounding on 1%-outlier data"
+
+
 def check_search_scale():
     W = workloads.weight(64, 256, cfg=96, layer=1)
     X = workloads.activations(64, 256, cfg=96, layer=1)
@@ -489,6 +545,19 @@ def test_search_scale():
     check_search_scale()
 
 
+def test_duo_scaling_candidates():
+    check_duo_candidates()
+    check_weight_scale_brute_force()
+
+
+def test_scale_weights():
+    check_scale_weights()
+
+
+def test_duo_search():
+    check_duo_search()
+
+
 def test_clip_weight():
     check_clip_weight()
 
@@ -544,6 +613,10 @@ ALL_CHECKS = (
     check_matmul_exact,
     check_scale_candidates,
     check_search_scale,
+    check_duo_candidates,
+    check_weight_scale_brute_force,
+    check_scale_weights,
+    check_duo_search,
     check_clip_weight,
     check_clip_errors,
     check_search_clip,
@@ -577,6 +650,9 @@ MUTATIONS = {
     "candidate_inverse_power": None,
     "search_keeps_largest_loss": None,
     "clip_low_bound_unscaled": None,
+    "duo_weight_power_flipped": None,
+    "weight_stat_max_not_mean": None,
+    "scale_weights_divides": None,
     "clip_error_against_clipped_weight": None,
 }
 
@@ -649,6 +725,22 @@ def _patch_function(mp, name):
             return int(np.argmax(losses)), S, losses
 
         mp.setattr(O, "search_scale", search)
+    elif name == "duo_weight_power_flipped":
+        orig_sc = O.scale_candidates
+
+        def sc(X16, alphas, W16=None):
+            if W16 is None:
+                return orig_sc(X16, alphas)
+            a, b = O.activation_scale(X16), O.weight_scale(W16)
+            return np.stack([(np.power(a, al) * np.power(b, 1.0 - al)).astype(np.float32) for al in alphas])
+
+        mp.setattr(O, "scale_candidates", sc)
+    elif name == "weight_stat_max_not_mean":
+        mp.setattr(O, "weight_scale",
+                   lambda W16: np.maximum(np.abs(np.asarray(W16, np.float64)).max(axis=0), O.WEIGHT_FLOOR))
+    elif name == "scale_weights_divides":
+        mp.setattr(O, "scale_weights", lambda W16, s: (W16.astype(np.float32) / np.asarray(s, np.float32)[None, :])
+                   .astype(np.float32).astype(np.float16))
     elif name == "clip_low_bound_unscaled":
         def cw(W16, g, zero_point, ratio):
             N, K = W16.shape
