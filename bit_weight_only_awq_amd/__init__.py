@@ -15,7 +15,7 @@ Entry points (same names and arguments as the C ABI):
 * ``awq_gemm_workspace_bytes(M, N, K, group_size)``, ``awq_strerror(status)``
 
 plus ``pack(W, q_group_size, zero_point)`` / ``linear(x, packed)`` which pick
-GEMV for one token and GEMM otherwise, following ``quant_config``'s
+GEMV up to 8 tokens and GEMM otherwise, following ``quant_config``'s
 ``version`` ("Optimization Awq", section "Quantizar seu próprio modelo").
 """
 from __future__ import annotations
@@ -41,7 +41,7 @@ AWQ_ERR_HIP = -7
 EXPORTED = ("awq_pack", "awq_dequant", "awq_gemv", "awq_gemm", "awq_gemm_workspace_bytes", "awq_strerror",
             "awq_scale_candidates", "awq_scale_candidates_workspace_bytes", "awq_scale_loss",
             "awq_scale_loss_workspace_bytes", "awq_scale_columns", "awq_clip_search",
-            "awq_clip_search_workspace_bytes")
+            "awq_clip_search_workspace_bytes", "awq_scale_search", "awq_scale_search_workspace_bytes")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -74,10 +74,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.awq_gemm_workspace_bytes.restype = SZ
     lib.awq_strerror.argtypes = [ctypes.c_int]
     lib.awq_strerror.restype = ctypes.c_char_p
-    lib.awq_scale_candidates.argtypes = [P, I32, I32, P, I32, P, P, SZ, P]
+    lib.awq_scale_candidates.argtypes = [P, I32, I32, P, I32, I32, P, I32, P, P, SZ, P]
     lib.awq_scale_candidates.restype = ctypes.c_int
-    lib.awq_scale_candidates_workspace_bytes.argtypes = [I32, I32]
+    lib.awq_scale_candidates_workspace_bytes.argtypes = [I32, I32, I32]
     lib.awq_scale_candidates_workspace_bytes.restype = SZ
+    lib.awq_scale_search.argtypes = [P, P, I32, I32, I32, I32, I32, P, I32, I32, P, P, P, P, SZ, P]
+    lib.awq_scale_search.restype = ctypes.c_int
+    lib.awq_scale_search_workspace_bytes.argtypes = [I32, I32, I32, I32]
+    lib.awq_scale_search_workspace_bytes.restype = SZ
     lib.awq_scale_loss.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, SZ, P, P]
     lib.awq_scale_loss.restype = ctypes.c_int
     lib.awq_scale_loss_workspace_bytes.argtypes = [I32, I32, I32, I32]
@@ -164,7 +168,7 @@ def _xy(x: torch.Tensor, N: int, y: Optional[torch.Tensor]):
 
 def awq_gemv(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional[torch.Tensor], N: int,
              K: int, group_size: int = 128, zero_point: bool = True, y: Optional[torch.Tensor] = None):
-    """Single-token layer y = x . W'^T for x fp16 [1, K]; returns fp16 [1, N]."""
+    """Single- and few-token layer Y = X . W'^T for X fp16 [M, K], 1 <= M <= 8; returns fp16 [M, N]."""
     lib = load_library()
     y = _xy(x, N, y)
     st = lib.awq_gemv(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros) if zero_point else None, _ptr(y),
@@ -278,27 +282,31 @@ def pack_fused(weights, q_group_size: int = 128, zero_point: bool = True) -> Pac
 
 
 def linear(x: torch.Tensor, pw: PackedWeight, version: str = "auto") -> torch.Tensor:
-    """Y = X . W'^T.  ``version`` "GEMV" (one token), "GEMM" (any batch) or "auto"."""
+    """Y = X . W'^T.  ``version`` "GEMV" (up to 8 tokens), "GEMM" (any batch) or "auto"."""
     x2 = x.reshape(-1, pw.K)
     v = version.upper()
     if v == "AUTO":
-        v = "GEMV" if x2.shape[0] == 1 else "GEMM"
+        v = "GEMV" if x2.shape[0] <= 8 else "GEMM"
     fn = awq_gemv if v == "GEMV" else awq_gemm
     y = fn(x2, pw.qweight, pw.scales, pw.qzeros, pw.N, pw.K, pw.group_size, pw.zero_point)
     return y.reshape(*x.shape[:-1], pw.N)
 
 
-def awq_scale_candidates(x: torch.Tensor, alphas) -> torch.Tensor:
+def awq_scale_candidates(x: torch.Tensor, alphas, w: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Candidate per-channel scales s[c] = max(mean |x|, 1e-4) ** alphas[c] for fp16
-    calibration activations ``x`` [M, K]; returns fp32 [len(alphas), K] on x's device."""
+    calibration activations ``x`` [M, K]; with ``w`` [N, K] (duo scaling) also
+    divided by max(mean |w|, 1e-4) ** (1 - alphas[c]).  Returns fp32
+    [len(alphas), K] on x's device."""
     lib = load_library()
     alphas = [float(a) for a in alphas]
     M, K = x.shape
+    N = w.shape[0] if w is not None else 0
     s = torch.empty((len(alphas), K), dtype=torch.float32, device=x.device)
-    ws = torch.empty(max(1, int(lib.awq_scale_candidates_workspace_bytes(M, K))), dtype=torch.uint8, device=x.device)
+    ws = torch.empty(max(1, int(lib.awq_scale_candidates_workspace_bytes(M, N, K))), dtype=torch.uint8,
+                     device=x.device)
     arr = (ctypes.c_float * len(alphas))(*alphas)
-    st = lib.awq_scale_candidates(_ptr(x), M, K, ctypes.cast(arr, ctypes.c_void_p), len(alphas), _ptr(s), _ptr(ws),
-                                  ws.numel(), _stream(x))
+    st = lib.awq_scale_candidates(_ptr(x), M, K, _ptr(w), N, int(w is not None), ctypes.cast(arr, ctypes.c_void_p),
+                                  len(alphas), _ptr(s), _ptr(ws), ws.numel(), _stream(x))
     _check(st, "awq_scale_candidates")
     return s
 
@@ -321,25 +329,50 @@ def awq_scale_loss(x: torch.Tensor, w: torch.Tensor, s: torch.Tensor, group_size
     return loss
 
 
+DEFAULT_ALPHAS = tuple(i / 20 for i in range(20))
+
+
 class ScaleSearch(NamedTuple):
-    alpha: float
-    scale: torch.Tensor   # fp32 [K], the chosen s
-    losses: list          # L(s) of every candidate, in the order of alphas
-    alphas: list
+    best: torch.Tensor    # int32 [1] on the device: index of the chosen candidate
+    scale: torch.Tensor   # fp32 [K] on the device: the chosen s
+    losses: torch.Tensor  # fp64 [count] on the device: L(s) of every candidate, in the order of alphas
+    alphas: tuple
+
+    @property
+    def alpha(self) -> float:
+        """The chosen exponent (reads the index back from the device)."""
+        return self.alphas[int(self.best.item())]
+
+
+def awq_scale_search(x: torch.Tensor, w: torch.Tensor, group_size: int = 128, zero_point: bool = True,
+                     alphas=DEFAULT_ALPHAS, duo: bool = False) -> ScaleSearch:
+    """Activation-aware scale search on the device: L(s) for s = a ** alpha
+    (duo: a ** alpha / b ** (1 - alpha)) over ``alphas`` and the first
+    candidate with the smallest loss.  ``x`` fp16 [M, K] calibration
+    activations, ``w`` fp16 [N, K].  Nothing is read back to the host."""
+    lib = load_library()
+    alphas = tuple(float(a) for a in alphas)
+    M, K = x.shape
+    N = w.shape[0]
+    dev = x.device
+    s_best = torch.empty(K, dtype=torch.float32, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    losses = torch.empty(len(alphas), dtype=torch.float64, device=dev)
+    ws = torch.empty(max(1, int(lib.awq_scale_search_workspace_bytes(len(alphas), M, N, K))), dtype=torch.uint8,
+                     device=dev)
+    arr = (ctypes.c_float * len(alphas))(*alphas)
+    st = lib.awq_scale_search(_ptr(x), _ptr(w), M, N, K, group_size, int(bool(zero_point)),
+                              ctypes.cast(arr, ctypes.c_void_p), len(alphas), int(bool(duo)), _ptr(s_best),
+                              _ptr(best), _ptr(losses), _ptr(ws), ws.numel(), _stream(x))
+    _check(st, "awq_scale_search")
+    return ScaleSearch(best, s_best, losses, alphas)
 
 
 def search_scale(x: torch.Tensor, w: torch.Tensor, group_size: int = 128, zero_point: bool = True,
-                 alphas=None) -> ScaleSearch:
-    """Activation-aware scale search: evaluate L(s) for s = a ** alpha over a
-    grid of exponents (default 0, 1/20, ..., 19/20) and keep the best.  The
+                 alphas=None, duo: bool = False) -> ScaleSearch:
+    """Activation-aware scale search (default grid 0, 1/20, ..., 19/20).  The
     chosen s is applied as W * s before packing and s^-1 on the activations."""
-    if alphas is None:
-        alphas = [i / 20 for i in range(20)]
-    alphas = [float(a) for a in alphas]
-    S = awq_scale_candidates(x, alphas)
-    losses = awq_scale_loss(x, w, S, group_size, zero_point).cpu().tolist()
-    best = min(range(len(alphas)), key=lambda i: (losses[i], i))
-    return ScaleSearch(alphas[best], S[best].clone(), losses, alphas)
+    return awq_scale_search(x, w, group_size, zero_point, DEFAULT_ALPHAS if alphas is None else alphas, duo)
 
 
 def awq_scale_columns(src: torch.Tensor, s: torch.Tensor, divide: bool = False,
@@ -381,20 +414,21 @@ def awq_clip_search(x: torch.Tensor, w: torch.Tensor, group_size: int = 128, zer
 class QuantizedLinear(NamedTuple):
     packed: PackedWeight
     input_scale: torch.Tensor  # fp32 [K]: the layer computes on fp16(x / input_scale)
-    alpha: float
+    search: ScaleSearch        # the scale search (chosen index and losses stay on the device)
 
 
 def quantize_awq(w: torch.Tensor, x: torch.Tensor, q_group_size: int = 128, zero_point: bool = True,
-                 alphas=None, clip_ratios=DEFAULT_CLIP_RATIOS, apply_clip: bool = True) -> QuantizedLinear:
+                 alphas=None, clip_ratios=DEFAULT_CLIP_RATIOS, apply_clip: bool = True,
+                 duo_scaling: bool = False) -> QuantizedLinear:
     """The activation-aware quantization of one linear layer from calibration
-    activations ``x`` [M, K]: scale search (s = a ** alpha with the smallest
+    activations ``x`` [M, K]: scale search (the candidate s with the smallest
     L(s)), weights scaled by s, optional clipping search on the scaled layer,
-    then packing.  The packed layer expects activations divided by
-    ``input_scale`` (``awq_scale_columns(x, s, divide=True)``, or folded into
-    the producer of x)."""
-    res = search_scale(x, w, q_group_size, zero_point, alphas)
+    then packing; every step on the device, with no host synchronization.
+    The packed layer expects activations divided by ``input_scale``
+    (``awq_scale_columns(x, s, divide=True)``, or folded into the producer of x)."""
+    res = search_scale(x, w, q_group_size, zero_point, alphas, duo_scaling)
     ws = awq_scale_columns(w, res.scale)
     if apply_clip:
         xs = awq_scale_columns(x, res.scale, divide=True)
         ws, _ = awq_clip_search(xs, ws, q_group_size, zero_point, clip_ratios)
-    return QuantizedLinear(pack(ws, q_group_size, zero_point), res.scale, res.alpha)
+    return QuantizedLinear(pack(ws, q_group_size, zero_point), res.scale, res)

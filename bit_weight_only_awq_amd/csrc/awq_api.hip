@@ -70,8 +70,8 @@ int awq_gemv(const void* x, const uint32_t* qweight, const void* scales, const u
   st = check_packed(qweight, scales, qzeros, zero_point);
   if (st != AWQ_OK) return st;
   if (!aligned16(x) || !aligned16(y)) return AWQ_ERR_ALIGN;
-  if (M != 1) return AWQ_ERR_UNSUPPORTED;
-  return from_hip(awq::launch_gemv(x, qweight, scales, zero_point ? qzeros : nullptr, y, N, K, group_size,
+  if (M > awq::kMaxGemvTokens) return AWQ_ERR_UNSUPPORTED;
+  return from_hip(awq::launch_gemv(x, qweight, scales, zero_point ? qzeros : nullptr, y, M, N, K, group_size,
                                    zero_point != 0, static_cast<hipStream_t>(stream)));
 }
 
@@ -99,19 +99,43 @@ int awq_gemm(const void* x, const uint32_t* qweight, const void* scales, const u
                                    static_cast<hipStream_t>(stream)));
 }
 
-size_t awq_scale_candidates_workspace_bytes(int32_t M, int32_t K) {
-  if (M < 1 || K < 8 || K > kMaxDim || (K & 7) != 0) return 0;
-  return awq::scale_candidates_workspace_bytes(M, K);
+size_t awq_scale_candidates_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (M < 1 || N < 0 || N > kMaxDim || K < 8 || K > kMaxDim || (K & 7) != 0) return 0;
+  return awq::scale_candidates_workspace_bytes(M, N, K);
 }
 
-int awq_scale_candidates(const void* x, int32_t M, int32_t K, const float* alphas, int32_t count, float* s,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+int awq_scale_candidates(const void* x, int32_t M, int32_t K, const void* w, int32_t N, int32_t duo,
+                         const float* alphas, int32_t count, float* s, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   if (M < 1 || K < 8 || K > kMaxDim || (K & 7) != 0) return AWQ_ERR_SHAPE;
   if (count < 1 || count > awq::kMaxScaleCandidates) return AWQ_ERR_SHAPE;
-  if (!x || !alphas || !s || !workspace) return AWQ_ERR_NULL;
-  if (!aligned16(x) || !aligned16(s) || !aligned16(workspace)) return AWQ_ERR_ALIGN;
-  if (workspace_bytes < awq::scale_candidates_workspace_bytes(M, K)) return AWQ_ERR_WORKSPACE;
-  return from_hip(awq::launch_scale_candidates(x, M, K, alphas, count, s, workspace, static_cast<hipStream_t>(stream)));
+  if (duo && (N < 1 || N > kMaxDim)) return AWQ_ERR_SHAPE;
+  if (!x || !alphas || !s || !workspace || (duo && !w)) return AWQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(s) || !aligned16(workspace) || (duo && !aligned16(w))) return AWQ_ERR_ALIGN;
+  if (workspace_bytes < awq::scale_candidates_workspace_bytes(M, duo ? N : 0, K)) return AWQ_ERR_WORKSPACE;
+  return from_hip(awq::launch_scale_candidates(x, M, K, duo ? w : nullptr, duo ? N : 0, alphas, count, s, workspace,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+size_t awq_scale_search_workspace_bytes(int32_t count, int32_t M, int32_t N, int32_t K) {
+  if (count < 1 || count > awq::kMaxScaleCandidates || M < 1 || N < 8 || K < 8 || N > kMaxDim || K > kMaxDim)
+    return 0;
+  return awq::scale_search_workspace_bytes(count, M, N, K);
+}
+
+int awq_scale_search(const void* x, const void* w, int32_t M, int32_t N, int32_t K, int32_t group_size,
+                     int32_t zero_point, const float* alphas, int32_t count, int32_t duo, float* s_best,
+                     int32_t* best, double* losses, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_weight_shape(N, K, group_size);
+  if (st != AWQ_OK) return st;
+  if (M < 1 || count < 1 || count > awq::kMaxScaleCandidates) return AWQ_ERR_SHAPE;
+  if (!x || !w || !alphas || !s_best || !best || !workspace) return AWQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(s_best) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(best) & 3u) != 0 || (reinterpret_cast<uintptr_t>(losses) & 7u) != 0)
+    return AWQ_ERR_ALIGN;
+  if (workspace_bytes < awq::scale_search_workspace_bytes(count, M, N, K)) return AWQ_ERR_WORKSPACE;
+  return from_hip(awq::launch_scale_search(x, w, M, N, K, group_size, zero_point != 0, alphas, count, duo != 0,
+                                           s_best, best, losses, workspace, static_cast<hipStream_t>(stream)));
 }
 
 size_t awq_scale_loss_workspace_bytes(int32_t count, int32_t M, int32_t N, int32_t K) {
@@ -172,7 +196,7 @@ const char* awq_strerror(int status) {
     case AWQ_ERR_SHAPE: return "invalid shape: need M >= 1, N >= 1 with N % 8 == 0, K >= 1";
     case AWQ_ERR_GROUP: return "invalid group size: need group_size in {32, 64, 128, 256} dividing K";
     case AWQ_ERR_ALIGN: return "a buffer pointer is not 16-byte aligned";
-    case AWQ_ERR_UNSUPPORTED: return "unsupported argument combination for this entry point (awq_gemv takes M == 1)";
+    case AWQ_ERR_UNSUPPORTED: return "unsupported argument combination for this entry point (awq_gemv takes M <= 8)";
     case AWQ_ERR_WORKSPACE: return "workspace smaller than awq_gemm_workspace_bytes()";
     case AWQ_ERR_HIP: return "the HIP runtime reported an error while launching";
     default: return "unknown awq status";

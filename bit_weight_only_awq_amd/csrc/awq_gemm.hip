@@ -6,9 +6,12 @@
 // rounding of the product with the group scale) and multiplied on the gfx950
 // fp16 matrix cores with fp32 accumulation.  Two kernels:
 //
-//   * gemm_skinny_kernel (M <= 64, but 33-64 tokens on layers with N >= 8192
-//     and 49-64 tokens on layers with K >= 8192 go to the matrix-core
-//     kernel): bound by the weight stream (and, from
+//   * up to 8 tokens: the single- and few-token kernels of awq_gemv (one
+//     token: the GEMV; 2-8: 4x4x4 MFMA blocks over 32-channel slices).
+//
+//   * gemm_skinny_kernel (9-64 tokens, but 33-64 tokens on layers with
+//     N >= 8192 and 49-64 tokens on layers with K >= 8192 go to the
+//     matrix-core kernel): bound by the weight stream (and, from
 //     ~16 tokens on, by the activation loads).  A workgroup owns NT tiles of
 //     16 output rows, all (<= 4) tiles of 16 tokens and one slice of K; its
 //     lanes load packed weights straight into MFMA B-operand registers (one
@@ -289,15 +292,12 @@ SkinnyPlan plan_skinny(int M, int N, int K) {
   SkinnyPlan p;
   p.mt = (M + 15) / 16;
   // Measured on the Llama-7B decode shapes (4096 x 4096, 4096 -> 11008,
-  // 11008 -> 4096): up to 8 tokens the weight stream rules, and 16-row tiles
-  // with 8 waves of two steps in flight are best (at 8 tokens 6.1 us instead
-  // of 7.0 us for 4096 x 4096); beyond that the activations dominate the load
-  // traffic and wider row tiles (each X fragment reused by NT weight tiles)
-  // win, with K split to keep every compute unit busy.
+  // 11008 -> 4096): from 9 tokens on (up to 8 go to the few-token kernel)
+  // the activations dominate the load traffic and wide row tiles (each X
+  // fragment reused by NT weight tiles) win, with K split to keep every
+  // compute unit busy.
   int target_blocks;
-  if (M <= 8) {
-    p.nt = 1, p.ks = 8, p.spw = 2, target_blocks = 256;
-  } else if (p.mt == 1) {
+  if (p.mt == 1) {
     p.nt = 2, p.ks = 4, p.spw = 2, target_blocks = 512;
   } else {
     p.nt = 4, p.ks = 4, p.spw = 1, target_blocks = 256;
@@ -784,12 +784,11 @@ hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales,
   const uint16_t* sc = static_cast<const uint16_t*>(scales);
   _Float16* Y = static_cast<_Float16*>(y);
   const int gs = log2_group(group_size);
+  if (M <= kMaxGemvTokens) return launch_gemv(x, qweight, scales, qzeros, y, M, N, K, group_size, ZP, stream);
   if (M <= 64 && !gemm_uses_mid(M, N, K)) {
     const SkinnyPlan p = plan_skinny(M, N, K);
     switch (p.mt) {
-      case 1:
-        return p.nt == 1 ? launch_skinny<1, 1, 8, 2, ZP>(p, x, qweight, sc, qzeros, Y, M, N, K, gs, workspace, stream)
-                         : launch_skinny<1, 2, 4, 2, ZP>(p, x, qweight, sc, qzeros, Y, M, N, K, gs, workspace, stream);
+      case 1: return launch_skinny<1, 2, 4, 2, ZP>(p, x, qweight, sc, qzeros, Y, M, N, K, gs, workspace, stream);
       case 2: return launch_skinny<2, 4, 4, 1, ZP>(p, x, qweight, sc, qzeros, Y, M, N, K, gs, workspace, stream);
       case 3: return launch_skinny<3, 4, 4, 1, ZP>(p, x, qweight, sc, qzeros, Y, M, N, K, gs, workspace, stream);
       default: return launch_skinny<4, 4, 4, 1, ZP>(p, x, qweight, sc, qzeros, Y, M, N, K, gs, workspace, stream);
@@ -801,6 +800,7 @@ hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales,
 }  // namespace
 
 size_t gemm_workspace_bytes(int M, int N, int K) {
+  if (M <= kMaxGemvTokens) return 0;
   if (M <= 64 && !gemm_uses_mid(M, N, K)) return skinny_workspace_bytes(plan_skinny(M, N, K));
   const LargePlan p = gemm_uses_mid(M, N, K) ? plan_mid(M, N, K) : plan_large(M, N, K);
   return p.splits > 1 ? kCounterBytes + (size_t)p.splits * M * N * 4 : 0;

@@ -14,8 +14,11 @@ hipError_t launch_pack(const void* w, int N, int K, int group_size, bool zero_po
 hipError_t launch_dequant(const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* w_out,
                           int N, int K, int group_size, bool zero_point, hipStream_t stream);
 
+// 1 <= M <= kMaxGemvTokens: one token on the single-token kernel, 2-8 on the
+// few-token kernel.
+constexpr int kMaxGemvTokens = 8;
 hipError_t launch_gemv(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros,
-                       void* y, int N, int K, int group_size, bool zero_point, hipStream_t stream);
+                       void* y, int M, int N, int K, int group_size, bool zero_point, hipStream_t stream);
 
 // Workspace bytes launch_gemm needs for an M x N x K product (0: none).
 size_t gemm_workspace_bytes(int M, int N, int K);
@@ -29,9 +32,17 @@ hipError_t launch_gemm(const void* x, const uint32_t* qweight, const void* scale
 // Candidate scales for the activation-aware scale search (at most
 // kMaxScaleCandidates exponents per call; `alphas` is a host array).
 constexpr int kMaxScaleCandidates = 64;
-size_t scale_candidates_workspace_bytes(int M, int K);
-hipError_t launch_scale_candidates(const void* x, int M, int K, const float* alphas, int count, float* s,
-                                   void* workspace, hipStream_t stream);
+// With w != NULL (duo scaling) the candidates also divide by a weight
+// statistic of w [N][K]; N is ignored otherwise.
+size_t scale_candidates_workspace_bytes(int M, int N, int K);
+hipError_t launch_scale_candidates(const void* x, int M, int K, const void* w, int N, const float* alphas, int count,
+                                   float* s, void* workspace, hipStream_t stream);
+// The whole search: candidates, losses, and the first candidate with the
+// smallest loss (index to best[0], its scales to s_best).
+size_t scale_search_workspace_bytes(int count, int M, int N, int K);
+hipError_t launch_scale_search(const void* x, const void* w, int M, int N, int K, int group_size, bool zero_point,
+                               const float* alphas, int count, bool duo, float* s_best, int32_t* best, double* losses,
+                               void* workspace, hipStream_t stream);
 
 // e[c][n][k] = fp16(Dq(Q(fp16(w[n][k] * s[c][k]))) / s[c][k] - w[n][k]) for each candidate c.
 hipError_t launch_scale_error(const void* w, const float* s, int count, int N, int K, int group_size, bool zero_point,

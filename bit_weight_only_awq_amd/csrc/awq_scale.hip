@@ -11,7 +11,11 @@
 // ingredients as activation statistics and per-channel scaling.  The pages do
 // not give the family of candidate scales; the one used here is
 //   s_k = a_k ^ alpha,  a_k = max(mean_m |x_mk|, 1e-4)
-// for a grid of exponents alpha (alpha = 0 is plain round-to-nearest).
+// for a grid of exponents alpha (alpha = 0 is plain round-to-nearest), or,
+// with duo scaling (the calibration parameter duo_scaling, "scale weights and
+// activations", section 自定义校准策略 / 校准参数全景), also divided by a
+// weight statistic of the channel:
+//   s_k = a_k ^ alpha / b_k ^ (1 - alpha),  b_k = max(mean_n |w_nk|, 1e-4).
 //
 // L(s) is evaluated as || X e^T ||_F with e = Q(W s) s^-1 - W (built by
 // scale_error_kernel next to the quantizer): the same quantity, one dense
@@ -27,11 +31,13 @@ namespace {
 // ---------------------------------------------------------------------------
 // Activation statistics and candidates.
 // ---------------------------------------------------------------------------
-constexpr int kStatRows = 64;  // rows of X summed per partial
+constexpr int kStatRows = 64;  // rows of X (or W) summed per partial
 constexpr float kActFloor = 1e-4f;
+constexpr float kWeightFloor = 1e-4f;
 
-// partial[b][k] = sum over rows 64 b .. 64 b + 63 of |x_mk|, in row order.
-// One thread per channel; consecutive threads read consecutive channels.
+// partial[b][k] = sum over rows 64 b .. 64 b + 63 of |x_mk|, in row order
+// (activations, or weights for duo scaling).  One thread per channel;
+// consecutive threads read consecutive channels.
 __global__ __launch_bounds__(256) void act_partial_kernel(const _Float16* __restrict__ x, int M, int K,
                                                           float* __restrict__ partial) {
   const int k = blockIdx.x * 256 + threadIdx.x;
@@ -46,15 +52,51 @@ struct Alphas {
   float v[kMaxScaleCandidates];
 };
 
-// a_k = max((sum of the partials in order) / M, 1e-4); s[c][k] = a_k ^ alpha_c.
-__global__ __launch_bounds__(256) void candidates_kernel(const float* __restrict__ partial, int nparts, int M, int K,
+// a_k = max((sum of the partials in order) / M, 1e-4); s[c][k] = a_k ^ alpha_c,
+// or with duo scaling (wparts > 0) b_k = max((sum of the weight partials in
+// order) / N, 1e-4) and s[c][k] = a_k ^ alpha_c / b_k ^ (1 - alpha_c).
+__global__ __launch_bounds__(256) void candidates_kernel(const float* __restrict__ partial, int nparts, int M,
+                                                         const float* __restrict__ wpartial, int wparts, int N, int K,
                                                          Alphas alphas, int count, float* __restrict__ s) {
   const int k = blockIdx.x * 256 + threadIdx.x;
   if (k >= K) return;
   float sum = 0.0f;
   for (int b = 0; b < nparts; ++b) sum += partial[(size_t)b * K + k];
   const float a = fmaxf(sum / (float)M, kActFloor);
-  for (int c = 0; c < count; ++c) s[(size_t)c * K + k] = alphas.v[c] == 0.0f ? 1.0f : powf(a, alphas.v[c]);
+  if (wparts == 0) {
+    for (int c = 0; c < count; ++c) s[(size_t)c * K + k] = alphas.v[c] == 0.0f ? 1.0f : powf(a, alphas.v[c]);
+    return;
+  }
+  float wsum = 0.0f;
+  for (int b = 0; b < wparts; ++b) wsum += wpartial[(size_t)b * K + k];
+  const float bk = fmaxf(wsum / (float)N, kWeightFloor);
+  for (int c = 0; c < count; ++c) {
+    const float al = alphas.v[c];
+    const float num = al == 0.0f ? 1.0f : al == 1.0f ? a : powf(a, al);
+    const float den = al == 1.0f ? 1.0f : al == 0.0f ? bk : powf(bk, 1.0f - al);
+    s[(size_t)c * K + k] = num / den;
+  }
+}
+
+// The search's choice: the first candidate with the smallest loss (a NaN
+// loss is never chosen), written to best[0], and its scale vector copied to
+// s_best.  Every workgroup finds the same index (count <= 64) and copies
+// its share of the K channels.
+__global__ __launch_bounds__(256) void scale_choose_kernel(const double* __restrict__ loss, int count,
+                                                           const float* __restrict__ s_all, int K,
+                                                           float* __restrict__ s_best, int32_t* __restrict__ best) {
+  int idx = 0;
+  double lo = __builtin_inf();
+  for (int c = 0; c < count; ++c) {
+    const double v = loss[c];
+    if (v < lo) {
+      lo = v;
+      idx = c;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) best[0] = idx;
+  const float* src = s_all + (size_t)idx * K;
+  for (int k = blockIdx.x * 256 + threadIdx.x; k < K; k += gridDim.x * 256) s_best[k] = src[k];
 }
 
 // dst[r][k] = fp16(src[r][k] * s[k]) (or / s[k]): fp32 product or correctly
@@ -293,20 +335,26 @@ int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 128 ? 7 : 8; }
 
 }  // namespace
 
-size_t scale_candidates_workspace_bytes(int M, int K) {
-  return align256((size_t)((M + kStatRows - 1) / kStatRows) * K * 4);
+size_t scale_candidates_workspace_bytes(int M, int N, int K) {
+  return align256((size_t)((M + kStatRows - 1) / kStatRows) * K * 4) +
+         (N > 0 ? align256((size_t)((N + kStatRows - 1) / kStatRows) * K * 4) : 0);
 }
 
-hipError_t launch_scale_candidates(const void* x, int M, int K, const float* alphas, int count, float* s,
-                                   void* workspace, hipStream_t stream) {
+hipError_t launch_scale_candidates(const void* x, int M, int K, const void* w, int N, const float* alphas, int count,
+                                   float* s, void* workspace, hipStream_t stream) {
   const int nparts = (M + kStatRows - 1) / kStatRows;
+  const int wparts = w ? (N + kStatRows - 1) / kStatRows : 0;
   float* partial = static_cast<float*>(workspace);
+  float* wpartial = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256((size_t)nparts * K * 4));
   hipLaunchKernelGGL(act_partial_kernel, dim3((K + 255) / 256, nparts), dim3(256), 0, stream,
                      static_cast<const _Float16*>(x), M, K, partial);
+  if (wparts > 0)
+    hipLaunchKernelGGL(act_partial_kernel, dim3((K + 255) / 256, wparts), dim3(256), 0, stream,
+                       static_cast<const _Float16*>(w), N, K, wpartial);
   Alphas a;
   for (int c = 0; c < kMaxScaleCandidates; ++c) a.v[c] = c < count ? alphas[c] : 0.0f;
-  hipLaunchKernelGGL(candidates_kernel, dim3((K + 255) / 256), dim3(256), 0, stream, partial, nparts, M, K, a, count,
-                     s);
+  hipLaunchKernelGGL(candidates_kernel, dim3((K + 255) / 256), dim3(256), 0, stream, partial, nparts, M, wpartial,
+                     wparts, N, K, a, count, s);
   return hipGetLastError();
 }
 
@@ -354,6 +402,34 @@ hipError_t launch_scale_loss(const void* x, const void* w, const float* s, int c
   err = launch_sumsq(static_cast<const _Float16*>(x), e, M, N, K, T, tiles_m, grid, partial, 0, nullptr, false, stream);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(loss_finalize_kernel, dim3(count), dim3(256), 0, stream, partial, tiles_m * tiles_n, loss);
+  return hipGetLastError();
+}
+
+// Workspace of the whole search: every candidate's scales, the candidates'
+// statistics, the loss product's workspace and the losses.
+size_t scale_search_workspace_bytes(int count, int M, int N, int K) {
+  return align256((size_t)count * K * 4) + scale_candidates_workspace_bytes(M, N, K) +
+         scale_loss_workspace_bytes(count, M, N, K) + align256((size_t)count * 8);
+}
+
+hipError_t launch_scale_search(const void* x, const void* w, int M, int N, int K, int group_size, bool zero_point,
+                               const float* alphas, int count, bool duo, float* s_best, int32_t* best, double* losses,
+                               void* workspace, hipStream_t stream) {
+  char* ws = static_cast<char*>(workspace);
+  float* s_all = reinterpret_cast<float*>(ws);
+  ws += align256((size_t)count * K * 4);
+  void* cand_ws = ws;
+  ws += scale_candidates_workspace_bytes(M, N, K);
+  void* loss_ws = ws;
+  ws += scale_loss_workspace_bytes(count, M, N, K);
+  double* L = losses ? losses : reinterpret_cast<double*>(ws);
+  hipError_t err = launch_scale_candidates(x, M, K, duo ? w : nullptr, N, alphas, count, s_all, cand_ws, stream);
+  if (err != hipSuccess) return err;
+  err = launch_scale_loss(x, w, s_all, count, M, N, K, group_size, zero_point, loss_ws, L, stream);
+  if (err != hipSuccess) return err;
+  int blocks = (K + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(scale_choose_kernel, dim3(blocks), dim3(256), 0, stream, L, count, s_all, K, s_best, best);
   return hipGetLastError();
 }
 

@@ -93,14 +93,19 @@ int awq_dequant(const uint32_t* qweight, const void* scales, const uint32_t* qze
                 int32_t N, int32_t K, int32_t group_size, int32_t zero_point, void* stream);
 
 /*
- * awq_gemv - single-token quantized linear layer, y = x . W'^T.
+ * awq_gemv - single- and few-token quantized linear layer, Y = X . W'^T.
  *
- * The GEMV variant ("AI-Research-SKILLs AWQ 高级使用指南", section WQLinear 内核全景,
- * WQLinear_GEMV: single-token generation, batch size 1 only).
- * x in fp16 [M][K] with M == 1 (AWQ_ERR_UNSUPPORTED otherwise);
- * y out fp16 [M][N].  Accumulation is fp32, the output rounded once to fp16.
- * Each output meets |y - y_ref| <= 1e-3 * sum_k |x_k w'_k| against the exact
- * product, and is bit-reproducible run to run.
+ * The GEMV variants ("AI-Research-SKILLs AWQ 高级使用指南", section WQLinear 内核全景,
+ * WQLinear_GEMV: single-token generation, batch size 1; WQLinear_GEMVFast:
+ * the fastest few-token decoding; "Optimization Awq", section "Backends de
+ * kernel": GEMV for batch size 1).  One token runs on the single-token
+ * kernel (fp32 dot products); 2-8 tokens on the few-token kernel (the
+ * products on the fp16 matrix cores from exact q - z, the group scale applied
+ * to each 32-channel fp32 sum).
+ * X in fp16 [M][K] with 1 <= M <= 8 (AWQ_ERR_UNSUPPORTED above; awq_gemm
+ * takes any M); Y out fp16 [M][N].  Accumulation is fp32, the output rounded
+ * once to fp16.  Each output meets |y - y_ref| <= 1e-3 * sum_k |x_k w'_k|
+ * against the exact product, and is bit-reproducible run to run.
  */
 int awq_gemv(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros,
              void* y, int32_t M, int32_t N, int32_t K, int32_t group_size, int32_t zero_point,
@@ -114,11 +119,12 @@ int awq_gemv(const void* x, const uint32_t* qweight, const void* scales, const u
  * decoded to fp16 in registers and multiplied on the fp16 matrix cores with
  * fp32 accumulation; the output is rounded once to fp16.
  * X in fp16 [M][K]; Y out fp16 [M][N].  Same accuracy contract as awq_gemv.
- * Deterministic run to run.
+ * Deterministic run to run.  Up to 8 tokens it runs awq_gemv's kernels (the
+ * same bits as awq_gemv) and needs no workspace.
  *
  * workspace: device scratch of at least awq_gemm_workspace_bytes(M, N, K,
  * group_size) bytes, 16-byte aligned, owned by the caller (may be NULL when
- * that size is 0).  For small M (<= 64, except 33-64 tokens on layers with
+ * that size is 0).  For small M (9-64, except 33-64 tokens on layers with
  * N >= 8192 and 49-64 tokens on layers with K >= 8192, which take the
  * matrix-core path below) the K dimension is split across workgroups: the
  * workspace then starts with a 512 KiB region of 32-bit per-tile counters,
@@ -140,6 +146,7 @@ int awq_gemm(const void* x, const uint32_t* qweight, const void* scales, const u
 /* Bytes of workspace awq_gemm needs for this shape (0 when it needs none). */
 size_t awq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t group_size);
 
+
 /*
  * awq_scale_candidates - candidate per-input-channel scales for the
  * activation-aware scale search.
@@ -147,21 +154,49 @@ size_t awq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t group_s
  * "AI-Research-SKILLs AWQ 高级使用指南", section 算法原理: salient channels are
  * found from the activation distribution and scaled up before quantization;
  * "AWQ Activation-aware Weight Quantization (Lin 2023年)": activation
- * statistics and per-channel scaling.  The pages give no candidate family;
- * this one is
+ * statistics and per-channel scaling; section 自定义校准策略 (校准参数全景):
+ * duo_scaling scales weights and activations.  The pages give no candidate
+ * family; this one is
  *   a_k = max(mean_m |x[m][k]|, 1e-4),   s[c][k] = a_k ^ alphas[c]
- * (fp32; the mean is an fp32 sum in row order divided by M; alphas[c] == 0
- * gives exactly 1).
+ * (alphas[c] == 0 gives exactly 1), or with duo != 0
+ *   b_k = max(mean_n |w[n][k]|, 1e-4),   s[c][k] = a_k ^ alphas[c] / b_k ^ (1 - alphas[c])
+ * (fp32; each mean is an fp32 sum in row order divided by the row count).
  * x       in   fp16 [M][K] calibration activations (device).
+ * w, N    in   fp16 [N][K] weights (device), read only with duo != 0 (may be
+ *              NULL, and N is ignored, otherwise).
  * alphas  in   HOST array of `count` exponents, 1 <= count <= 64.
  * s       out  fp32 [count][K] (device).
- * workspace: device scratch of awq_scale_candidates_workspace_bytes(M, K)
- * bytes, 16-byte aligned, contents not needed before or after the call.
- * K must be a multiple of 8.  Deterministic.
+ * workspace: device scratch of awq_scale_candidates_workspace_bytes(M,
+ * duo ? N : 0, K) bytes, 16-byte aligned, contents not needed before or
+ * after the call.  K must be a multiple of 8.  Deterministic.
  */
-int awq_scale_candidates(const void* x, int32_t M, int32_t K, const float* alphas, int32_t count, float* s,
-                         void* workspace, size_t workspace_bytes, void* stream);
-size_t awq_scale_candidates_workspace_bytes(int32_t M, int32_t K);
+int awq_scale_candidates(const void* x, int32_t M, int32_t K, const void* w, int32_t N, int32_t duo,
+                         const float* alphas, int32_t count, float* s, void* workspace, size_t workspace_bytes,
+                         void* stream);
+size_t awq_scale_candidates_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
+/*
+ * awq_scale_search - the activation-aware scale search of one linear layer
+ * ("AI-Research-SKILLs AWQ 高级使用指南", section 算法原理: choose the
+ * per-channel scale s that makes L(s) = ||Q(W * s)(s^-1 * X) - W * X||
+ * small): the candidates of awq_scale_candidates (duo scaling with duo != 0),
+ * the loss of each as awq_scale_loss computes it, and the choice of the
+ * first candidate with the smallest loss (a NaN loss is never chosen), all on
+ * the device: nothing is copied to the host and the call does not wait.
+ * x       in   fp16 [M][K] calibration activations.
+ * w       in   fp16 [N][K] unquantized weights.
+ * alphas  in   HOST array of `count` exponents, 1 <= count <= 64.
+ * s_best  out  fp32 [K] (device): the chosen scale vector.
+ * best    out  int32 [1] (device): the index of the chosen candidate.
+ * losses  out  fp64 [count] (device, 8-byte aligned), or NULL.
+ * workspace: device scratch of awq_scale_search_workspace_bytes(count, M, N,
+ * K) bytes, 16-byte aligned; contents not needed before or after.
+ * Same shape rules as awq_pack; deterministic.
+ */
+int awq_scale_search(const void* x, const void* w, int32_t M, int32_t N, int32_t K, int32_t group_size,
+                     int32_t zero_point, const float* alphas, int32_t count, int32_t duo, float* s_best,
+                     int32_t* best, double* losses, void* workspace, size_t workspace_bytes, void* stream);
+size_t awq_scale_search_workspace_bytes(int32_t count, int32_t M, int32_t N, int32_t K);
 
 /*
  * awq_scale_loss - reconstruction error of the activation-aware scaling,

@@ -115,7 +115,7 @@ def test_gemv_gemm_validation(lib):
     gemv = lambda M, N, K, g, zp, **kw: lib.awq_gemv(  # noqa: E731
         kw.get("x", A) or None, kw.get("qw", B) or None, kw.get("sc", C) or None, kw.get("qz", D) or None,
         kw.get("y", E) or None, M, N, K, g, zp, None)
-    assert gemv(2, 8, 128, 32, 1) == awq.AWQ_ERR_UNSUPPORTED
+    assert gemv(9, 8, 128, 32, 1) == awq.AWQ_ERR_UNSUPPORTED  # more than 8 tokens: awq_gemm
     assert gemv(0, 8, 128, 32, 1) == awq.AWQ_ERR_SHAPE
     assert gemv(1, 8, 128, 100, 1) == awq.AWQ_ERR_GROUP
     assert gemv(1, 8, 128, 32, 1, y=0) == awq.AWQ_ERR_NULL
@@ -165,7 +165,8 @@ def test_binding_rejects_host_tensors():
 def test_scale_search_validation(lib):
     alphas = (ctypes.c_float * 2)(0.0, 0.5)
     cand = lambda M, K, cnt, **kw: lib.awq_scale_candidates(  # noqa: E731
-        kw.get("x", A) or None, M, K, ctypes.cast(alphas, ctypes.c_void_p) if kw.get("al", 1) else None, cnt,
+        kw.get("x", A) or None, M, K, kw.get("w", None), kw.get("N", 0), kw.get("duo", 0),
+        ctypes.cast(alphas, ctypes.c_void_p) if kw.get("al", 1) else None, cnt,
         kw.get("s", B) or None, kw.get("ws", C) or None, kw.get("wsb", 1 << 30), None)
     assert cand(0, 64, 2) == awq.AWQ_ERR_SHAPE
     assert cand(4, 12, 2) == awq.AWQ_ERR_SHAPE
@@ -175,7 +176,29 @@ def test_scale_search_validation(lib):
     assert cand(4, 64, 2, s=0) == awq.AWQ_ERR_NULL
     assert cand(4, 64, 2, x=A + 2) == awq.AWQ_ERR_ALIGN
     assert cand(4, 64, 2, wsb=0) == awq.AWQ_ERR_WORKSPACE
-    assert awq.load_library().awq_scale_candidates_workspace_bytes(100, 64) >= 2 * 64 * 4
+    assert cand(4, 64, 2, duo=1, N=8) == awq.AWQ_ERR_NULL  # duo scaling reads w
+    assert cand(4, 64, 2, duo=1, N=0, w=D) == awq.AWQ_ERR_SHAPE
+    assert cand(4, 64, 2, duo=1, N=8, w=D + 4) == awq.AWQ_ERR_ALIGN
+    wsb = awq.load_library().awq_scale_candidates_workspace_bytes
+    assert wsb(100, 0, 64) >= 2 * 64 * 4
+    assert wsb(100, 300, 64) >= wsb(100, 0, 64) + 5 * 64 * 4  # the weight statistic's partial sums
+    srch = lambda cnt, M, N, K, g, **kw: lib.awq_scale_search(  # noqa: E731
+        kw.get("x", A) or None, kw.get("w", B) or None, M, N, K, g, 1,
+        ctypes.cast(alphas, ctypes.c_void_p) if kw.get("al", 1) else None, cnt, kw.get("duo", 0),
+        kw.get("s", C) or None, kw.get("best", D) or None, kw.get("losses", None), kw.get("ws", E) or None,
+        kw.get("wsb", 1 << 40), None)
+    assert srch(2, 4, 12, 128, 32) == awq.AWQ_ERR_SHAPE
+    assert srch(2, 4, 8, 100, 32) == awq.AWQ_ERR_GROUP
+    assert srch(0, 4, 8, 128, 32) == awq.AWQ_ERR_SHAPE
+    assert srch(65, 4, 8, 128, 32) == awq.AWQ_ERR_SHAPE
+    assert srch(2, 0, 8, 128, 32) == awq.AWQ_ERR_SHAPE
+    assert srch(2, 4, 8, 128, 32, al=0) == awq.AWQ_ERR_NULL
+    assert srch(2, 4, 8, 128, 32, best=0) == awq.AWQ_ERR_NULL
+    assert srch(2, 4, 8, 128, 32, best=D + 2) == awq.AWQ_ERR_ALIGN
+    assert srch(2, 4, 8, 128, 32, losses=E + 4) == awq.AWQ_ERR_ALIGN
+    need = awq.load_library().awq_scale_search_workspace_bytes(2, 4, 8, 128)
+    assert need >= 2 * 128 * 4 + 2 * 8 * 128 * 2
+    assert srch(2, 4, 8, 128, 32, wsb=need - 1) == awq.AWQ_ERR_WORKSPACE
     loss = lambda cnt, M, N, K, g, **kw: lib.awq_scale_loss(  # noqa: E731
         kw.get("x", A) or None, kw.get("w", B) or None, kw.get("s", C) or None, cnt, M, N, K, g, 1,
         kw.get("ws", D) or None, kw.get("wsb", 1 << 40), kw.get("loss", E) or None, None)

@@ -66,8 +66,8 @@ def test_gemm_ragged_tiles(M, N, K, g):
     check(M, N, K, g, False)
 
 
-@pytest.mark.parametrize("M,N,K,g", [(7, 264, 2080, 32), (40, 8, 4096, 128), (64, 4104, 11008, 128),
-                                     (2, 40, 1664, 64), (17, 136, 8192, 256)])
+@pytest.mark.parametrize("M,N,K,g", [(9, 264, 2080, 32), (40, 8, 4096, 128), (64, 4104, 11008, 128),
+                                     (12, 40, 1664, 64), (17, 136, 8192, 256)])
 def test_gemm_split_k(M, N, K, g):
     """Shapes whose K is split across workgroups (partials in the workspace,
     reduced by the last workgroup of each tile), with ragged row tiles and
@@ -84,7 +84,7 @@ def test_gemm_split_k_workspace_reuse():
     awq = G.lib()
     g = 128
     shapes = [(16, 4096, 4096), (64, 4104, 11008), (4, 11008, 4096), (300, 1024, 8192), (64, 1024, 8192),
-              (3, 4096, 4096)]
+              (3, 4096, 4096), (9, 264, 4096)]
     need = max(awq.awq_gemm_workspace_bytes(M, N, K, g) for M, N, K in shapes)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     for M, N, K in shapes:
@@ -109,7 +109,7 @@ def test_gemm_split_k_back_to_back_new_data():
     zeroed workspace and meet the oracle's tolerance."""
     awq = G.lib()
     g = 128
-    for M, N, K in [(16, 4096, 4096), (56, 1032, 8192), (7, 264, 4096)]:
+    for M, N, K in [(16, 4096, 4096), (56, 1032, 8192), (9, 264, 4096)]:
         need = awq.awq_gemm_workspace_bytes(M, N, K, g)
         assert need > 0
         ws = torch.zeros(need, dtype=torch.uint8, device="cuda")

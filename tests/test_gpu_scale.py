@@ -24,16 +24,20 @@ def gpu_losses(X16, W16, S, g, zp):
     return loss.cpu().numpy()
 
 
+@pytest.mark.parametrize("duo", [False, True])
 @pytest.mark.parametrize("M,K", [(1, 8), (64, 512), (300, 4096), (129, 11008)])
-def test_scale_candidates_match_oracle(M, K):
+def test_scale_candidates_match_oracle(M, K, duo):
     awq = G.lib()
     X = workloads.activations(M, K, cfg=6, layer=K)
+    W = workloads.weight(72, K, cfg=6, layer=K, row_offset=True)
+    W[:, 3] = 0  # an all-zero weight channel takes the floor
     alphas = [0.0, 0.05, 0.25, 0.5, 0.95, 1.0]
-    s = awq.awq_scale_candidates(G.dev_f16(X), alphas).cpu().numpy()
-    ref = O.scale_candidates(X, alphas)
+    s = awq.awq_scale_candidates(G.dev_f16(X), alphas, G.dev_f16(W) if duo else None).cpu().numpy()
+    ref = O.scale_candidates(X, alphas, W if duo else None)
     assert s.shape == ref.shape and s.dtype == np.float32
-    assert np.array_equal(s[0], np.ones(K, np.float32))
-    # fp32 sum in row order and powf against fp64 mean and power
+    if not duo:
+        assert np.array_equal(s[0], np.ones(K, np.float32))
+    # fp32 sums in row order and powf against fp64 means and powers
     assert np.max(np.abs(s.astype(np.float64) / ref.astype(np.float64) - 1)) <= 1e-5
 
 
@@ -75,28 +79,63 @@ def test_scale_loss_exact_cases():
     assert got[0] > 0 and got[1] == got[0]
 
 
+def check_choice(got_losses, got_best, losses, best, what):
+    """The device's losses within tolerance of the oracle's, and its choice the
+    oracle's unless the two best candidates are within twice the tolerance
+    (then any candidate that close to the best is a correct choice)."""
+    losses = np.array(losses)
+    assert np.all(np.abs(got_losses - losses) <= LOSS_TOL * losses), what
+    order = np.argsort(losses, kind="stable")
+    if losses[order[1]] - losses[order[0]] > 2 * LOSS_TOL * losses[order[0]]:
+        assert got_best == best, (what, got_best, best)
+    else:
+        assert losses[got_best] <= losses[order[0]] * (1 + 2 * LOSS_TOL), what
+
+
+@pytest.mark.parametrize("duo", [False, True])
 @pytest.mark.parametrize("zp", [True, False])
-def test_search_scale_end_to_end(zp):
-    """The GPU search (candidates, losses, smallest loss) against the oracle's:
-    same losses within tolerance and the same choice unless the two best
-    candidates are within tolerance of each other."""
+def test_search_scale_end_to_end(zp, duo):
+    """awq_scale_search (candidates, losses and the choice, all on the device)
+    against the oracle's search; the chosen scale vector is the chosen
+    candidate's, bit for bit."""
     awq = G.lib()
     N, K, M, g = 512, 1024, 64, 128
     W = workloads.weight(N, K, cfg=6, layer=3)
     X = workloads.activations(M, K, cfg=6, layer=3)
     alphas = [i / 20 for i in range(20)]
-    res = awq.search_scale(G.dev_f16(X), G.dev_f16(W), g, zp, alphas)
-    best, S, losses = O.search_scale(W, X, g, zp, alphas)
-    got = np.array(res.losses)
-    assert np.all(np.abs(got - np.array(losses)) <= LOSS_TOL * np.array(losses))
-    i = alphas.index(res.alpha)
-    order = np.argsort(losses)
-    if losses[order[1]] - losses[order[0]] > 2 * LOSS_TOL * losses[order[0]]:
-        assert i == best
-    else:
-        assert losses[i] <= losses[order[0]] * (1 + 2 * LOSS_TOL)
-    assert losses[best] < losses[0], "scaling the outlier channels must beat plain rounding here"
+    x, w = G.dev_f16(X), G.dev_f16(W)
+    res = awq.search_scale(x, w, g, zp, alphas, duo=duo)
+    cands = awq.awq_scale_candidates(x, alphas, w if duo else None)
+    torch.cuda.synchronize()
+    best, S, losses = O.search_scale(W, X, g, zp, alphas, duo=duo)
+    i = int(res.best.cpu().item())
+    check_choice(res.losses.cpu().numpy(), i, losses, best, f"zp={zp} duo={duo}")
+    assert res.alpha == alphas[i]
+    assert torch.equal(res.scale, cands[i])
     assert np.max(np.abs(res.scale.cpu().numpy() / S[i] - 1)) <= 1e-5
+    assert losses[best] < losses[0] * (0.8 if not duo else 1.0), "scaling must beat plain rounding here"
+
+
+@pytest.mark.parametrize("zp", [True, False])
+@pytest.mark.parametrize("g", [32, 128])
+def test_scaled_weight_codes_bit_exact(g, zp):
+    """The quantizer on scaled weights: awq_scale_columns (fp16 of the fp32
+    product W * s) then awq_pack, against the oracle's pack of
+    scale_weights(W, s), bit for bit, for an activation-only and a duo
+    candidate."""
+    awq = G.lib()
+    N, K, M = 264, 1024, 48
+    W = workloads.weight(N, K, cfg=6, layer=11, row_offset=True)
+    X = workloads.activations(M, K, cfg=6, layer=11)
+    for s in (O.scale_candidates(X, [0.5])[0], O.scale_candidates(X, [0.3], W)[0]):
+        ws = awq.awq_scale_columns(G.dev_f16(W), torch.from_numpy(s).cuda())
+        assert np.array_equal(G.host_f16_bits(ws), O.scale_weights(W, s).view(np.uint16))
+        qw, sc, qz = awq.awq_pack(ws, g, zp)
+        oq, os_, oz = O.pack(O.scale_weights(W, s), g, zp)
+        assert np.array_equal(G.host_u32(qw), oq)
+        assert np.array_equal(G.host_f16_bits(sc), os_)
+        if zp:
+            assert np.array_equal(G.host_u32(qz), oz)
 
 
 def test_scale_loss_full_size_llama7b():
@@ -110,6 +149,20 @@ def test_scale_loss_full_size_llama7b():
     for c in range(2):
         ref = O.recon_loss(W, X, S[c], g, True)
         assert abs(got[c] - ref) <= LOSS_TOL * ref, (c, got[c], ref)
+
+
+def test_scale_search_full_size_llama7b_duo():
+    """awq_scale_search with duo scaling on a Llama-7B q_proj, 256 tokens,
+    four candidates: losses and choice against the oracle."""
+    awq = G.lib()
+    N = K = 4096
+    M, g = 256, 128
+    W = workloads.weight(N, K, cfg=6, layer=8)
+    X = workloads.activations(M, K, cfg=6, layer=8)
+    alphas = [0.2, 0.4, 0.6, 0.8]
+    res = awq.awq_scale_search(G.dev_f16(X), G.dev_f16(W), g, True, alphas, duo=True)
+    best, S, losses = O.search_scale(W, X, g, True, alphas, duo=True)
+    check_choice(res.losses.cpu().numpy(), int(res.best.cpu().item()), losses, best, "7B duo")
 
 
 def test_scale_loss_deterministic():
