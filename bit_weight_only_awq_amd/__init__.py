@@ -37,11 +37,13 @@ AWQ_ERR_ALIGN = -4
 AWQ_ERR_UNSUPPORTED = -5
 AWQ_ERR_WORKSPACE = -6
 AWQ_ERR_HIP = -7
+AWQ_ERR_SCRATCH = -8
 
 EXPORTED = ("awq_pack", "awq_dequant", "awq_gemv", "awq_gemm", "awq_gemm_workspace_bytes", "awq_strerror",
             "awq_scale_candidates", "awq_scale_candidates_workspace_bytes", "awq_scale_loss",
             "awq_scale_loss_workspace_bytes", "awq_scale_columns", "awq_clip_search",
-            "awq_clip_search_workspace_bytes", "awq_scale_search", "awq_scale_search_workspace_bytes")
+            "awq_clip_search_workspace_bytes", "awq_scale_search", "awq_scale_search_workspace_bytes",
+            "awq_gemm_noalloc", "awq_gemm_noalloc_max_workspace_bytes")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -82,6 +84,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.awq_scale_search.restype = ctypes.c_int
     lib.awq_scale_search_workspace_bytes.argtypes = [I32, I32, I32, I32]
     lib.awq_scale_search_workspace_bytes.restype = SZ
+    lib.awq_gemm_noalloc.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, P]
+    lib.awq_gemm_noalloc.restype = ctypes.c_int
+    lib.awq_gemm_noalloc_max_workspace_bytes.argtypes = []
+    lib.awq_gemm_noalloc_max_workspace_bytes.restype = SZ
     lib.awq_scale_loss.argtypes = [P, P, P, I32, I32, I32, I32, I32, I32, P, SZ, P, P]
     lib.awq_scale_loss.restype = ctypes.c_int
     lib.awq_scale_loss_workspace_bytes.argtypes = [I32, I32, I32, I32]
@@ -227,6 +233,24 @@ def awq_gemm(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, qzero
     st = lib.awq_gemm(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros) if zero_point else None, _ptr(y), M, N, K,
                       group_size, int(bool(zero_point)), _ptr(workspace), ws_bytes, _stream(x))
     _check(st, "awq_gemm")
+    return y
+
+
+def awq_gemm_noalloc(x: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, qzeros: Optional[torch.Tensor],
+                     N: int, K: int, group_size: int = 128, zero_point: bool = True,
+                     y: torch.Tensor = None) -> torch.Tensor:
+    """awq_gemm with the library's fixed device scratch as the split-K
+    workspace: the C call allocates nothing (``y`` must be passed, so that
+    this wrapper allocates nothing either).  Calls that may overlap on one
+    GPU share the scratch and race."""
+    lib = load_library()
+    if y is None:
+        raise ValueError("awq_gemm_noalloc takes a preallocated output y")
+    if x.dtype != torch.float16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D float16 tensor [M, K]")
+    st = lib.awq_gemm_noalloc(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(qzeros) if zero_point else None, _ptr(y),
+                              x.shape[0], N, K, group_size, int(bool(zero_point)), _stream(x))
+    _check(st, "awq_gemm_noalloc")
     return y
 
 

@@ -199,6 +199,9 @@ const char* awq_strerror(int status) {
     case AWQ_ERR_UNSUPPORTED: return "unsupported argument combination for this entry point (awq_gemv takes M <= 8)";
     case AWQ_ERR_WORKSPACE: return "workspace smaller than awq_gemm_workspace_bytes()";
     case AWQ_ERR_HIP: return "the HIP runtime reported an error while launching";
+    case AWQ_ERR_SCRATCH:
+      return "the shape needs more split-K workspace than awq_gemm_noalloc's fixed scratch "
+             "(awq_gemm_noalloc_max_workspace_bytes()); use awq_gemm with a workspace";
     default: return "unknown awq status";
   }
 }

@@ -799,6 +799,8 @@ hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales,
 
 }  // namespace
 
+size_t gemm_counter_bytes() { return kCounterBytes; }
+
 size_t gemm_workspace_bytes(int M, int N, int K) {
   if (M <= kMaxGemvTokens) return 0;
   if (M <= 64 && !gemm_uses_mid(M, N, K)) return skinny_workspace_bytes(plan_skinny(M, N, K));

@@ -22,6 +22,9 @@ hipError_t launch_gemv(const void* x, const uint32_t* qweight, const void* scale
 
 // Workspace bytes launch_gemm needs for an M x N x K product (0: none).
 size_t gemm_workspace_bytes(int M, int N, int K);
+// Bytes of the per-tile counter region at the start of every non-empty
+// workspace (the part that must be zero when a workspace is first used).
+size_t gemm_counter_bytes();
 
 // `workspace` holds gemm_workspace_bytes(M, N, K) bytes whose leading
 // per-tile counters are zero; the call leaves them zero again.

@@ -60,7 +60,8 @@ enum awq_status {
   AWQ_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                */
   AWQ_ERR_UNSUPPORTED = -5, /* valid arguments this entry point does not take  */
   AWQ_ERR_WORKSPACE = -6,   /* workspace smaller than awq_gemm_workspace_bytes */
-  AWQ_ERR_HIP = -7          /* the HIP runtime reported an error at launch     */
+  AWQ_ERR_HIP = -7,         /* the HIP runtime reported an error at launch     */
+  AWQ_ERR_SCRATCH = -8      /* awq_gemm_noalloc: shape needs more than its scratch */
 };
 
 /*
@@ -146,6 +147,27 @@ int awq_gemm(const void* x, const uint32_t* qweight, const void* scales, const u
 /* Bytes of workspace awq_gemm needs for this shape (0 when it needs none). */
 size_t awq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t group_size);
 
+/*
+ * awq_gemm_noalloc - awq_gemm for callers that cannot allocate: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, validation, kernels and results (bit for bit) as awq_gemm,
+ * but the split-K workspace is a fixed array owned by the library: a
+ * file-scope device array of awq_gemm_noalloc_max_workspace_bytes() bytes
+ * (64 MiB) that each GPU the library runs on holds until the process ends.
+ * The call allocates and frees nothing.  On the first call on a device the
+ * array's address is looked up and its counter region is cleared by a
+ * kernel on `stream`; every call leaves it zero again.
+ * Shapes whose awq_gemm_workspace_bytes() exceeds the array return
+ * AWQ_ERR_SCRATCH and launch nothing (e.g. 1536 tokens on a 28672 -> 8192
+ * layer); every shape up to 128 tokens on the Llama-7B and 70B-shaped
+ * layers fits.  All calls on one GPU share its array: calls that may
+ * overlap on one GPU (different streams, or different host threads without
+ * ordering) race and give wrong results; order them on one stream.
+ */
+int awq_gemm_noalloc(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* y,
+                     int32_t M, int32_t N, int32_t K, int32_t group_size, int32_t zero_point, void* stream);
+size_t awq_gemm_noalloc_max_workspace_bytes(void);
 
 /*
  * awq_scale_candidates - candidate per-input-channel scales for the
