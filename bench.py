@@ -33,6 +33,7 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--blocks 32]
        python bench.py --leg-only pack|fused|batched|dense|prefill|scale|clip|sweep|gemv70b|power|ceiling
                        (one leg, for profiling)
        python bench.py --copy-calibration | --summarize DB... [--kernel-filter NAME] [--last N]
+       python bench.py --kernel-hash SRC...   (hash of kernel sources + compile flags)
 """
 from __future__ import annotations
 
@@ -71,6 +72,8 @@ def parse():
     ap.add_argument("--summarize", nargs="+", metavar="DB",
                     help="print a per-kernel summary of rocprofv3 result databases and exit")
     ap.add_argument("--kernel-filter", default=None, help="with --summarize: only kernels whose name contains this")
+    ap.add_argument("--kernel-hash", nargs="+", metavar="SRC",
+                    help="print the hash of these kernel sources and the compile flags (for counter summaries)")
     ap.add_argument("--last", type=int, default=None,
                     help="with --summarize: only the last N matching dispatches (e.g. the timed replays)")
     ap.add_argument("--no-layer-timing", action="store_true",
@@ -148,28 +151,58 @@ def per_layer_launch_times(torch, awq, layers, reps, g, zp, replays=20):
     return out
 
 
-def hbm_traffic(step_launches):
-    """Measured HBM bytes per GEMV launch from the committed counter summary,
-    if it was taken on the current kernel source and build flags; else None."""
+def kernel_hash(rel_paths):
+    """sha256 over the given kernel source files (repository-relative) and the
+    library's compile flags: identifies the kernel a counter summary was
+    taken on."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", "gemv_llama7b_decode_traffic.txt")
+    from bit_weight_only_awq_amd import build as B
+
+    h = hashlib.sha256()
+    for rel in rel_paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(B.COMMON_FLAGS).encode())
+    return h.hexdigest()
+
+
+def profile_record(name):
+    """The key: value lines of a committed profile summary, if it was taken on
+    the current kernel sources and build flags; else (None, reason)."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
-        return None, "no counter summary"
+        return None, "no profile summary"
     rec = {}
     with open(path) as f:
         for line in f:
-            if line.startswith("#") or ":" not in line:
+            if line.startswith("#") or ":" not in line or line.startswith("_Z"):
                 continue
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-    h = hashlib.sha256()
-    for rel in rec["sources"].split():
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    if h.hexdigest() != rec["sources_sha256"]:
-        return None, "kernel source or build flags changed since the counters were taken"
+    if kernel_hash(rec["sources"].split()) != rec["sources_sha256"]:
+        return None, "kernel source or build flags changed since the profile was taken"
+    return rec, None
+
+
+def hbm_traffic(step_launches):
+    """Measured HBM bytes per GEMV launch from the committed counter summary,
+    if it was taken on the current kernel source and build flags; else None."""
+    rec, why = profile_record("gemv_llama7b_decode_traffic.txt")
+    if rec is None:
+        return None, why
     return int(rec["hbm_bytes_per_launch"]), rec["note"]
+
+
+def dispatch_stats():
+    """Per-shape rocprofv3 dispatch durations (median, p10, p90) of the timed
+    decode replays from the committed kernel-trace summary, if it was taken
+    on the current kernel; else None."""
+    rec, why = profile_record("gemv_llama7b_decode_kernel_trace.txt")
+    if rec is None:
+        return {"note": why}
+    return dict(json.loads(rec["dispatch_stats"]), source="profiles/gemv_llama7b_decode_kernel_trace.txt "
+                "(rocprofv3 --kernel-trace of the timed replays; the tracer adds per-dispatch overhead)")
 
 
 def leg_pack(torch, awq, layers, g, zp, reps=5):
@@ -770,6 +803,9 @@ def main():
     if args.summarize:
         print(summarize(args.summarize, args.kernel_filter, args.last))
         return 0
+    if args.kernel_hash:
+        print(kernel_hash(args.kernel_hash))
+        return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -886,6 +922,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_note": traffic_note,
                      "kernel": "gemv_kernel", "avg_launch_us": round(avg_us, 3),
+                     "dispatch_stats": dispatch_stats(),
                      "bytes_per_launch": int(bytes_per_launch), "per_layer": layer_stats},
     }
 

@@ -21,7 +21,8 @@ LIB_NAME = "libawq_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 ARCH = "gfx950"
-SOURCES = ("awq_api.hip", "awq_pack.hip", "awq_gemv.hip", "awq_gemm.hip", "awq_scale.hip", "awq_noalloc.hip")
+SOURCES = ("awq_api.hip", "awq_pack.hip", "awq_gemv.hip", "awq_gemv_small.hip", "awq_gemm.hip", "awq_scale.hip",
+           "awq_noalloc.hip")
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -71,8 +71,12 @@ int awq_gemv(const void* x, const uint32_t* qweight, const void* scales, const u
   if (st != AWQ_OK) return st;
   if (!aligned16(x) || !aligned16(y)) return AWQ_ERR_ALIGN;
   if (M > awq::kMaxGemvTokens) return AWQ_ERR_UNSUPPORTED;
-  return from_hip(awq::launch_gemv(x, qweight, scales, zero_point ? qzeros : nullptr, y, M, N, K, group_size,
-                                   zero_point != 0, static_cast<hipStream_t>(stream)));
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (M == 1)
+    return from_hip(awq::launch_gemv(x, qweight, scales, zero_point ? qzeros : nullptr, y, N, K, group_size,
+                                     zero_point != 0, hs));
+  return from_hip(awq::launch_gemv_small(x, qweight, scales, zero_point ? qzeros : nullptr, y, M, N, K, group_size,
+                                         zero_point != 0, hs));
 }
 
 size_t awq_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t group_size) {

@@ -784,7 +784,8 @@ hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales,
   const uint16_t* sc = static_cast<const uint16_t*>(scales);
   _Float16* Y = static_cast<_Float16*>(y);
   const int gs = log2_group(group_size);
-  if (M <= kMaxGemvTokens) return launch_gemv(x, qweight, scales, qzeros, y, M, N, K, group_size, ZP, stream);
+  if (M == 1) return launch_gemv(x, qweight, scales, qzeros, y, N, K, group_size, ZP, stream);
+  if (M <= kMaxGemvTokens) return launch_gemv_small(x, qweight, scales, qzeros, y, M, N, K, group_size, ZP, stream);
   if (M <= 64 && !gemm_uses_mid(M, N, K)) {
     const SkinnyPlan p = plan_skinny(M, N, K);
     switch (p.mt) {

@@ -14,11 +14,14 @@ hipError_t launch_pack(const void* w, int N, int K, int group_size, bool zero_po
 hipError_t launch_dequant(const uint32_t* qweight, const void* scales, const uint32_t* qzeros, void* w_out,
                           int N, int K, int group_size, bool zero_point, hipStream_t stream);
 
-// 1 <= M <= kMaxGemvTokens: one token on the single-token kernel, 2-8 on the
-// few-token kernel.
-constexpr int kMaxGemvTokens = 8;
+// One token (awq_gemv.hip).
 hipError_t launch_gemv(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros,
-                       void* y, int M, int N, int K, int group_size, bool zero_point, hipStream_t stream);
+                       void* y, int N, int K, int group_size, bool zero_point, hipStream_t stream);
+
+// 2 <= M <= kMaxGemvTokens tokens (awq_gemv_small.hip).
+constexpr int kMaxGemvTokens = 8;
+hipError_t launch_gemv_small(const void* x, const uint32_t* qweight, const void* scales, const uint32_t* qzeros,
+                             void* y, int M, int N, int K, int group_size, bool zero_point, hipStream_t stream);
 
 // Workspace bytes launch_gemm needs for an M x N x K product (0: none).
 size_t gemm_workspace_bytes(int M, int N, int K);
