@@ -32,6 +32,7 @@ Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--blocks 32]
                        [--legs all|none|<comma list>] [--no-cpu-baseline] [--no-layer-timing]
        python bench.py --leg-only pack|fused|batched|dense|prefill|scale|clip|sweep|gemv70b|power|ceiling
                        (one leg, for profiling)
+       python bench.py --leg-only loop --shape M,N,K [--launches 200]   (awq_gemm on one shape, for profiling)
        python bench.py --copy-calibration | --summarize DB... [--kernel-filter NAME] [--last N]
        python bench.py --kernel-hash SRC...   (hash of kernel sources + compile flags)
 """
@@ -79,8 +80,10 @@ def parse():
     ap.add_argument("--no-layer-timing", action="store_true",
                     help="skip the per-layer timing graphs after the timed steps (so that a kernel trace ends "
                          "with the timed replays)")
+    ap.add_argument("--shape", default="16,4096,4096", help="with --leg-only loop: M,N,K")
+    ap.add_argument("--launches", type=int, default=200, help="with --leg-only loop: launches")
     ap.add_argument("--leg-only", default=None, choices=["pack", "fused", "batched", "dense", "prefill", "scale", "clip", "sweep", "gemv70b", "power",
-                             "ceiling"],
+                             "ceiling", "loop"],
                     help="run just this leg (no headline, no CPU baseline) and print its JSON; for profiling")
     return ap.parse_args()
 
@@ -555,6 +558,31 @@ def leg_clip_search(torch, awq, workloads, g=128, zp=True, M=512, iters=5):
     return out
 
 
+def leg_loop(torch, awq, workloads, shape, launches=200, g=128, zp=True):
+    """One shape for profiling: awq_gemm (M tokens, K -> N) launched
+    ``launches`` times in a row, eagerly, over enough distinct copies of the
+    packed weight to total >= 1 GiB (every launch reads HBM)."""
+    M, N, K = shape
+    W = torch.from_numpy(workloads.weight(N, K, cfg=3, layer=0)).cuda()
+    base = awq.awq_pack(W, g, zp)
+    del W
+    nbytes = algorithmic_bytes(M, N, K, g, zp)
+    copies = max(2, -(-(1 << 30) // (K * N // 2)))
+    reps = [tuple(t.clone() if t is not None else None for t in base) for _ in range(copies)]
+    x = torch.from_numpy(workloads.activations(M, K, cfg=3, layer=0)).cuda()
+    y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    for i in range(10):
+        awq.awq_gemm(x, *reps[i % copies], N, K, g, zp, y=y)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    tm.start()
+    for i in range(launches):
+        awq.awq_gemm(x, *reps[i % copies], N, K, g, zp, y=y)
+    us = tm.stop_ms() * 1e3 / launches
+    return {"M": M, "N": N, "K": K, "copies": copies, "launches": launches, "us_per_launch_eager": round(us, 3),
+            "GB/s": round(nbytes / us / 1e3, 1)}
+
+
 def _smi_sample():
     """Socket power (amd-smi) and graphics clock (rocm-smi) of GPU 0, as text."""
     import subprocess
@@ -834,7 +862,7 @@ def main():
 
     g, zp = 128, True
     if args.leg_only in ("fused", "batched", "dense", "prefill", "scale", "clip", "sweep", "gemv70b", "power",
-                         "ceiling"):
+                         "ceiling", "loop"):
         fn = {"fused": lambda: leg_fused_decode(torch, awq, workloads, g, zp, blocks=args.blocks),
               "batched": lambda: leg_batched_decode(torch, awq, workloads, g, zp),
               "dense": lambda: leg_dense_decode(torch, workloads),
@@ -844,7 +872,9 @@ def main():
               "sweep": lambda: leg_sweep(torch, awq, workloads),
               "gemv70b": lambda: leg_gemv_70b(torch, awq, workloads, g, zp),
               "power": lambda: leg_power(torch, awq, workloads, g, zp),
-              "ceiling": lambda: leg_ceiling(torch)}[args.leg_only]
+              "ceiling": lambda: leg_ceiling(torch),
+              "loop": lambda: leg_loop(torch, awq, workloads, tuple(int(v) for v in args.shape.split(",")),
+                                       args.launches)}[args.leg_only]
         print(json.dumps({"leg": args.leg_only, "result": fn()}), flush=True)
         return 0
     log(f"building {args.blocks} decode blocks")
