@@ -4,8 +4,11 @@
 // 使用指南", section WQLinear 内核全景: single-token generation, batch 1).  At
 // batch 1 every packed weight byte is used exactly once, so the kernel is a
 // stream over HBM.  Design for gfx950:
-//   * one workgroup per quad (or, on layers large enough to fill the chip
-//     with half as many workgroups, per octet) of output rows; a lane owns
+//   * NW waves per quad (or, on layers large enough to fill the chip with half
+//     as many workgroups, per octet) of output rows, two quads per workgroup
+//     (4% faster on the 4096 x 4096 layers than one: fewer, fuller
+//     workgroups, the quads' activation reads served by one compute unit's
+//     L1); a lane owns
 //     32-channel chunks of all its rows and loads them as 128-bit words, so
 //     every weight load of a wave reads 1 KiB of one row contiguously;
 //   * the rows share the lane's activations; their scales arrive in one 64-bit
@@ -26,17 +29,20 @@
 namespace awq {
 namespace {
 
-template <int NW, bool ZP, int ROWS>
-__global__ __launch_bounds__(NW * 64) void gemv_kernel(const u32x4* __restrict__ x, const u32x4* __restrict__ qweight,
-                                                       const uint16_t* __restrict__ scales,
-                                                       const uint32_t* __restrict__ qzeros,
-                                                       _Float16* __restrict__ y, int N, int K, int gshift) {
+// QPW row groups (quads or octets) per workgroup, NW waves each.
+template <int NW, bool ZP, int ROWS, int QPW>
+__global__ __launch_bounds__(NW * QPW * 64) void gemv_kernel(const u32x4* __restrict__ x,
+                                                             const u32x4* __restrict__ qweight,
+                                                             const uint16_t* __restrict__ scales,
+                                                             const uint32_t* __restrict__ qzeros,
+                                                             _Float16* __restrict__ y, int N, int K, int gshift) {
   static_assert(ROWS == 4 || ROWS == 8, "row quads or octets");
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  __shared__ float red[NW][ROWS];
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int n0 = blockIdx.x * ROWS;
+  __shared__ float red[QPW][NW][ROWS];
+  const int lane = threadIdx.x & 63, wave_all = threadIdx.x >> 6;
+  const int part = wave_all / NW, wave = wave_all - part * NW;  // row group of the wave, wave within it
+  const int t = wave * 64 + lane;                               // thread within the row group
+  const int n0 = (blockIdx.x * QPW + part) * ROWS;
   const int chunks = K >> 5;                // 32-channel chunks per row
   const int G = K >> gshift;
   const size_t row_u4 = (size_t)(K >> 5);   // a row is K/2 bytes = K/32 128-bit words
@@ -110,13 +116,14 @@ __global__ __launch_bounds__(NW * 64) void gemv_kernel(const u32x4* __restrict__
     if (writer) y[n0 + row] = (_Float16)total;
     return;
   }
-  if (writer) red[wave][row] = total;
+  if (writer) red[part][wave][row] = total;
   __syncthreads();
-  if (t < ROWS) {
-    float sum = red[0][t];
+  if (threadIdx.x < QPW * ROWS) {
+    const int p = threadIdx.x / ROWS, r = threadIdx.x - p * ROWS;
+    float sum = red[p][0][r];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) sum += red[w][t];
-    y[n0 + t] = (_Float16)sum;
+    for (int w = 1; w < NW; ++w) sum += red[p][w][r];
+    y[(blockIdx.x * QPW + p) * ROWS + r] = (_Float16)sum;
   }
 }
 
@@ -133,13 +140,19 @@ int gemv_waves(int K) {
 
 bool gemv_uses_octets(int N, int K) { return (long)(N / 8) * gemv_waves(K) >= 16 * 256; }
 
+// Quads go two per workgroup while that fits 1024 threads (N is a multiple
+// of 8, so the quads always pair up); octets and 12-wave quads one.
 template <bool ZP, int ROWS>
 hipError_t launch_rows(const u32x4* xv, const u32x4* wv, const uint16_t* sc, const uint32_t* qzeros, _Float16* yv,
                        int N, int K, int gs, int nw, hipStream_t stream) {
-  const dim3 grid(N / ROWS);
-#define AWQ_GEMV_CASE(W)                                                                                    \
-  case W:                                                                                                   \
-    hipLaunchKernelGGL((gemv_kernel<W, ZP, ROWS>), grid, dim3(W * 64), 0, stream, xv, wv, sc, qzeros, yv, N, K, gs); \
+#define AWQ_GEMV_CASE(W)                                                                                        \
+  case W:                                                                                                       \
+    if (ROWS == 4 && W <= 8)                                                                                    \
+      hipLaunchKernelGGL((gemv_kernel<W, ZP, ROWS, (ROWS == 4 && W <= 8) ? 2 : 1>), dim3(N / (2 * ROWS)),      \
+                         dim3(W * 128), 0, stream, xv, wv, sc, qzeros, yv, N, K, gs);                           \
+    else                                                                                                        \
+      hipLaunchKernelGGL((gemv_kernel<W, ZP, ROWS, 1>), dim3(N / ROWS), dim3(W * 64), 0, stream, xv, wv, sc,    \
+                         qzeros, yv, N, K, gs);                                                                 \
     break;
   switch (nw) {
     AWQ_GEMV_CASE(1)

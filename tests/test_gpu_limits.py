@@ -1,6 +1,6 @@
-"""The largest shapes the library takes (N, K up to 2^21): pack, GEMV and both
-GEMM kernels at K = 2^21 and at N = 2^21, where the 32-bit buffer offsets of
-the kernels come closest to their limit.  Checked against the oracle (packing
+"""The largest shapes the library takes (N, K up to 2^21): pack, the single-
+and few-token GEMV and both GEMM kernels at K = 2^21 and at N = 2^21, where
+the 32-bit buffer offsets of the kernels come closest to their limit.  Checked against the oracle (packing
 bit-exact, products within tolerance on sampled rows)."""
 from __future__ import annotations
 
@@ -35,7 +35,8 @@ def test_max_k_pack_gemv_gemm():
     assert np.array_equal(G.host_u32(qz), oz)
     del w
     wdq = O.dequant_packed(oq, os_, oz, N, K, g, True)
-    for M, fn in ((1, "gemv"), (3, "gemm"), (257, "gemm")):
+    # 2, 3 and 8 tokens: the few-token kernel, 171 rounds of sub-chunks at 8 tokens
+    for M, fn in ((1, "gemv"), (2, "gemv"), (3, "gemm"), (8, "gemv"), (257, "gemm")):
         X = workloads.activations(M, K, cfg=8, layer=M)
         x = G.dev_f16(X)
         f = awq.awq_gemv if fn == "gemv" else awq.awq_gemm
@@ -61,7 +62,7 @@ def test_max_n_pack_gemv_gemm():
     cols = (cols[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
     cols = np.concatenate([cols, np.arange(N - 8, N)])  # the last octet
     wdq = O.dequant_packed(oq[cols], os_[cols[::8] // 8], oz[cols[::8] // 8], len(cols), K, g, True)
-    for M, fn in ((1, "gemv"), (5, "gemm"), (48, "gemm"), (300, "gemm")):
+    for M, fn in ((1, "gemv"), (5, "gemm"), (8, "gemv"), (48, "gemm"), (300, "gemm")):
         X = workloads.activations(M, K, cfg=8, layer=M + 1)
         y = G.host_f16((awq.awq_gemv if fn == "gemv" else awq.awq_gemm)(G.dev_f16(X), qw, sc, qz, N, K, g, True))
         rows = np.arange(M) if M < 8 else np.sort(np.random.default_rng(M).choice(M, 8, replace=False))
