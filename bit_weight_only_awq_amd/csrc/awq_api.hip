@@ -17,6 +17,11 @@ bool valid_group(int32_t g) { return g == 32 || g == 64 || g == 128 || g == 256;
 // the kernels below 2^31 bytes.
 constexpr int32_t kMaxDim = 1 << 21;
 
+// The loss product addresses one candidate's group parameters (K / 32 * N
+// words at most) through a 32-bit buffer range, with offsets up to one group
+// past its end.
+bool loss_shape_ok(int32_t N, int32_t K) { return (int64_t)K * N < ((int64_t)1 << 34); }
+
 // Checks shared by every entry point that reads or writes a packed weight.
 int check_weight_shape(int32_t N, int32_t K, int32_t group_size) {
   if (!valid_group(group_size)) return AWQ_ERR_GROUP;
@@ -132,7 +137,7 @@ int awq_scale_search(const void* x, const void* w, int32_t M, int32_t N, int32_t
                      int32_t* best, double* losses, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_weight_shape(N, K, group_size);
   if (st != AWQ_OK) return st;
-  if (M < 1 || count < 1 || count > awq::kMaxScaleCandidates) return AWQ_ERR_SHAPE;
+  if (M < 1 || count < 1 || count > awq::kMaxScaleCandidates || !loss_shape_ok(N, K)) return AWQ_ERR_SHAPE;
   if (!x || !w || !alphas || !s_best || !best || !workspace) return AWQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(w) || !aligned16(s_best) || !aligned16(workspace) ||
       (reinterpret_cast<uintptr_t>(best) & 3u) != 0 || (reinterpret_cast<uintptr_t>(losses) & 7u) != 0)
@@ -152,7 +157,7 @@ int awq_scale_loss(const void* x, const void* w, const float* s, int32_t count, 
                    void* stream) {
   int st = check_weight_shape(N, K, group_size);
   if (st != AWQ_OK) return st;
-  if (M < 1 || count < 1 || count > 65535) return AWQ_ERR_SHAPE;
+  if (M < 1 || count < 1 || count > 65535 || !loss_shape_ok(N, K)) return AWQ_ERR_SHAPE;
   if (!x || !w || !s || !workspace || !loss) return AWQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(workspace) ||
       (reinterpret_cast<uintptr_t>(loss) & 7u) != 0)

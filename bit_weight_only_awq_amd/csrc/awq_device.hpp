@@ -17,6 +17,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Bit offset of channel c (0..7) inside its packed word.
 __host__ __device__ constexpr int nibble_shift(int c) { return 16 * (c & 1) + 4 * (c >> 1); }

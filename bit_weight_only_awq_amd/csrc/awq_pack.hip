@@ -13,6 +13,7 @@
 //   q = clamp(rne(w / s) + z, 0, 15)
 #include "awq_device.hpp"
 #include "awq_launch.hpp"
+#include "awq_quant.hpp"
 
 #pragma clang fp contract(off)
 
@@ -22,155 +23,6 @@ namespace {
 
 constexpr int kPackThreads = 256;  // 8 rows x 32 lanes
 constexpr int kPackWords = 2;      // packed words (8 channels each) per lane and pass of pack_kernel
-constexpr float kRangeFloor = 1e-5f;
-
-// Combine v over the GW consecutive lanes of a group (GW = 4, 8, 16 or 32,
-// aligned); every lane gets the result.  Partners come by DPP lane swaps
-// inside the 16-lane rows (xor 1 and xor 2 within quads, then mirrored
-// halves of 8 lanes, then the mirrored halves of the row) and, for 32-lane
-// groups, one permute across the two rows.  The min / max is taken on an
-// order-preserving integer image of the (finite) floats: integer min / max
-// needs no NaN canonicalization of the permuted operand, so each step is one
-// DPP-fused instruction.  -0 orders below +0 there, which changes no scale,
-// zero point or code.
-__device__ __forceinline__ int ord_of(float x) {
-  const int i = __builtin_bit_cast(int, x);
-  return i ^ ((i >> 31) & 0x7FFFFFFF);
-}
-__device__ __forceinline__ float float_of(int o) { return __builtin_bit_cast(float, o ^ ((o >> 31) & 0x7FFFFFFF)); }
-
-template <int CTRL>
-__device__ __forceinline__ int dpp_mov(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
-}
-
-template <int GW, class Op>
-__device__ __forceinline__ float group_all(float v, Op op) {
-  int o = ord_of(v);
-  if constexpr (GW >= 2) o = op(o, dpp_mov<0xB1>(o));   // quad_perm [1, 0, 3, 2]
-  if constexpr (GW >= 4) o = op(o, dpp_mov<0x4E>(o));   // quad_perm [2, 3, 0, 1]
-  if constexpr (GW >= 8) o = op(o, dpp_mov<0x141>(o));  // row_half_mirror
-  if constexpr (GW >= 16) o = op(o, dpp_mov<0x140>(o)); // row_mirror
-  if constexpr (GW >= 32) o = op(o, __shfl_xor(o, 16));
-  return float_of(o);
-}
-
-struct MinOp {
-  __device__ int operator()(int a, int b) const { return a < b ? a : b; }
-};
-struct MaxOp {
-  __device__ int operator()(int a, int b) const { return a > b ? a : b; }
-};
-
-// Scale and zero point of the group a lane's NV weights (one or two packed
-// words) belong to.  A group of g channels is GW = g / NV consecutive lanes of
-// one row, reduced with butterfly shuffles (GW divides 32, so a group never
-// leaves its half-wave, and all lanes of a group are active or inactive
-// together).  s16 is the fp16 scale,
-// s its fp32 value, zf the zero point as a float.
-// amax is the group's largest magnitude (a bound for every |a[c]|).
-template <int GW, bool ZP, int NV>
-__device__ __forceinline__ void group_scale_zero(const float (&a)[NV], _Float16& s16, float& s, float& zf,
-                                                 float& amax) {
-  if constexpr (ZP) {
-    float mn = a[0], mx = a[0];
-#pragma unroll
-    for (int c = 1; c < NV; ++c) {
-      mn = fminf(mn, a[c]);
-      mx = fmaxf(mx, a[c]);
-    }
-    mn = group_all<GW>(mn, MinOp());
-    mx = group_all<GW>(mx, MaxOp());
-    amax = fmaxf(fabsf(mn), fabsf(mx));
-    float rng = mx - mn;
-    if (rng < kRangeFloor) rng = kRangeFloor;
-    s16 = (_Float16)(rng / 15.0f);
-    s = (float)s16;
-    zf = rintf(-mn / s);
-    zf = fminf(fmaxf(zf, 0.0f), 15.0f);
-  } else {
-    float m = fabsf(a[0]);
-#pragma unroll
-    for (int c = 1; c < NV; ++c) m = fmaxf(m, fabsf(a[c]));
-    amax = group_all<GW>(m, MaxOp());
-    const float am = amax < kRangeFloor ? kRangeFloor : amax;
-    s16 = (_Float16)(am / 7.0f);
-    s = (float)s16;
-    zf = 8.0f;
-  }
-}
-
-// Codes of a lane's 8 weights of one group, clamp(rne(a / s) + z, 0, 15) as
-// floats, with a / s the correctly rounded fp32 quotient.  The quotient is
-// first taken as x = a * rcp(s): the reciprocal is within 1 ulp and the
-// product adds half an ulp, so x lies within |x| * 2^-21 of the correctly
-// rounded quotient f, and rint(x) and rne(f) can differ only if a
-// half-integer lies within that distance of x.  With m = amax * rcp(s) *
-// 2^-20, at least twice that distance for every weight of the group, a lane
-// keeps rint(x) when all its 8 products lie more than m from a half-integer
-// (|x - rint(x)| < 0.5 - m; about 2^-15 of the weights of a Gaussian group
-// fail it), and divides all 8 weights exactly otherwise (every weight of a
-// group on an exact half-step grid, every group whose quotients pass 2^19).
-// Bit-identical to dividing every weight.
-__device__ __forceinline__ void codes_of(const float (&a)[8], float s, float zf, float amax, float (&q)[8]) {
-  const float rs = __builtin_amdgcn_rcpf(s);
-  const float lim = 0.5f - amax * rs * 0x1p-20f;
-  float k[8];
-  float dmax = 0.0f;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const float x = a[c] * rs;
-    k[c] = rintf(x);
-    dmax = fmaxf(dmax, fabsf(x - k[c]));
-  }
-  if (!(dmax < lim)) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) k[c] = rintf(a[c] / s);
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) q[c] = fminf(fmaxf(k[c] + zf, 0.0f), 15.0f);
-}
-
-// The packed word of 8 codes (small integers held as floats): two codes per
-// byte, byte b holding the codes of channels 2b' and 2b' + 2 in the order of
-// nibble_shift, each byte inserted by one float-to-u8 conversion.
-__device__ __forceinline__ uint32_t pack_word(const float (&q)[8]) {
-  uint32_t w = 0;
-  // nibble_shift: c = 0, 2 -> byte 0; 4, 6 -> byte 1; 1, 3 -> byte 2; 5, 7 -> byte 3
-  // (exact: small integers)
-  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[2], 16.0f, q[0]), 0, w);
-  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[6], 16.0f, q[4]), 1, w);
-  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[3], 16.0f, q[1]), 2, w);
-  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[7], 16.0f, q[5]), 3, w);
-  return w;
-}
-
-// Range of the group a lane's 8 weights belong to, shrunk by `r` (weight
-// clipping): [r * min, r * max] with a zero point, [-r * amax, r * amax]
-// without (fp32 products).
-template <int GW, bool ZP, int NV>
-__device__ __forceinline__ void group_clip_bounds(const float (&a)[NV], float r, float& lo, float& hi) {
-  if constexpr (ZP) {
-    float mn = a[0], mx = a[0];
-#pragma unroll
-    for (int c = 1; c < NV; ++c) {
-      mn = fminf(mn, a[c]);
-      mx = fmaxf(mx, a[c]);
-    }
-    mn = group_all<GW>(mn, MinOp());
-    mx = group_all<GW>(mx, MaxOp());
-    lo = r * mn;
-    hi = r * mx;
-  } else {
-    float amax = fabsf(a[0]);
-#pragma unroll
-    for (int c = 1; c < NV; ++c) amax = fmaxf(amax, fabsf(a[c]));
-    amax = group_all<GW>(amax, MaxOp());
-    hi = r * amax;
-    lo = -hi;
-  }
-}
-
 // One block quantizes one octet of rows (n0 .. n0+7) over one slice of K
 // (blockIdx.y: packed words [chunk_words * y, + chunk_words), a multiple of a
 // 512-channel pass, so slices end on group boundaries; several slices per row
@@ -239,15 +91,15 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restr
         for (int c = 0; c < 8; ++c) aw[i][c] = a[8 * i + c] = (float)h[c];
       }
 
-      float s, zf, amax;
+      float s, zf;
       _Float16 s16;
-      group_scale_zero<GW, ZP>(a, s16, s, zf, amax);
+      group_scale_zero<GW, ZP>(a, s16, s, zf);
 
       wordsT out;
 #pragma unroll
       for (int i = 0; i < WPL; ++i) {
         float q[8];
-        codes_of(aw[i], s, zf, amax, q);
+        codes_of(aw[i], s, zf, q);
         out[i] = pack_word(q);
       }
       if (active) *reinterpret_cast<wordsT*>(qweight + (size_t)n * kw + j) = out;
@@ -264,81 +116,87 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restr
   }
 }
 
-// Weight error of the activation-aware scaling, for the objective
+// Group parameters of the candidate-scaled weights, for the objective
 //   L(s) = || Q(W diag(s)) (diag(s)^-1 X) - W X ||
-// ("AI-Research-SKILLs AWQ 高级使用指南", section 算法原理).  For candidate c
-// (blockIdx.y) with per-input-channel scales s_c:
-//   e[n][k] = fp16( w'[n][k] / s_c[k] - w[n][k] ),  w' = Dq(Q(fp16(w[n][k] * s_c[k])))
-// so that L(s_c) = || X e^T ||_F: one dense product instead of two.  The
-// quantizer is the one of pack_kernel (same code, same fp32 order); w * s is
-// an fp32 product rounded to fp16, w' = (q - z) * s is exact, and the
-// product by the reciprocal of s_c[k] (1 ulp) and the subtraction are fp32
-// roundings far below the final fp16 one.  Same block shape as pack_kernel:
-// one octet of rows per block.
+// ("AI-Research-SKILLs AWQ 高级使用指南", section 算法原理), which the loss
+// product evaluates as || X e^T || with e = Dq(Q(fp16(w * s))) / s - w built
+// tile by tile beside the matrix cores.  Whatever needs a whole group comes
+// from here: for every candidate c (an inner loop, so the weights are read
+// once for all candidates), row n and group j of the scaled weights
+// a = fp16(w[n][k] * s_c[k]) (fp32 product, rounded once),
+//   gp[c][j][n] = fp16 scale bits | zero point << 16,
+// the scale and zero point of pack_kernel's quantizer, so that the loss
+// product's codes are pack_kernel's codes bit for bit.  The blocks of the first row octet also write
+// rs[c][k] = rcp(s_c[k]).  Same block shape and K slices as pack_kernel.
 template <int GW, bool ZP>
-__global__ __launch_bounds__(kPackThreads) void scale_error_kernel(const u32x4* __restrict__ w,
-                                                                   const float* __restrict__ s_all, int N, int K,
-                                                                   u32x4* __restrict__ e_all) {
-  constexpr int WPL = kPackWords;  // lane l of a row owns words 2l, 2l + 1 of each 64-word pass
+__global__ __launch_bounds__(kPackThreads) void scale_group_params_kernel(const u32x4* __restrict__ w,
+                                                                          const float* __restrict__ s_all, int count,
+                                                                          int N, int K, int chunk_words,
+                                                                          uint32_t* __restrict__ gp,
+                                                                          float* __restrict__ rs_all) {
+  constexpr int WPL = kPackWords;
+  constexpr int kPass = 32 * WPL;
   const int t = threadIdx.x;
   const int r = t >> 5, l = t & 31;
   const int n = blockIdx.x * 8 + r;
   const int kw = K >> 3;
-  const float* sc = s_all + (size_t)blockIdx.y * K;
-  u32x4* e = e_all + (size_t)blockIdx.y * N * kw;
-
-  // the next pass's weights and scales are loaded while this pass is processed
+  const int G = kw / (WPL * GW);
+  const int j_begin = blockIdx.y * chunk_words;
+  const int j_end = min(kw, j_begin + chunk_words);  // multiples of WPL: no lane's words straddle j_end
   const u32x4* wrow = w + (size_t)n * kw;
-  u32x4 nraw[WPL];
-  float4_t ns[2 * WPL];
-  auto fetch = [&](int j) {
-#pragma unroll
-    for (int i = 0; i < WPL; ++i) nraw[i] = j < kw ? wrow[j + i] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 2 * WPL; ++i)
-      ns[i] = j < kw ? *reinterpret_cast<const float4_t*>(sc + 8 * j + 4 * i) : float4_t{1.f, 1.f, 1.f, 1.f};
-  };
-  fetch(WPL * l);
-  for (int w0 = 0; w0 < kw; w0 += 32 * WPL) {
-    const int j = w0 + WPL * l;  // kw is a multiple of 4: a lane's words are all in or all out
-    const bool active = j < kw;
-    u32x4 raw[WPL];
-    float sv[8 * WPL];
-#pragma unroll
-    for (int i = 0; i < WPL; ++i) raw[i] = nraw[i];
-#pragma unroll
-    for (int i = 0; i < 2 * WPL; ++i)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) sv[4 * i + c] = ns[i][c];
-    fetch(j + 32 * WPL);
-    float hv[8 * WPL], a[8 * WPL];
+  for (int w0 = j_begin; w0 < j_end; w0 += kPass) {
+    const int j = w0 + WPL * l;
+    const bool active = j < j_end;
+    float hv[8 * WPL];
 #pragma unroll
     for (int i = 0; i < WPL; ++i) {
-      const half8_t h = as_half8(raw[i]);
+      const half8_t h = as_half8(active ? wrow[j + i] : u32x4{0u, 0u, 0u, 0u});
 #pragma unroll
       for (int c = 0; c < 8; ++c) hv[8 * i + c] = (float)h[c];
     }
+    const int grp = j / (WPL * GW);
+    const bool leader = active && (l % GW) == 0;
+    for (int c = 0; c < count; ++c) {
+      const float* sc = s_all + (size_t)c * K + 8 * j;
+      float sv[8 * WPL];
 #pragma unroll
-    for (int c = 0; c < 8 * WPL; ++c) a[c] = (float)(_Float16)(hv[c] * sv[c]);
-
-    float s, zf, amax;
-    _Float16 s16;
-    group_scale_zero<GW, ZP>(a, s16, s, zf, amax);
-
-    // e only needs fp16 accuracy: w' / s by a reciprocal (1 ulp in fp32)
+      for (int i = 0; i < 2 * WPL; ++i) {
+        const float4_t v = active ? *reinterpret_cast<const float4_t*>(sc + 4 * i) : float4_t{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-    for (int i = 0; i < WPL; ++i) {
-      float ai[8], q[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) ai[c] = a[8 * i + c];
-      codes_of(ai, s, zf, amax, q);
-      half8_t out;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float wq = (q[c] - zf) * s;
-        out[c] = (_Float16)(wq * __builtin_amdgcn_rcpf(sv[8 * i + c]) - hv[8 * i + c]);
+        for (int q = 0; q < 4; ++q) sv[4 * i + q] = v[q];
       }
-      if (active) e[(size_t)n * kw + j + i] = __builtin_bit_cast(u32x4, out);
+      // the group's extremes of fp16(w * s_c) are the fp16 roundings of the
+      // extremes of the fp32 products (rounding is monotone): two
+      // conversions per lane instead of one per weight
+      float mn, mx;
+      if constexpr (ZP) {
+        mn = mx = fp32_product(hv[0], sv[0]);
+#pragma unroll
+        for (int q = 1; q < 8 * WPL; ++q) {
+          const float v = fp32_product(hv[q], sv[q]);
+          mn = fminf(mn, v);
+          mx = fmaxf(mx, v);
+        }
+        mn = (float)(_Float16)mn;
+      } else {
+        mn = 0.0f;
+        mx = fabsf(fp32_product(hv[0], sv[0]));
+#pragma unroll
+        for (int q = 1; q < 8 * WPL; ++q) mx = fmaxf(mx, fabsf(fp32_product(hv[q], sv[q])));
+      }
+      mx = (float)(_Float16)mx;
+      float s, zf;
+      _Float16 s16;
+      group_scale_zero_of<GW, ZP>(mn, mx, s16, s, zf);
+      if (leader) gp[((size_t)c * G + grp) * N + n] = (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)zf << 16);
+      if (blockIdx.x == 0 && r == 0 && active) {
+        float* rs = rs_all + (size_t)c * K + 8 * j;
+#pragma unroll
+        for (int i = 0; i < 2 * WPL; ++i)
+          *reinterpret_cast<float4_t*>(rs + 4 * i) =
+              float4_t{__builtin_amdgcn_rcpf(sv[4 * i]), __builtin_amdgcn_rcpf(sv[4 * i + 1]),
+                       __builtin_amdgcn_rcpf(sv[4 * i + 2]), __builtin_amdgcn_rcpf(sv[4 * i + 3])};
+      }
     }
   }
 }
@@ -380,15 +238,15 @@ __global__ __launch_bounds__(kPackThreads) void clip_error_kernel(const u32x4* _
     float cl[8 * WPL];
 #pragma unroll
     for (int c = 0; c < 8 * WPL; ++c) cl[c] = (float)(_Float16)fminf(fmaxf(a[c], lo), hi);
-    float s, zf, amax;
+    float s, zf;
     _Float16 s16;
-    group_scale_zero<GW, ZP>(cl, s16, s, zf, amax);
+    group_scale_zero<GW, ZP>(cl, s16, s, zf);
 #pragma unroll
     for (int i = 0; i < WPL; ++i) {
       float ci[8], q[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) ci[c] = cl[8 * i + c];
-      codes_of(ci, s, zf, amax, q);
+      codes_of(ci, s, zf, q);
       half8_t out;
 #pragma unroll
       for (int c = 0; c < 8; ++c) out[c] = (_Float16)((q[c] - zf) * s - a[8 * i + c]);
@@ -514,17 +372,26 @@ hipError_t launch_pack_zp(const void* w, int N, int K, int group_size, uint32_t*
 
 int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 128 ? 7 : 8; }
 
+// K slices as in launch_pack_zp, to about 4096 blocks (every block loops over
+// all candidates).
 template <bool ZP>
-hipError_t launch_scale_error_zp(const void* w, const float* s, int count, int N, int K, int group_size, void* e,
-                                 hipStream_t stream) {
-  const dim3 grid(N / 8, count), block(kPackThreads);
+hipError_t launch_scale_group_params_zp(const void* w, const float* s, int count, int N, int K, int group_size,
+                                        void* gp, float* rs, hipStream_t stream) {
+  constexpr int kTargetBlocks = 4096, kRingWords = 32 * kPackWords;
+  const int kw = K >> 3, octets = N / 8;
+  const int rings = (kw + kRingWords - 1) / kRingWords;
+  int slices = (kTargetBlocks + octets - 1) / octets;
+  if (slices > rings) slices = rings;
+  if (slices < 1) slices = 1;
+  const int chunk = ((rings + slices - 1) / slices) * kRingWords;
+  const dim3 grid(octets, (kw + chunk - 1) / chunk), block(kPackThreads);
   const u32x4* wv = static_cast<const u32x4*>(w);
-  u32x4* ev = static_cast<u32x4*>(e);
+  uint32_t* g = static_cast<uint32_t*>(gp);
   switch (group_size) {
-    case 32: hipLaunchKernelGGL((scale_error_kernel<4 / kPackWords, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
-    case 64: hipLaunchKernelGGL((scale_error_kernel<8 / kPackWords, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
-    case 128: hipLaunchKernelGGL((scale_error_kernel<16 / kPackWords, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
-    case 256: hipLaunchKernelGGL((scale_error_kernel<32 / kPackWords, ZP>), grid, block, 0, stream, wv, s, N, K, ev); break;
+    case 32: hipLaunchKernelGGL((scale_group_params_kernel<4 / kPackWords, ZP>), grid, block, 0, stream, wv, s, count, N, K, chunk, g, rs); break;
+    case 64: hipLaunchKernelGGL((scale_group_params_kernel<8 / kPackWords, ZP>), grid, block, 0, stream, wv, s, count, N, K, chunk, g, rs); break;
+    case 128: hipLaunchKernelGGL((scale_group_params_kernel<16 / kPackWords, ZP>), grid, block, 0, stream, wv, s, count, N, K, chunk, g, rs); break;
+    case 256: hipLaunchKernelGGL((scale_group_params_kernel<32 / kPackWords, ZP>), grid, block, 0, stream, wv, s, count, N, K, chunk, g, rs); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -576,12 +443,11 @@ hipError_t launch_clip_apply(const void* w, const float* part, int parts, const 
                     : launch_clip_zp<false>(w, ratios, count, N, K, group_size, nullptr, choice, w_out, true, stream);
 }
 
-hipError_t launch_scale_error(const void* w, const float* s, int count, int N, int K, int group_size, bool zero_point,
-                              void* e, hipStream_t stream) {
-  return zero_point ? launch_scale_error_zp<true>(w, s, count, N, K, group_size, e, stream)
-                    : launch_scale_error_zp<false>(w, s, count, N, K, group_size, e, stream);
+hipError_t launch_scale_group_params(const void* w, const float* s, int count, int N, int K, int group_size,
+                                     bool zero_point, void* gp, float* rs, hipStream_t stream) {
+  return zero_point ? launch_scale_group_params_zp<true>(w, s, count, N, K, group_size, gp, rs, stream)
+                    : launch_scale_group_params_zp<false>(w, s, count, N, K, group_size, gp, rs, stream);
 }
-
 hipError_t launch_pack(const void* w, int N, int K, int group_size, bool zero_point, uint32_t* qweight,
                        void* scales, uint32_t* qzeros, hipStream_t stream) {
   return zero_point ? launch_pack_zp<true>(w, N, K, group_size, qweight, scales, qzeros, stream)

@@ -1,0 +1,196 @@
+// The group quantizer shared by the packing kernel and the search kernels:
+// group statistics across the lanes of a wave, the fp16 scale and zero point
+// of a group, and the 4-bit codes of its weights.
+//
+// "AI-Research-SKILLs AWQ 高级使用指南", section 分组大小与零点量化: every group
+// of g consecutive input channels of one output row shares one scale and one
+// zero point.  The arithmetic is IEEE fp32 in one fixed order (each function
+// turns off contraction into fused multiply-adds for its own body), with round-half-to-even and correctly rounded
+// division, so every caller gets the same bits:
+//   zero_point:  r = max(max - min, 1e-5); s = fp16(r / 15); z = clamp(rne(-min / s), 0, 15)
+//   symmetric:   a = max(max|w|, 1e-5);    s = fp16(a / 7);  z = 8
+//   q = clamp(rne(w / s) + z, 0, 15)
+#pragma once
+
+#include "awq_device.hpp"
+
+namespace awq {
+namespace {
+
+constexpr float kRangeFloor = 1e-5f;
+
+// Combine v over the GW consecutive lanes of a group (GW = 4, 8, 16 or 32,
+// aligned); every lane gets the result.  Partners come by DPP lane swaps
+// inside the 16-lane rows (xor 1 and xor 2 within quads, then mirrored
+// halves of 8 lanes, then the mirrored halves of the row) and, for 32-lane
+// groups, one permute across the two rows.  The min / max is taken on an
+// order-preserving integer image of the (finite) floats: integer min / max
+// needs no NaN canonicalization of the permuted operand, so each step is one
+// DPP-fused instruction.  -0 orders below +0 there, which changes no scale,
+// zero point or code.
+__device__ __forceinline__ int ord_of(float x) {
+  const int i = __builtin_bit_cast(int, x);
+  return i ^ ((i >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float float_of(int o) { return __builtin_bit_cast(float, o ^ ((o >> 31) & 0x7FFFFFFF)); }
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+
+template <int GW, class Op>
+__device__ __forceinline__ float group_all(float v, Op op) {
+  int o = ord_of(v);
+  if constexpr (GW >= 2) o = op(o, dpp_mov<0xB1>(o));   // quad_perm [1, 0, 3, 2]
+  if constexpr (GW >= 4) o = op(o, dpp_mov<0x4E>(o));   // quad_perm [2, 3, 0, 1]
+  if constexpr (GW >= 8) o = op(o, dpp_mov<0x141>(o));  // row_half_mirror
+  if constexpr (GW >= 16) o = op(o, dpp_mov<0x140>(o)); // row_mirror
+  if constexpr (GW >= 32) o = op(o, __shfl_xor(o, 16));
+  return float_of(o);
+}
+
+struct MinOp {
+  __device__ int operator()(int a, int b) const { return a < b ? a : b; }
+};
+struct MaxOp {
+  __device__ int operator()(int a, int b) const { return a > b ? a : b; }
+};
+
+// Scale and zero point of a group from its lanes' own extremes: with a zero
+// point, mn and mx are the smallest and largest of the lane's weights;
+// without, mx is the lane's largest magnitude (mn unused).  A group of g
+// channels is GW consecutive lanes of one row, reduced with butterfly
+// shuffles (GW divides 32, so a group never leaves its half-wave, and all
+// lanes of a group are active or inactive together).  s16 is the fp16 scale,
+// s its fp32 value, zf the zero point as a float.
+template <int GW, bool ZP>
+__device__ __forceinline__ void group_scale_zero_of(float mn, float mx, _Float16& s16, float& s, float& zf) {
+#pragma clang fp contract(off)
+  if constexpr (ZP) {
+    mn = group_all<GW>(mn, MinOp());
+    mx = group_all<GW>(mx, MaxOp());
+    float rng = mx - mn;
+    if (rng < kRangeFloor) rng = kRangeFloor;
+    s16 = (_Float16)(rng / 15.0f);
+    s = (float)s16;
+    zf = rintf(-mn / s);
+    zf = fminf(fmaxf(zf, 0.0f), 15.0f);
+  } else {
+    const float amax = group_all<GW>(mx, MaxOp());
+    const float am = amax < kRangeFloor ? kRangeFloor : amax;
+    s16 = (_Float16)(am / 7.0f);
+    s = (float)s16;
+    zf = 8.0f;
+  }
+}
+
+// The same from the lane's NV weights (one or two packed words).
+template <int GW, bool ZP, int NV>
+__device__ __forceinline__ void group_scale_zero(const float (&a)[NV], _Float16& s16, float& s, float& zf) {
+  if constexpr (ZP) {
+    float mn = a[0], mx = a[0];
+#pragma unroll
+    for (int c = 1; c < NV; ++c) {
+      mn = fminf(mn, a[c]);
+      mx = fmaxf(mx, a[c]);
+    }
+    group_scale_zero_of<GW, ZP>(mn, mx, s16, s, zf);
+  } else {
+    float m = fabsf(a[0]);
+#pragma unroll
+    for (int c = 1; c < NV; ++c) m = fmaxf(m, fabsf(a[c]));
+    group_scale_zero_of<GW, ZP>(0.0f, m, s16, s, zf);
+  }
+}
+
+// fp16(fp32(a * b)): the fp32 product, rounded to fp16 (a weight scaled by a
+// per-channel factor, as the quantizer sees it).  The empty asm keeps the
+// product an fp32 value: left alone, the compiler fuses the multiply and the
+// conversion into one mixed-precision instruction (v_fma_mixlo_f16) that
+// rounds the exact product to fp16 once, which differs from rounding the fp32
+// product wherever that lands on an fp16 midpoint (measured on gfx950).
+__device__ __forceinline__ float fp32_product(float a, float b) {
+  float p = a * b;
+  asm("" : "+v"(p));
+  return p;
+}
+
+// rne(a / s) for a lane's 8 weights of one group, as floats, where a and s
+// are fp16 values (a weight and its group's scale), computed without a
+// division and without a branch.  x = a * rcp(s) lies within 2 ulp of the
+// quotient; one correction step r = fma(-x, s, a), x' = fma(r, rcp(s), x)
+// makes it exact when the quotient is a half-integer j + 1/2 (then q - x is a
+// multiple of x's ulp of at most a few units, (q - x) * s has at most 13
+// significant bits, so r = a - x s is exact and x' rounds to q) and leaves it
+// within an ulp otherwise.  A quotient of two fp16 values that is not a
+// half-integer lies at least ~2^-13 from one (numerator and denominator have
+// 11-bit significands), far more than x' can be off while |x| < 16, so
+// rint(x') = rne(a / s) there; beyond, every code saturates (q = clamp(k + z,
+// 0, 15) with 0 <= z <= 15) and an off-by-one in k changes nothing.
+// (Half-integer quotients are common: fp16 weights are coarse against a
+// 16-level grid, about 1 in 250 weights.)
+__device__ __forceinline__ void rounded_quotients(const float (&a)[8], float s, float (&k)[8]) {
+#pragma clang fp contract(off)
+  const float rs = __builtin_amdgcn_rcpf(s);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float x = a[c] * rs;
+    const float r = __builtin_fmaf(-x, s, a[c]);
+    k[c] = rintf(__builtin_fmaf(r, rs, x));
+  }
+}
+
+// Codes of a lane's 8 weights of one group, clamp(rne(a / s) + z, 0, 15) as
+// floats.
+__device__ __forceinline__ void codes_of(const float (&a)[8], float s, float zf, float (&q)[8]) {
+#pragma clang fp contract(off)
+  float k[8];
+  rounded_quotients(a, s, k);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) q[c] = fminf(fmaxf(k[c] + zf, 0.0f), 15.0f);
+}
+
+// The packed word of 8 codes (small integers held as floats): two codes per
+// byte, byte b holding the codes of channels 2b' and 2b' + 2 in the order of
+// nibble_shift, each byte inserted by one float-to-u8 conversion.
+__device__ __forceinline__ uint32_t pack_word(const float (&q)[8]) {
+  uint32_t w = 0;
+  // nibble_shift: c = 0, 2 -> byte 0; 4, 6 -> byte 1; 1, 3 -> byte 2; 5, 7 -> byte 3
+  // (exact: small integers)
+  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[2], 16.0f, q[0]), 0, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[6], 16.0f, q[4]), 1, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[3], 16.0f, q[1]), 2, w);
+  w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(q[7], 16.0f, q[5]), 3, w);
+  return w;
+}
+
+// Range of the group a lane's 8 weights belong to, shrunk by `r` (weight
+// clipping): [r * min, r * max] with a zero point, [-r * amax, r * amax]
+// without (fp32 products).
+template <int GW, bool ZP, int NV>
+__device__ __forceinline__ void group_clip_bounds(const float (&a)[NV], float r, float& lo, float& hi) {
+#pragma clang fp contract(off)
+  if constexpr (ZP) {
+    float mn = a[0], mx = a[0];
+#pragma unroll
+    for (int c = 1; c < NV; ++c) {
+      mn = fminf(mn, a[c]);
+      mx = fmaxf(mx, a[c]);
+    }
+    mn = group_all<GW>(mn, MinOp());
+    mx = group_all<GW>(mx, MaxOp());
+    lo = r * mn;
+    hi = r * mx;
+  } else {
+    float amax = fabsf(a[0]);
+#pragma unroll
+    for (int c = 1; c < NV; ++c) amax = fmaxf(amax, fabsf(a[c]));
+    amax = group_all<GW>(amax, MaxOp());
+    hi = r * amax;
+    lo = -hi;
+  }
+}
+
+}  // namespace
+}  // namespace awq

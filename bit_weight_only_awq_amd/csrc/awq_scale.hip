@@ -17,13 +17,17 @@
 // weight statistic of the channel:
 //   s_k = a_k ^ alpha / b_k ^ (1 - alpha),  b_k = max(mean_n |w_nk|, 1e-4).
 //
-// L(s) is evaluated as || X e^T ||_F with e = Q(W s) s^-1 - W (built by
-// scale_error_kernel next to the quantizer): the same quantity, one dense
-// product instead of two.  The product runs on the fp16 matrix cores with fp32
-// accumulation; the squares are summed per tile and the tiles are added in a
-// fixed order in fp64 (deterministic).
+// L(s) is evaluated as || X e^T ||_F with e = Q(W s) s^-1 - W (the same
+// quantity, one dense product instead of two), written as
+//   X e^T = (X diag(s)^-1) (Q(W s) - W diag(s))^T:
+// the activations are scaled once per candidate and the weight error
+// Q(W s) - W s is built tile by tile next to the matrix cores
+// (loss_fused_kernel) and never stored.  The product runs on the fp16 matrix
+// cores with fp32 accumulation; the squares are summed per wave and the
+// partial sums are added in a fixed order in fp64 (deterministic).
 #include "awq_device.hpp"
 #include "awq_launch.hpp"
+#include "awq_quant.hpp"
 
 namespace awq {
 namespace {
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(256) void scale_columns_kernel(const u32x4* __restr
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float sc = c < 4 ? s0[c] : s1[c - 4];
-      out[c] = (_Float16)(divide ? (float)h[c] / sc : (float)h[c] * sc);
+      out[c] = (_Float16)(divide ? (float)h[c] / sc : fp32_product((float)h[c], sc));
     }
     dst[i] = __builtin_bit_cast(u32x4, out);
   }
@@ -308,6 +312,252 @@ __global__ __launch_bounds__(WM * WN * 64) void sumsq_gemm_kernel(const _Float16
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// The loss product with the weight error built in place.
+// ---------------------------------------------------------------------------
+// xs[c][m][k] = fp16(x[m][k] * rcp(s_c[k])): the activations of candidate c
+// (the reciprocal within 1 ulp; the operand only needs fp16 accuracy).  One
+// thread per 8 channels.
+__global__ __launch_bounds__(256) void scaled_activations_kernel(const u32x4* __restrict__ x,
+                                                                 const float* __restrict__ s_all, int M, int K,
+                                                                 u32x4* __restrict__ xs) {
+  const int kw = K >> 3;
+  const size_t words = (size_t)M * kw;
+  const int c = blockIdx.y;
+  const float* sc = s_all + (size_t)c * K;
+  u32x4* out = xs + (size_t)c * words;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (size_t)gridDim.x * 256) {
+    const int j = (int)(i % kw);
+    const half8_t h = as_half8(x[i]);
+    const float4_t s0 = *reinterpret_cast<const float4_t*>(sc + 8 * j);
+    const float4_t s1 = *reinterpret_cast<const float4_t*>(sc + 8 * j + 4);
+    half8_t r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      r[q] = (_Float16)((float)h[q] * __builtin_amdgcn_rcpf(s0[q]));
+      r[4 + q] = (_Float16)((float)h[4 + q] * __builtin_amdgcn_rcpf(s1[q]));
+    }
+    out[i] = __builtin_bit_cast(u32x4, r);
+  }
+}
+
+// Scaled errors of one row's 8 channels of one group for one candidate:
+//   e = fp16( (q - z) * s_g - w * s_c ),  q = clamp(rne(a / s_g) + z, 0, 15),  a = fp16(w * s_c)
+// (the difference formed by one fused multiply-add from the exact (q - z) s_g),
+// with the group's fp16 scale s_g and zero point z from p = s_g bits |
+// z << 16, and q by pack_kernel's rule (a is the
+// fp32 product rounded to fp16, as the quantizer sees it).  med3(k, -z,
+// 15 - z) is q - z exactly (small integers).
+__device__ __forceinline__ half8_t scaled_error8(u32x4 raw, uint32_t p, float4_t s0, float4_t s1) {
+  const half8_t h = as_half8(raw);
+  const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFFu));
+  const float zf = (float)(p >> 16);
+  float a[8], k[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) a[c] = (float)(_Float16)fp32_product((float)h[c], sv[c]);
+  rounded_quotients(a, s, k);
+  half8_t e;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    e[c] = (_Float16)__builtin_fmaf(-(float)h[c], sv[c], __builtin_amdgcn_fmed3f(k[c], -zf, 15.0f - zf) * s);
+  return e;
+}
+
+// Sum of the squares of xs_c e_c^T for candidate c, e_c as in scaled_error8
+// with the group quantities of scale_group_params_kernel (= L(s_c)^2).  e
+// never goes to memory: every K step the workgroup builds the 128 x 64 tile
+// of e for the next step from weights already in registers and writes it to
+// LDS, where the matrix cores read it as the B operand while the scaled
+// activations stream in by buffer-to-LDS loads, as in sumsq_gemm_kernel.
+// Tile 512 tokens x 128 weight rows, so an element of e (about eight fp32
+// operations) is built once per 512 tokens, against 512 multiply-adds on the
+// matrix cores; 8 waves of 128 x 64 (4 x 2 v_mfma_f32_32x32x16_f16 tiles);
+// 160 KiB of LDS.  For the build, lane l of wave w takes channels
+// 8 (l % 8) .. + 7 of the step (LDS chunk l % 8) in rows 16 w + l / 8 and
+// 16 w + 8 + l / 8, so each wave load covers whole 128-byte lines of 8 rows.
+// Every load is an unconditional buffer load (out-of-range offsets return
+// zero): no branch separates a load from its use, and the waits count
+// exactly.  Tiles are ordered candidate-major: the workgroups on one XCD
+// share one candidate's scaled activations in its L2.  Output: per wave, the
+// fp64 value of its fp32 sum of squares, partial[(c * tiles + tile) * 8 + wave].
+constexpr int kLossM = 512, kLossN = 128, kLossWaves = 8;
+
+template <bool KTAIL>
+__global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Float16* __restrict__ XS,
+                                                                   const _Float16* __restrict__ W,
+                                                                   const float* __restrict__ s_all,
+                                                                   const uint32_t* __restrict__ gp, int M, int N, int K,
+                                                                   int gshift, int tiles_m, int tiles,
+                                                                   double* __restrict__ partial) {
+  constexpr int AM = 4, AN = 2, WM = 4;
+  constexpr int XOP = kLossM * TK * 2, EOP = kLossN * TK * 2;
+  __shared__ __attribute__((aligned(1024))) char lx0[XOP], lx1[XOP], le0[EOP], le1[EOP];
+  // (the wave index is uniform: readfirstlane keeps it, and the LDS addresses
+  // derived from it, in scalar registers)
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lin = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  const int cand = lin / tiles, tile = lin - cand * tiles;
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const int m0 = tm * kLossM, n0 = tn * kLossN;
+  const int rows_m = min(kLossM, M - m0), rows_n = min(kLossN, N - n0);
+  const int nsteps = (K + TK - 1) / TK;
+  const int G = K >> gshift;
+
+  // scaled activations: wave w fills rows 64 w .. 64 w + 63 of the X tile
+  // with 8 loads of 8 rows x 128 B (lane l: row 64 w + 8 j + l / 8, slot
+  // l % 8).  The swizzled chunk of a lane depends on j only through j's
+  // parity, so two lane offsets serve all 8 loads; the row block 8 j and the
+  // step go in the scalar offset.
+  const __amdgpu_buffer_rsrc_t rx = rsrc(XS + ((size_t)cand * M + m0) * K, (uint32_t)rows_m * K * 2);
+  const int xrow = 64 * wave + (lane >> 3);
+  int xchunk[2];
+  uint32_t xoff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    xchunk[j] = swz_chunk(xrow + 8 * j, lane & 7);
+    xoff[j] = (uint32_t)xrow * K * 2 + xchunk[j] * 16;
+  }
+  auto load_x = [&](int step, int buf) {
+    char* dx = (buf ? lx1 : lx0) + wave * 8192;
+    // (readfirstlane: the step offset stays scalar instead of being shared
+    // with the weights' lane offsets, which would make the loads divergent)
+    const int sx = __builtin_amdgcn_readfirstlane(step * TK * 2);
+    // the scalar offset is outside the hardware's range check: rows past M
+    // and a prefetch past the last step take the out-of-range lane offset
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t o = step < nsteps && xrow + 8 * j < rows_m ? xoff[j & 1] : kOutOfRange;
+      if constexpr (KTAIL) {
+        if (step * TK + 8 * xchunk[j & 1] >= K) o = kOutOfRange;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(dx + 1024 * j), 16, o,
+                                               sx + 8 * j * K * 2, 0, 0);
+    }
+  };
+
+  // the error tile: this lane's two rows and one chunk of 8 channels
+  const int ec = lane & 7, er0 = 16 * wave + (lane >> 3), er1 = er0 + 8;
+  const bool ok0 = er0 < rows_n, ok1 = er1 < rows_n;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(W + (size_t)n0 * K, (uint32_t)rows_n * K * 2);
+  const __amdgpu_buffer_rsrc_t rsv = rsrc(s_all + (size_t)cand * K, (uint32_t)K * 4);
+  // group parameters of this candidate (G * N * 4 <= 2^31 bytes, checked by the caller)
+  const __amdgpu_buffer_rsrc_t rg = rsrc(gp + (size_t)cand * G * N, (uint32_t)G * N * 4);
+  const uint32_t wo0 = (uint32_t)er0 * K * 2 + 16 * ec, wo1 = (uint32_t)er1 * K * 2 + 16 * ec;
+  const uint32_t go0 = (uint32_t)(n0 + er0) * 4, go1 = (uint32_t)(n0 + er1) * 4;
+  struct Rows {
+    u32x4 w0, w1;
+    uint32_t p0, p1;
+  };
+  struct Scales {
+    float4_t s0, s1;
+  };
+  // The loads below need no guards: past the last step or past K a scale or
+  // group-parameter offset lies past its resource's range (zero), and a
+  // weight offset reads the next row or nothing (the last row); the build
+  // masks channels past K, and a tile built past the last step is never read.
+  // the candidate's scales of the lane's 8 channels (the same for all rows:
+  // L2-resident, loaded in the step that uses them)
+  auto fetch_scales = [&](int step, Scales& c) {
+    const uint32_t so = (uint32_t)(step * TK + 8 * ec) * 4;
+    c.s0 = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rsv, so, 0, 0));
+    c.s1 = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rsv, so, 16, 0));
+  };
+  auto fetch = [&](int step, Rows& f) {
+    f.w0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo0 + step * TK * 2, 0, 0));
+    f.w1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo1 + step * TK * 2, 0, 0));
+    const uint32_t go = (uint32_t)((step * TK + 8 * ec) >> gshift) * N * 4;
+    f.p0 = __builtin_amdgcn_raw_buffer_load_b32(rg, go + go0, 0, 0);
+    f.p1 = __builtin_amdgcn_raw_buffer_load_b32(rg, go + go1, 0, 0);
+  };
+  const int es0 = er0 * 128 + 16 * swz_chunk(er0, ec), es1 = er1 * 128 + 16 * swz_chunk(er1, ec);
+  auto build = [&](int step, const Rows& f, const Scales& c, int buf) {
+    const bool kin = !KTAIL || step * TK + 8 * ec < K;
+    // rows past N and channels past K hold zeros (their parameters are zero
+    // and would give NaN)
+    const half8_t e0 = scaled_error8(f.w0, f.p0, c.s0, c.s1), e1 = scaled_error8(f.w1, f.p1, c.s0, c.s1);
+    char* de = buf ? le1 : le0;
+    *reinterpret_cast<u32x4*>(de + es0) = kin && ok0 ? __builtin_bit_cast(u32x4, e0) : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(de + es1) = kin && ok1 ? __builtin_bit_cast(u32x4, e1) : u32x4{0u, 0u, 0u, 0u};
+  };
+
+  float16_t acc[AM][AN];
+#pragma unroll
+  for (int a = 0; a < AM; ++a)
+#pragma unroll
+    for (int b = 0; b < AN; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+  const int wm = (wave % WM) * (32 * AM), wn = (wave / WM) * (32 * AN);
+  const int fi = lane & 31, fh = lane >> 5;  // fragment row and k-half of this lane
+  const int fsw = (fi >> 1) & 7;             // swizzle of the fragment rows (bases are multiples of 32)
+  auto compute = [&](int buf) {
+    const char* xa = (buf ? lx1 : lx0) + (wm + fi) * 128;
+    const char* eb = (buf ? le1 : le0) + (wn + fi) * 128;
+#pragma unroll
+    for (int ks = 0; ks < TK / 16; ++ks) {
+      const int slot = 16 * ((2 * ks + fh) ^ fsw);
+      half8_t af[AM], bf[AN];
+#pragma unroll
+      for (int a = 0; a < AM; ++a) af[a] = *reinterpret_cast<const half8_t*>(xa + 32 * 128 * a + slot);
+#pragma unroll
+      for (int b = 0; b < AN; ++b) bf[b] = *reinterpret_cast<const half8_t*>(eb + 32 * 128 * b + slot);
+#pragma unroll
+      for (int a = 0; a < AM; ++a)
+#pragma unroll
+        for (int b = 0; b < AN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+    }
+  };
+
+  // Two steps per trip (constant buffer indices).  A step's activation loads
+  // and the weights two steps ahead are issued first; the error tile of the
+  // next step is built while the matrix cores work on this one.
+  Rows cur, nxt;
+  Scales sc;
+  fetch_scales(0, sc);
+  fetch(0, cur);
+  load_x(0, 0);
+  fetch(1, nxt);
+  build(0, cur, sc, 0);
+  __syncthreads();
+  int step = 0;
+  for (; step + 1 < nsteps; step += 2) {
+    cur = nxt;
+    fetch_scales(step + 1, sc);
+    load_x(step + 1, 1);
+    fetch(step + 2, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    build(step + 1, cur, sc, 1);
+    compute(0);
+    __syncthreads();
+    cur = nxt;
+    fetch_scales(step + 2, sc);
+    load_x(step + 2, 0);
+    fetch(step + 3, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    // (past the last step this builds a tile that is never read: no branch
+    // here, so the waits for the loads above stay exact)
+    build(step + 2, cur, sc, 0);
+    compute(1);
+    __syncthreads();
+  }
+  if (step < nsteps) compute(0);
+
+  float ss = 0.0f;
+#pragma unroll
+  for (int a = 0; a < AM; ++a)
+#pragma unroll
+    for (int b = 0; b < AN; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ss += acc[a][b][r] * acc[a][b][r];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  if (lane == 0) partial[((size_t)cand * tiles + tile) * kLossWaves + wave] = (double)ss;
+}
+
 // Tile edge of the loss product: 256 (8 waves) once M fills it, else 128.
 int loss_tile(int M) { return M > 128 ? 256 : 128; }
 
@@ -383,25 +633,48 @@ static hipError_t launch_sumsq(const _Float16* x, const _Float16* e, int M, int 
   return hipGetLastError();
 }
 
+// Workspace of the loss: the group parameters (4 bytes per candidate, row and
+// group, sized for the smallest group, 32 channels), the scaled activations
+// (count x M x K fp16), the candidates' reciprocals (written by the
+// parameter pass, unused here) and the per-wave partial sums.
 size_t scale_loss_workspace_bytes(int count, int M, int N, int K) {
-  const int T = loss_tile(M);
-  const size_t tiles = (size_t)((M + T - 1) / T) * ((N + T - 1) / T);
-  return align256((size_t)count * N * K * 2) + align256((size_t)count * tiles * 8);
+  const size_t tiles = (size_t)((M + kLossM - 1) / kLossM) * ((N + kLossN - 1) / kLossN);
+  return align256((size_t)count * (K / 32) * N * 4) + align256((size_t)count * M * K * 2) +
+         align256((size_t)count * K * 4) + align256((size_t)count * tiles * kLossWaves * 8);
 }
 
 hipError_t launch_scale_loss(const void* x, const void* w, const float* s, int count, int M, int N, int K,
                              int group_size, bool zero_point, void* workspace, double* loss, hipStream_t stream) {
-  const int T = loss_tile(M);
-  const int tiles_m = (M + T - 1) / T, tiles_n = (N + T - 1) / T;
+  const int tiles_m = (M + kLossM - 1) / kLossM, tiles_n = (N + kLossN - 1) / kLossN;
+  const int tiles = tiles_m * tiles_n;
   char* ws = static_cast<char*>(workspace);
-  _Float16* e = reinterpret_cast<_Float16*>(ws);
-  double* partial = reinterpret_cast<double*>(ws + align256((size_t)count * N * K * 2));
-  hipError_t err = launch_scale_error(w, s, count, N, K, group_size, zero_point, e, stream);
+  uint32_t* gp = reinterpret_cast<uint32_t*>(ws);
+  ws += align256((size_t)count * (K / 32) * N * 4);
+  _Float16* xs = reinterpret_cast<_Float16*>(ws);
+  ws += align256((size_t)count * M * K * 2);
+  float* rs = reinterpret_cast<float*>(ws);
+  ws += align256((size_t)count * K * 4);
+  double* partial = reinterpret_cast<double*>(ws);
+  hipError_t err = launch_scale_group_params(w, s, count, N, K, group_size, zero_point, gp, rs, stream);
   if (err != hipSuccess) return err;
-  const dim3 grid(tiles_m * tiles_n, count);
-  err = launch_sumsq(static_cast<const _Float16*>(x), e, M, N, K, T, tiles_m, grid, partial, 0, nullptr, false, stream);
+  const size_t words = (size_t)M * (K >> 3);
+  size_t blocks = (words + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(scaled_activations_kernel, dim3((unsigned)blocks, count), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(x), s, M, K, reinterpret_cast<u32x4*>(xs));
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(loss_finalize_kernel, dim3(count), dim3(256), 0, stream, partial, tiles_m * tiles_n, loss);
+  const dim3 grid((unsigned)((size_t)tiles * count)), block(kLossWaves * 64);
+  const _Float16* wh = static_cast<const _Float16*>(w);
+  if (K % TK == 0)
+    hipLaunchKernelGGL((loss_fused_kernel<false>), grid, block, 0, stream, xs, wh, s, gp, M, N, K,
+                       log2_group(group_size), tiles_m, tiles, partial);
+  else
+    hipLaunchKernelGGL((loss_fused_kernel<true>), grid, block, 0, stream, xs, wh, s, gp, M, N, K,
+                       log2_group(group_size), tiles_m, tiles, partial);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(loss_finalize_kernel, dim3(count), dim3(256), 0, stream, partial, tiles * kLossWaves, loss);
   return hipGetLastError();
 }
 

@@ -213,7 +213,7 @@ size_t awq_scale_candidates_workspace_bytes(int32_t M, int32_t N, int32_t K);
  * losses  out  fp64 [count] (device, 8-byte aligned), or NULL.
  * workspace: device scratch of awq_scale_search_workspace_bytes(count, M, N,
  * K) bytes, 16-byte aligned; contents not needed before or after.
- * Same shape rules as awq_pack; deterministic.
+ * Same shape rules as awq_scale_loss; deterministic.
  */
 int awq_scale_search(const void* x, const void* w, int32_t M, int32_t N, int32_t K, int32_t group_size,
                      int32_t zero_point, const float* alphas, int32_t count, int32_t duo, float* s_best,
@@ -232,11 +232,16 @@ size_t awq_scale_search_workspace_bytes(int32_t count, int32_t M, int32_t N, int
  * s     in   fp32 [count][K], every entry finite and > 0 (not checked).
  * loss  out  fp64 [count] (device, 8-byte aligned).
  * workspace: device scratch of awq_scale_loss_workspace_bytes(count, M, N, K)
- * bytes (count * N * K * 2 for the per-candidate weight errors, plus the
- * per-tile sums), 16-byte aligned; contents not needed before or after.
- * Accuracy: the weight error Q(W s) s^-1 - W is formed in fp32 and rounded to
- * fp16 (relative 2^-11), the product accumulates in fp32 and the sum of
- * squares in fp64: |loss - L| <= 1e-3 * L.  Deterministic.
+ * bytes (count * N * K / 8 for the groups' scales and zero points of every
+ * candidate, count * M * K * 2 for the activations scaled by each candidate,
+ * plus per-wave sums), 16-byte aligned; contents not needed before or after.
+ * Shapes: as awq_pack, and K * N < 2^34.
+ * Computed as || (X diag(s)^-1) (Q(W s)' - W s)^T ||: the scaled weight error
+ * is formed next to the matrix cores (never stored) in fp32 from the exact
+ * code times scale, rounded once to fp16 (relative 2^-11), the scaled
+ * activations are rounded to fp16 (relative 2^-11), the product accumulates
+ * in fp32 and the sum of squares in fp64: |loss - L| <= 1e-3 * L.  The codes
+ * are awq_pack's codes of fp16(W s) bit for bit.  Deterministic.
  */
 int awq_scale_loss(const void* x, const void* w, const float* s, int32_t count, int32_t M, int32_t N, int32_t K,
                    int32_t group_size, int32_t zero_point, void* workspace, size_t workspace_bytes, double* loss,
