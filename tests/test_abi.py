@@ -210,8 +210,13 @@ def test_scale_search_validation(lib):
     assert loss(1, 4, 8, 128, 32, loss=E + 4) == awq.AWQ_ERR_ALIGN
     assert loss(1, 4, 8, 128, 32, s=C + 8) == awq.AWQ_ERR_ALIGN
     need = awq.load_library().awq_scale_loss_workspace_bytes(3, 4, 8, 128)
-    assert need >= 3 * 8 * 128 * 2
+    # group parameters (4 bytes per candidate, row and 32-channel group) and
+    # the activations scaled by each candidate
+    assert need >= 3 * (128 // 32) * 8 * 4 + 3 * 4 * 128 * 2
     assert loss(3, 4, 8, 128, 32, wsb=need - 1) == awq.AWQ_ERR_WORKSPACE
+    # the loss product's parameter range: K * N < 2^34 (checked before anything runs)
+    assert loss(1, 4, 1 << 17, 1 << 17, 128) == awq.AWQ_ERR_SHAPE
+    assert srch(2, 4, 1 << 17, 1 << 17, 128) == awq.AWQ_ERR_SHAPE
 
 
 def test_clip_and_scale_columns_validation(lib):
