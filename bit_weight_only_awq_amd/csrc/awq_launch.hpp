@@ -51,10 +51,9 @@ hipError_t launch_scale_search(const void* x, const void* w, int M, int N, int K
                                void* workspace, hipStream_t stream);
 
 // Group parameters of fp16(w[n][k] * s[c][k]) for each candidate c:
-// gp[c][j][n] = fp16 scale bits | zero point << 16 (4 bytes each), and
-// rs[c][k] = rcp(s[c][k]).
+// gp[c][j][n] = fp16 scale bits | zero point << 16 (4 bytes each).
 hipError_t launch_scale_group_params(const void* w, const float* s, int count, int N, int K, int group_size,
-                                     bool zero_point, void* gp, float* rs, hipStream_t stream);
+                                     bool zero_point, void* gp, hipStream_t stream);
 
 // dst = fp16(src * s) or fp16(src / s), s per column (input channel).
 hipError_t launch_scale_columns(const void* src, int rows, int K, const float* s, bool divide, void* dst,

@@ -119,21 +119,26 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restr
 // Group parameters of the candidate-scaled weights, for the objective
 //   L(s) = || Q(W diag(s)) (diag(s)^-1 X) - W X ||
 // ("AI-Research-SKILLs AWQ 高级使用指南", section 算法原理), which the loss
-// product evaluates as || X e^T || with e = Dq(Q(fp16(w * s))) / s - w built
-// tile by tile beside the matrix cores.  Whatever needs a whole group comes
-// from here: for every candidate c (an inner loop, so the weights are read
-// once for all candidates), row n and group j of the scaled weights
-// a = fp16(w[n][k] * s_c[k]) (fp32 product, rounded once),
+// product evaluates with the quantization error of W diag(s) built tile by
+// tile beside the matrix cores.  What needs a whole group comes from here:
+// for every candidate c, row n and group j of the scaled weights
+// a = fp16(w[n][k] * s_c[k]) (fp32 product, rounded once to fp16),
 //   gp[c][j][n] = fp16 scale bits | zero point << 16,
 // the scale and zero point of pack_kernel's quantizer, so that the loss
-// product's codes are pack_kernel's codes bit for bit.  The blocks of the first row octet also write
-// rs[c][k] = rcp(s_c[k]).  Same block shape and K slices as pack_kernel.
+// product's codes are pack_kernel's codes bit for bit.  The weights are read
+// once for all candidates.  The group's extremes of a are the fp16 roundings
+// of the extremes of the fp32 products (rounding is monotone), so a lane
+// takes the extremes of its 16 products per candidate and rounds only the
+// group's two.  Candidates go in sets of GW (the lanes of a group): a
+// transposed reduction leaves lane p of the group with the extremes of
+// candidate p of the set, and each lane computes one scale and zero point
+// (two divisions) per set instead of one per candidate.  Same block shape
+// and K slices as pack_kernel.
 template <int GW, bool ZP>
 __global__ __launch_bounds__(kPackThreads) void scale_group_params_kernel(const u32x4* __restrict__ w,
                                                                           const float* __restrict__ s_all, int count,
                                                                           int N, int K, int chunk_words,
-                                                                          uint32_t* __restrict__ gp,
-                                                                          float* __restrict__ rs_all) {
+                                                                          uint32_t* __restrict__ gp) {
   constexpr int WPL = kPackWords;
   constexpr int kPass = 32 * WPL;
   const int t = threadIdx.x;
@@ -141,62 +146,66 @@ __global__ __launch_bounds__(kPackThreads) void scale_group_params_kernel(const 
   const int n = blockIdx.x * 8 + r;
   const int kw = K >> 3;
   const int G = kw / (WPL * GW);
+  const int pos = l % GW;  // the lane's place in its group
   const int j_begin = blockIdx.y * chunk_words;
   const int j_end = min(kw, j_begin + chunk_words);  // multiples of WPL: no lane's words straddle j_end
-  const u32x4* wrow = w + (size_t)n * kw;
+  // Unconditional buffer loads: a lane past the slice end reads other
+  // weights or zeros and writes nothing, and its whole group is past the end
+  // with it (no branch around each load).
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(w + (size_t)blockIdx.x * 8 * kw), 0, 8 * kw * 16, 0x00020000);
   for (int w0 = j_begin; w0 < j_end; w0 += kPass) {
     const int j = w0 + WPL * l;
     const bool active = j < j_end;
     float hv[8 * WPL];
 #pragma unroll
     for (int i = 0; i < WPL; ++i) {
-      const half8_t h = as_half8(active ? wrow[j + i] : u32x4{0u, 0u, 0u, 0u});
+      const half8_t h = __builtin_bit_cast(
+          half8_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t)(r * kw + j + i) * 16, 0, 0));
 #pragma unroll
       for (int c = 0; c < 8; ++c) hv[8 * i + c] = (float)h[c];
     }
     const int grp = j / (WPL * GW);
-    const bool leader = active && (l % GW) == 0;
-    for (int c = 0; c < count; ++c) {
-      const float* sc = s_all + (size_t)c * K + 8 * j;
-      float sv[8 * WPL];
+    for (int c0 = 0; c0 < count; c0 += GW) {
+      int mn[GW], mx[GW];  // order-preserving images of the lane's extremes
 #pragma unroll
-      for (int i = 0; i < 2 * WPL; ++i) {
-        const float4_t v = active ? *reinterpret_cast<const float4_t*>(sc + 4 * i) : float4_t{1.f, 1.f, 1.f, 1.f};
+      for (int i = 0; i < GW; ++i) {
+        const int c = min(c0 + i, count - 1);  // a short last set repeats the last candidate
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s_all + (size_t)c * K), 0, K * 4, 0x00020000);
+        float sv[8 * WPL];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sv[4 * i + q] = v[q];
-      }
-      // the group's extremes of fp16(w * s_c) are the fp16 roundings of the
-      // extremes of the fp32 products (rounding is monotone): two
-      // conversions per lane instead of one per weight
-      float mn, mx;
-      if constexpr (ZP) {
-        mn = mx = fp32_product(hv[0], sv[0]);
+        for (int q4 = 0; q4 < 2 * WPL; ++q4) {
+          const float4_t v = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)j * 32, 16 * q4, 0));
 #pragma unroll
-        for (int q = 1; q < 8 * WPL; ++q) {
-          const float v = fp32_product(hv[q], sv[q]);
-          mn = fminf(mn, v);
-          mx = fmaxf(mx, v);
+          for (int q = 0; q < 4; ++q) sv[4 * q4 + q] = v[q];
         }
-        mn = (float)(_Float16)mn;
-      } else {
-        mn = 0.0f;
-        mx = fabsf(fp32_product(hv[0], sv[0]));
+        if constexpr (ZP) {
+          float lo = fp32_product(hv[0], sv[0]), hi = lo;
 #pragma unroll
-        for (int q = 1; q < 8 * WPL; ++q) mx = fmaxf(mx, fabsf(fp32_product(hv[q], sv[q])));
+          for (int q = 1; q < 8 * WPL; ++q) {
+            const float v = fp32_product(hv[q], sv[q]);
+            lo = fminf(lo, v);
+            hi = fmaxf(hi, v);
+          }
+          mn[i] = ord_of(lo);
+          mx[i] = ord_of(hi);
+        } else {
+          float hi = fabsf(fp32_product(hv[0], sv[0]));
+#pragma unroll
+          for (int q = 1; q < 8 * WPL; ++q) hi = fmaxf(hi, fabsf(fp32_product(hv[q], sv[q])));
+          mx[i] = ord_of(hi);
+        }
       }
-      mx = (float)(_Float16)mx;
+      if constexpr (ZP) group_transpose<GW>(mn, MinOp());
+      group_transpose<GW>(mx, MaxOp());
+      const int c = c0 + pos;
       float s, zf;
       _Float16 s16;
-      group_scale_zero_of<GW, ZP>(mn, mx, s16, s, zf);
-      if (leader) gp[((size_t)c * G + grp) * N + n] = (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)zf << 16);
-      if (blockIdx.x == 0 && r == 0 && active) {
-        float* rs = rs_all + (size_t)c * K + 8 * j;
-#pragma unroll
-        for (int i = 0; i < 2 * WPL; ++i)
-          *reinterpret_cast<float4_t*>(rs + 4 * i) =
-              float4_t{__builtin_amdgcn_rcpf(sv[4 * i]), __builtin_amdgcn_rcpf(sv[4 * i + 1]),
-                       __builtin_amdgcn_rcpf(sv[4 * i + 2]), __builtin_amdgcn_rcpf(sv[4 * i + 3])};
-      }
+      scale_zero_of_extremes<ZP>(ZP ? (float)(_Float16)float_of(mn[0]) : 0.0f, (float)(_Float16)float_of(mx[0]), s16,
+                                 s, zf);
+      if (active && c < count)
+        gp[((size_t)c * G + grp) * N + n] = (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)zf << 16);
     }
   }
 }
@@ -376,7 +385,7 @@ int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 128 ? 7 : 8; }
 // all candidates).
 template <bool ZP>
 hipError_t launch_scale_group_params_zp(const void* w, const float* s, int count, int N, int K, int group_size,
-                                        void* gp, float* rs, hipStream_t stream) {
+                                        void* gp, hipStream_t stream) {
   constexpr int kTargetBlocks = 4096, kRingWords = 32 * kPackWords;
   const int kw = K >> 3, octets = N / 8;
   const int rings = (kw + kRingWords - 1) / kRingWords;
@@ -388,10 +397,10 @@ hipError_t launch_scale_group_params_zp(const void* w, const float* s, int count
   const u32x4* wv = static_cast<const u32x4*>(w);
   uint32_t* g = static_cast<uint32_t*>(gp);
   switch (group_size) {
-    case 32: hipLaunchKernelGGL((scale_group_params_kernel<4 / kPackWords, ZP>), grid, block, 0, stream, wv, s, count, N, K, chunk, g, rs); break;
-    case 64: hipLaunchKernelGGL((scale_group_params_kernel<8 / kPackWords, ZP>), grid, block, 0, stream, wv, s, count, N, K, chunk, g, rs); break;
-    case 128: hipLaunchKernelGGL((scale_group_params_kernel<16 / kPackWords, ZP>), grid, block, 0, stream, wv, s, count, N, K, chunk, g, rs); break;
-    case 256: hipLaunchKernelGGL((scale_group_params_kernel<32 / kPackWords, ZP>), grid, block, 0, stream, wv, s, count, N, K, chunk, g, rs); break;
+    case 32: hipLaunchKernelGGL((scale_group_params_kernel<4 / kPackWords, ZP>), grid, block, 0, stream, wv, s, count, N, K, chunk, g); break;
+    case 64: hipLaunchKernelGGL((scale_group_params_kernel<8 / kPackWords, ZP>), grid, block, 0, stream, wv, s, count, N, K, chunk, g); break;
+    case 128: hipLaunchKernelGGL((scale_group_params_kernel<16 / kPackWords, ZP>), grid, block, 0, stream, wv, s, count, N, K, chunk, g); break;
+    case 256: hipLaunchKernelGGL((scale_group_params_kernel<32 / kPackWords, ZP>), grid, block, 0, stream, wv, s, count, N, K, chunk, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -444,9 +453,9 @@ hipError_t launch_clip_apply(const void* w, const float* part, int parts, const 
 }
 
 hipError_t launch_scale_group_params(const void* w, const float* s, int count, int N, int K, int group_size,
-                                     bool zero_point, void* gp, float* rs, hipStream_t stream) {
-  return zero_point ? launch_scale_group_params_zp<true>(w, s, count, N, K, group_size, gp, rs, stream)
-                    : launch_scale_group_params_zp<false>(w, s, count, N, K, group_size, gp, rs, stream);
+                                     bool zero_point, void* gp, hipStream_t stream) {
+  return zero_point ? launch_scale_group_params_zp<true>(w, s, count, N, K, group_size, gp, stream)
+                    : launch_scale_group_params_zp<false>(w, s, count, N, K, group_size, gp, stream);
 }
 hipError_t launch_pack(const void* w, int N, int K, int group_size, bool zero_point, uint32_t* qweight,
                        void* scales, uint32_t* qzeros, hipStream_t stream) {

@@ -64,12 +64,12 @@ struct MaxOp {
 // shuffles (GW divides 32, so a group never leaves its half-wave, and all
 // lanes of a group are active or inactive together).  s16 is the fp16 scale,
 // s its fp32 value, zf the zero point as a float.
-template <int GW, bool ZP>
-__device__ __forceinline__ void group_scale_zero_of(float mn, float mx, _Float16& s16, float& s, float& zf) {
+// ... from the group's own extremes (mn, mx: smallest and largest weight with
+// a zero point; mx the largest magnitude without).
+template <bool ZP>
+__device__ __forceinline__ void scale_zero_of_extremes(float mn, float mx, _Float16& s16, float& s, float& zf) {
 #pragma clang fp contract(off)
   if constexpr (ZP) {
-    mn = group_all<GW>(mn, MinOp());
-    mx = group_all<GW>(mx, MaxOp());
     float rng = mx - mn;
     if (rng < kRangeFloor) rng = kRangeFloor;
     s16 = (_Float16)(rng / 15.0f);
@@ -77,12 +77,22 @@ __device__ __forceinline__ void group_scale_zero_of(float mn, float mx, _Float16
     zf = rintf(-mn / s);
     zf = fminf(fmaxf(zf, 0.0f), 15.0f);
   } else {
-    const float amax = group_all<GW>(mx, MaxOp());
-    const float am = amax < kRangeFloor ? kRangeFloor : amax;
+    const float am = mx < kRangeFloor ? kRangeFloor : mx;
     s16 = (_Float16)(am / 7.0f);
     s = (float)s16;
     zf = 8.0f;
   }
+}
+
+template <int GW, bool ZP>
+__device__ __forceinline__ void group_scale_zero_of(float mn, float mx, _Float16& s16, float& s, float& zf) {
+  if constexpr (ZP) {
+    mn = group_all<GW>(mn, MinOp());
+    mx = group_all<GW>(mx, MaxOp());
+  } else {
+    mx = group_all<GW>(mx, MaxOp());
+  }
+  scale_zero_of_extremes<ZP>(mn, mx, s16, s, zf);
 }
 
 // The same from the lane's NV weights (one or two packed words).
@@ -104,6 +114,45 @@ __device__ __forceinline__ void group_scale_zero(const float (&a)[NV], _Float16&
   }
 }
 
+// Transposed reduction over the GW consecutive lanes of a group: lane p of
+// the group enters with v[0..GW) (one value per item, here per candidate) and
+// leaves with v[0] = op over the group's lanes of item p.  At the step over
+// lane bit b (b = GW/2, ..., 1) a lane keeps the half of its items selected
+// by that bit and combines it with its partner's copy of the same half; the
+// partners (lane ^ 1, ^ 2, ^ 7, ^ 15 by DPP swaps and mirrors) flip bit b and
+// no higher bit, and together they span all GW lanes.  Values are the
+// order-preserving integer images of ord_of.  A group's place p is lane % GW,
+// so bit b of it is a fixed lane pattern; the selects take it as a constant
+// lane mask (left to itself the compiler rewrites the chain of selects as a
+// switch on p, eight compares and selects per value).
+__device__ __forceinline__ int select_lanes(uint64_t mask, int if_set, int if_clear) {
+  int r;
+  asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(r) : "v"(if_clear), "v"(if_set), "s"(mask));
+  return r;
+}
+
+template <int GW, class Op>
+__device__ __forceinline__ void group_transpose(int (&v)[GW], Op op) {
+#pragma unroll
+  for (int b = GW / 2; b >= 1; b /= 2) {
+    const uint64_t m = b == 1 ? 0xAAAAAAAAAAAAAAAAull
+                     : b == 2 ? 0xCCCCCCCCCCCCCCCCull
+                     : b == 4 ? 0xF0F0F0F0F0F0F0F0ull
+                              : 0xFF00FF00FF00FF00ull;
+#pragma unroll
+    for (int i = 0; i < b; ++i) {
+      const int send = select_lanes(m, v[i], v[i + b]);
+      const int keep = select_lanes(m, v[i + b], v[i]);
+      int recv;
+      if (b == 1) recv = dpp_mov<0xB1>(send);        // quad_perm [1, 0, 3, 2]
+      else if (b == 2) recv = dpp_mov<0x4E>(send);   // quad_perm [2, 3, 0, 1]
+      else if (b == 4) recv = dpp_mov<0x141>(send);  // row_half_mirror
+      else recv = dpp_mov<0x140>(send);              // row_mirror
+      v[i] = op(keep, recv);
+    }
+  }
+}
+
 // fp16(fp32(a * b)): the fp32 product, rounded to fp16 (a weight scaled by a
 // per-channel factor, as the quantizer sees it).  The empty asm keeps the
 // product an fp32 value: left alone, the compiler fuses the multiply and the
@@ -116,7 +165,7 @@ __device__ __forceinline__ float fp32_product(float a, float b) {
   return p;
 }
 
-// rne(a / s) for a lane's 8 weights of one group, as floats, where a and s
+// rne(a / s) for NE weights of one group, as floats, where a and s
 // are fp16 values (a weight and its group's scale), computed without a
 // division and without a branch.  x = a * rcp(s) lies within 2 ulp of the
 // quotient; one correction step r = fma(-x, s, a), x' = fma(r, rcp(s), x)
@@ -130,11 +179,12 @@ __device__ __forceinline__ float fp32_product(float a, float b) {
 // 0, 15) with 0 <= z <= 15) and an off-by-one in k changes nothing.
 // (Half-integer quotients are common: fp16 weights are coarse against a
 // 16-level grid, about 1 in 250 weights.)
-__device__ __forceinline__ void rounded_quotients(const float (&a)[8], float s, float (&k)[8]) {
+template <int NE>
+__device__ __forceinline__ void rounded_quotients(const float (&a)[NE], float s, float (&k)[NE]) {
 #pragma clang fp contract(off)
   const float rs = __builtin_amdgcn_rcpf(s);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < NE; ++c) {
     const float x = a[c] * rs;
     const float r = __builtin_fmaf(-x, s, a[c]);
     k[c] = rintf(__builtin_fmaf(r, rs, x));

@@ -635,12 +635,11 @@ static hipError_t launch_sumsq(const _Float16* x, const _Float16* e, int M, int 
 
 // Workspace of the loss: the group parameters (4 bytes per candidate, row and
 // group, sized for the smallest group, 32 channels), the scaled activations
-// (count x M x K fp16), the candidates' reciprocals (written by the
-// parameter pass, unused here) and the per-wave partial sums.
+// (count x M x K fp16) and the per-wave partial sums.
 size_t scale_loss_workspace_bytes(int count, int M, int N, int K) {
   const size_t tiles = (size_t)((M + kLossM - 1) / kLossM) * ((N + kLossN - 1) / kLossN);
   return align256((size_t)count * (K / 32) * N * 4) + align256((size_t)count * M * K * 2) +
-         align256((size_t)count * K * 4) + align256((size_t)count * tiles * kLossWaves * 8);
+         align256((size_t)count * tiles * kLossWaves * 8);
 }
 
 hipError_t launch_scale_loss(const void* x, const void* w, const float* s, int count, int M, int N, int K,
@@ -652,10 +651,8 @@ hipError_t launch_scale_loss(const void* x, const void* w, const float* s, int c
   ws += align256((size_t)count * (K / 32) * N * 4);
   _Float16* xs = reinterpret_cast<_Float16*>(ws);
   ws += align256((size_t)count * M * K * 2);
-  float* rs = reinterpret_cast<float*>(ws);
-  ws += align256((size_t)count * K * 4);
   double* partial = reinterpret_cast<double*>(ws);
-  hipError_t err = launch_scale_group_params(w, s, count, N, K, group_size, zero_point, gp, rs, stream);
+  hipError_t err = launch_scale_group_params(w, s, count, N, K, group_size, zero_point, gp, stream);
   if (err != hipSuccess) return err;
   const size_t words = (size_t)M * (K >> 3);
   size_t blocks = (words + 255) / 256;

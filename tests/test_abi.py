@@ -197,7 +197,8 @@ def test_scale_search_validation(lib):
     assert srch(2, 4, 8, 128, 32, best=D + 2) == awq.AWQ_ERR_ALIGN
     assert srch(2, 4, 8, 128, 32, losses=E + 4) == awq.AWQ_ERR_ALIGN
     need = awq.load_library().awq_scale_search_workspace_bytes(2, 4, 8, 128)
-    assert need >= 2 * 128 * 4 + 2 * 8 * 128 * 2
+    # the candidates' scales, their group parameters and the activations scaled by each
+    assert need >= 2 * 128 * 4 + 2 * (128 // 32) * 8 * 4 + 2 * 4 * 128 * 2
     assert srch(2, 4, 8, 128, 32, wsb=need - 1) == awq.AWQ_ERR_WORKSPACE
     loss = lambda cnt, M, N, K, g, **kw: lib.awq_scale_loss(  # noqa: E731
         kw.get("x", A) or None, kw.get("w", B) or None, kw.get("s", C) or None, cnt, M, N, K, g, 1,
