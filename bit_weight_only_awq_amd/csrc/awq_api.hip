@@ -21,6 +21,8 @@ constexpr int32_t kMaxDim = 1 << 21;
 // words at most) through a 32-bit buffer range, with offsets up to one group
 // past its end.
 bool loss_shape_ok(int32_t N, int32_t K) { return (int64_t)K * N < ((int64_t)1 << 34); }
+// The clip search's parameters take 8 bytes per ratio, row and group.
+bool clip_shape_ok(int32_t N, int32_t K) { return (int64_t)K * N < ((int64_t)1 << 33); }
 
 // Checks shared by every entry point that reads or writes a packed weight.
 int check_weight_shape(int32_t N, int32_t K, int32_t group_size) {
@@ -186,7 +188,7 @@ int awq_clip_search(const void* x, const void* w, int32_t M, int32_t N, int32_t 
                     void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_weight_shape(N, K, group_size);
   if (st != AWQ_OK) return st;
-  if (M < 1 || count < 1 || count > awq::kMaxClipCandidates) return AWQ_ERR_SHAPE;
+  if (M < 1 || count < 1 || count > awq::kMaxClipCandidates || !clip_shape_ok(N, K)) return AWQ_ERR_SHAPE;
   if (!x || !w || !ratios || !w_clipped || !workspace) return AWQ_ERR_NULL;
   for (int c = 0; c < count; ++c)
     if (!(ratios[c] > 0.0f && ratios[c] <= 1.0f)) return AWQ_ERR_SHAPE;

@@ -65,9 +65,11 @@ struct ClipRatios {
   float v[kMaxClipCandidates];
 };
 
-// e[c][n][k] = fp16(Dq(Q(clip_c(w)))[n][k] - w[n][k]) for each ratio c.
-hipError_t launch_clip_error(const void* w, const ClipRatios& ratios, int count, int N, int K, int group_size,
-                             bool zero_point, void* e, hipStream_t stream);
+// Group parameters of the clipped weights for each ratio c:
+// gp[c][j][n] = {fp16 scale bits | zero point << 16, fp16 lower bound bits |
+// fp16 upper bound bits << 16} (8 bytes each).
+hipError_t launch_clip_group_params(const void* w, const ClipRatios& ratios, int count, int N, int K, int group_size,
+                                    bool zero_point, void* gp, hipStream_t stream);
 // Per group: the ratio with the smallest summed partial error to choice[n][j]
 // (device, [N][K / group_size], always written), then the clipped weights to w_out.
 hipError_t launch_clip_apply(const void* w, const float* part, int parts, const ClipRatios& ratios, int count, int N,

@@ -210,56 +210,87 @@ __global__ __launch_bounds__(kPackThreads) void scale_group_params_kernel(const 
   }
 }
 
-// Output error of weight clipping, for the search of apply_clip ("AI-Research-
-// SKILLs AWQ 高级使用指南", section 自定义校准策略 (校准参数全景): clip the weights to reduce
-// the effect of outliers on the quantization error).  For candidate ratio
-// r_c (blockIdx.y): every group is clamped to its range shrunk by r_c (fp32,
-// then fp16), quantized as by pack_kernel, decoded, and compared with the
-// unclipped weight:  e[c][n][k] = fp16(Dq(Q(clip_c(w)))[n][k] - w[n][k]).
+// Group parameters of weight clipping, for the search of apply_clip
+// ("AI-Research-SKILLs AWQ 高级使用指南", section 自定义校准策略 (校准参数全景): clip the
+// weights to reduce the effect of outliers on the quantization error).  For
+// ratio r_c every group is clamped to its range shrunk by r_c ([r min, r max]
+// with a zero point, [-r amax, r amax] without; fp32 products), the clamped
+// weights are rounded to fp16 and quantized as by pack_kernel.  Clamping and
+// rounding are monotone, so the clamped group's extremes are those of its
+// unclamped extremes: one pass over the weights gives every ratio's scale and
+// zero point.  Per (ratio c, group j, row n):
+//   gp[c][j][n] = { fp16 scale bits | zero point << 16, fp16(lo) bits | fp16(hi) bits << 16 }.
+// The GW lanes of a group share its extremes and split the ratios between
+// them (lane p takes ratios p, p + GW, ...), so each lane computes about
+// count / GW scales.  Same block shape and K slices as pack_kernel.
 template <int GW, bool ZP>
-__global__ __launch_bounds__(kPackThreads) void clip_error_kernel(const u32x4* __restrict__ w, ClipRatios ratios,
-                                                                  int N, int K, u32x4* __restrict__ e_all) {
-  constexpr int WPL = kPackWords;  // lane l of a row owns words 2l, 2l + 1 of each 64-word pass
+__global__ __launch_bounds__(kPackThreads) void clip_group_params_kernel(const u32x4* __restrict__ w,
+                                                                         ClipRatios ratios, int count, int N, int K,
+                                                                         int chunk_words, u32x2* __restrict__ gp) {
+  constexpr int WPL = kPackWords;
+  constexpr int kPass = 32 * WPL;
   const int t = threadIdx.x;
   const int r = t >> 5, l = t & 31;
   const int n = blockIdx.x * 8 + r;
   const int kw = K >> 3;
-  const float ratio = ratios.v[blockIdx.y];
-  u32x4* e = e_all + (size_t)blockIdx.y * N * kw;
-  const u32x4* wrow = w + (size_t)n * kw;
-  u32x4 next[WPL];
-#pragma unroll
-  for (int i = 0; i < WPL; ++i) next[i] = WPL * l < kw ? wrow[WPL * l + i] : u32x4{0u, 0u, 0u, 0u};
-  for (int w0 = 0; w0 < kw; w0 += 32 * WPL) {
-    const int j = w0 + WPL * l;  // kw is a multiple of 4: a lane's words are all in or all out
-    const bool active = j < kw;
-    const int jn = j + 32 * WPL;
+  const int G = kw / (WPL * GW);
+  const int pos = l % GW;
+  const int j_begin = blockIdx.y * chunk_words;
+  const int j_end = min(kw, j_begin + chunk_words);  // multiples of WPL: no lane's words straddle j_end
+  // unconditional loads: a lane past the slice end reads other weights or
+  // zeros and writes nothing (its whole group is past the end with it)
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(w + (size_t)blockIdx.x * 8 * kw), 0, 8 * kw * 16, 0x00020000);
+  for (int w0 = j_begin; w0 < j_end; w0 += kPass) {
+    const int j = w0 + WPL * l;
+    const bool active = j < j_end;
     float a[8 * WPL];
 #pragma unroll
     for (int i = 0; i < WPL; ++i) {
-      const half8_t h = as_half8(next[i]);
+      const half8_t h = __builtin_bit_cast(
+          half8_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t)(r * kw + j + i) * 16, 0, 0));
 #pragma unroll
       for (int c = 0; c < 8; ++c) a[8 * i + c] = (float)h[c];
-      next[i] = jn < kw ? wrow[jn + i] : u32x4{0u, 0u, 0u, 0u};
     }
-    float lo, hi;
-    group_clip_bounds<GW, ZP>(a, ratio, lo, hi);
-    float cl[8 * WPL];
+    float mn = 0.0f, mx;
+    if constexpr (ZP) {
+      mn = mx = a[0];
 #pragma unroll
-    for (int c = 0; c < 8 * WPL; ++c) cl[c] = (float)(_Float16)fminf(fmaxf(a[c], lo), hi);
-    float s, zf;
-    _Float16 s16;
-    group_scale_zero<GW, ZP>(cl, s16, s, zf);
+      for (int c = 1; c < 8 * WPL; ++c) {
+        mn = fminf(mn, a[c]);
+        mx = fmaxf(mx, a[c]);
+      }
+      mn = group_all<GW>(mn, MinOp());
+      mx = group_all<GW>(mx, MaxOp());
+    } else {
+      mx = fabsf(a[0]);
 #pragma unroll
-    for (int i = 0; i < WPL; ++i) {
-      float ci[8], q[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) ci[c] = cl[8 * i + c];
-      codes_of(ci, s, zf, q);
-      half8_t out;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) out[c] = (_Float16)((q[c] - zf) * s - a[8 * i + c]);
-      if (active) e[(size_t)n * kw + j + i] = __builtin_bit_cast(u32x4, out);
+      for (int c = 1; c < 8 * WPL; ++c) mx = fmaxf(mx, fabsf(a[c]));
+      mx = group_all<GW>(mx, MaxOp());
+    }
+    const int grp = j / (WPL * GW);
+    for (int c = pos; c < count; c += GW) {
+      const float ratio = ratios.v[c];
+      float lo, hi, cmn = 0.0f, cmx;
+      // (fp32 products kept explicit: the bounds are rounded to fp16 below)
+      if constexpr (ZP) {
+        lo = fp32_product(ratio, mn);
+        hi = fp32_product(ratio, mx);
+        cmn = (float)(_Float16)fminf(fmaxf(mn, lo), hi);
+        cmx = (float)(_Float16)fminf(fmaxf(mx, lo), hi);
+      } else {
+        hi = fp32_product(ratio, mx);
+        lo = -hi;
+        cmx = (float)(_Float16)fminf(mx, hi);
+      }
+      float s, zf;
+      _Float16 s16;
+      scale_zero_of_extremes<ZP>(cmn, cmx, s16, s, zf);
+      if (active)
+        gp[((size_t)c * G + grp) * N + n] =
+            u32x2{(uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)zf << 16),
+                  (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16)};
     }
   }
 }
@@ -407,16 +438,24 @@ hipError_t launch_scale_group_params_zp(const void* w, const float* s, int count
 }
 
 template <bool ZP>
-hipError_t launch_clip_zp(const void* w, const ClipRatios& ratios, int count, int N, int K, int group_size, void* e,
+hipError_t launch_clip_zp(const void* w, const ClipRatios& ratios, int count, int N, int K, int group_size, void* gp,
                           const int32_t* choice, void* w_out, bool apply, hipStream_t stream) {
   const u32x4* wv = static_cast<const u32x4*>(w);
   const dim3 block(kPackThreads);
+  // parameters: K slices as in launch_pack_zp, to about 4096 blocks
+  constexpr int kRingWords = 32 * kPackWords;
+  const int kw = K >> 3, octets = N / 8;
+  const int rings = (kw + kRingWords - 1) / kRingWords;
+  int slices = (4096 + octets - 1) / octets;
+  if (slices > rings) slices = rings;
+  if (slices < 1) slices = 1;
+  const int chunk = ((rings + slices - 1) / slices) * kRingWords;
+  const dim3 pgrid(octets, (kw + chunk - 1) / chunk);
 #define AWQ_CLIP_CASE(G_, GW_)                                                                                   \
   case G_:                                                                                                     \
     if (!apply)                                                                                                \
-      hipLaunchKernelGGL((clip_error_kernel<GW_ / kPackWords, ZP>), dim3(N / 8, count), block, 0, stream, wv,     \
-                         ratios, N, K,                                                                         \
-                         static_cast<u32x4*>(e));                                                              \
+      hipLaunchKernelGGL((clip_group_params_kernel<GW_ / kPackWords, ZP>), pgrid, block, 0, stream, wv, ratios,  \
+                         count, N, K, chunk, static_cast<u32x2*>(gp));                                         \
     else                                                                                                       \
       hipLaunchKernelGGL((clip_apply_kernel<GW_, ZP>), dim3(N / 8), block, 0, stream, wv, N, K, ratios, choice,  \
                          static_cast<u32x4*>(w_out));                                                          \
@@ -434,10 +473,10 @@ hipError_t launch_clip_zp(const void* w, const ClipRatios& ratios, int count, in
 
 }  // namespace
 
-hipError_t launch_clip_error(const void* w, const ClipRatios& ratios, int count, int N, int K, int group_size,
-                             bool zero_point, void* e, hipStream_t stream) {
-  return zero_point ? launch_clip_zp<true>(w, ratios, count, N, K, group_size, e, nullptr, nullptr, false, stream)
-                    : launch_clip_zp<false>(w, ratios, count, N, K, group_size, e, nullptr, nullptr, false, stream);
+hipError_t launch_clip_group_params(const void* w, const ClipRatios& ratios, int count, int N, int K, int group_size,
+                                    bool zero_point, void* gp, hipStream_t stream) {
+  return zero_point ? launch_clip_zp<true>(w, ratios, count, N, K, group_size, gp, nullptr, nullptr, false, stream)
+                    : launch_clip_zp<false>(w, ratios, count, N, K, group_size, gp, nullptr, nullptr, false, stream);
 }
 
 hipError_t launch_clip_apply(const void* w, const float* part, int parts, const ClipRatios& ratios, int count, int N,

@@ -29,6 +29,8 @@
 #include "awq_launch.hpp"
 #include "awq_quant.hpp"
 
+#include <type_traits>
+
 namespace awq {
 namespace {
 
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(256) void scale_columns_kernel(const u32x4* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Sum of squares of X e_c^T.
+// Shared by the loss products.
 // ---------------------------------------------------------------------------
 // Buffer resource over `bytes` bytes at `base`: loads past the end return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -141,177 +143,6 @@ constexpr int TK = 64;  // K step
 // bank groups, and a 1 KiB run of slots is what one buffer-to-LDS load of 64
 // lanes x 16 bytes writes.
 __device__ __forceinline__ int swz_chunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
-
-// Workgroup of WM x WN waves; tile (32 WM WN) x (32 WM WN) with every wave
-// loading 32 rows of each operand: 2 x 2 waves of 64 x 64 (128 x 128 tile) or
-// 2 x 4 waves of 128 x 64 (256 x 256 tile), v_mfma_f32_32x32x16_f16; grid
-// (tiles, candidates).  Both operands stream from HBM into LDS by
-// buffer-to-LDS loads, double-buffered, one barrier per K step.  Rows past M
-// or N read as zero and add nothing to the sum.  Output: the fp64 sum of the
-// squares of the tile's outputs (each square and the per-lane sums in fp32,
-// the wave and workgroup sums in a fixed order).
-//
-// GROUPED: the squares are taken per group of g input channels instead (the
-// output error of each weight group, for the clipping search): at every group
-// boundary each wave adds the squares of its accumulators over its rows, per
-// column, writes them to gpart[c][tm][wave row half][group][n] and restarts
-// its accumulators from zero.
-template <int WM, int WN, bool KTAIL, bool GROUPED>
-__global__ __launch_bounds__(WM * WN * 64) void sumsq_gemm_kernel(const _Float16* __restrict__ X,
-                                                                  const _Float16* __restrict__ E_all, int M, int N,
-                                                                  int K, int tiles_m, double* __restrict__ partial,
-                                                                  int gshift, float* __restrict__ gpart) {
-  constexpr int NW = WM * WN;
-  constexpr int T = 32 * NW;             // tile rows of X and of E
-  constexpr int AM = T / WM / 32;        // 32x32 MFMA tiles per wave along M
-  constexpr int AN = T / WN / 32;        // ... along N
-  constexpr int OP = T * TK * 2;         // bytes of one operand tile
-  // the two buffers of each operand are separate arrays, so the compiler can
-  // tell them apart and does not make reads of one wait for the loads into
-  // the other
-  __shared__ __attribute__((aligned(1024))) char lx0[OP], lx1[OP], le0[OP], le1[OP];
-  __shared__ double wsum[NW];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  // (tile, candidate) from the workgroup's place in an XCD-contiguous order:
-  // the row tiles of one column band of a candidate's E run on one XCD and
-  // share its L2, so E is fetched once per XCD rather than once per row tile
-  const int lin = xcd_contiguous_tile(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x * gridDim.y);
-  const int tile = lin % gridDim.x, cand = lin / gridDim.x;
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
-  const int m0 = tm * T, n0 = tn * T;
-  const _Float16* E = E_all + (size_t)cand * N * K;
-  const int rows_m = min(T, M - m0), rows_n = min(T, N - n0);
-  const int nsteps = (K + TK - 1) / TK;
-
-  const __amdgpu_buffer_rsrc_t rx = rsrc(X + (size_t)m0 * K, (uint32_t)rows_m * K * 2);
-  const __amdgpu_buffer_rsrc_t re = rsrc(E + (size_t)n0 * K, (uint32_t)rows_n * K * 2);
-
-  // wave w fills rows 32 w .. 32 w + 31 of both tiles with 4 loads of 8 rows
-  // x 128 B each; lane l of load j writes slot l of that 1 KiB run: row
-  // 32 w + 8 j + l / 8, physical chunk l % 8, holding the logical chunk that
-  // swizzles there (the swizzle is an involution)
-  int chunk[4];
-  uint32_t off[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 32 * wave + 8 * j + (lane >> 3);
-    chunk[j] = swz_chunk(row, lane & 7);
-    off[j] = (uint32_t)row * K * 2 + chunk[j] * 16;
-  }
-  // `buf` is a constant at every call site (the K loop below is unrolled by two)
-  auto load = [&](int step, int buf) {
-    char* dx = (buf ? lx1 : lx0) + wave * 4096;
-    char* de = (buf ? le1 : le0) + wave * 4096;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // the step sits in the scalar offset, outside the hardware's range
-      // check: a prefetch past the last step takes the out-of-range lane offset
-      uint32_t o = step < nsteps ? off[j] : kOutOfRange;
-      if constexpr (KTAIL) {  // channels past K of the last step load as zero
-        if (step * TK + 8 * chunk[j] >= K) o = kOutOfRange;
-      }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(dx + 1024 * j), 16, o,
-                                               step * TK * 2, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (__attribute__((address_space(3))) void*)(de + 1024 * j), 16, o,
-                                               step * TK * 2, 0, 0);
-    }
-  };
-
-  float16_t acc[AM][AN];
-#pragma unroll
-  for (int a = 0; a < AM; ++a)
-#pragma unroll
-    for (int b = 0; b < AN; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-
-  const int wm = (wave % WM) * (32 * AM), wn = (wave / WM) * (32 * AN);
-  const int fi = lane & 31, fh = lane >> 5;  // fragment row and k-half of this lane
-  const int fsw = (fi >> 1) & 7;             // swizzle of the fragment rows (bases are multiples of 32)
-
-  // per-group flush (GROUPED): squares per column over this wave's rows
-  const int G = K >> gshift;
-  float* gout = GROUPED ? gpart + (((size_t)cand * tiles_m + tm) * WM + (wave % WM)) * G * N : nullptr;
-  auto flush = [&](int grp) {
-#pragma unroll
-    for (int b = 0; b < AN; ++b) {
-      float v = 0.0f;
-#pragma unroll
-      for (int a = 0; a < AM; ++a)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          v += acc[a][b][r] * acc[a][b][r];
-          acc[a][b][r] = 0.0f;
-        }
-      // lanes l and l + 32 hold the two row halves of column l % 32
-      v += __shfl_xor(v, 32);
-      const int n = n0 + wn + 32 * b + lane;
-      if (lane < 32 && n < N) gout[(size_t)grp * N + n] = v;
-    }
-  };
-
-  auto compute = [&](int buf, int step) {
-    const char* xa = (buf ? lx1 : lx0) + (wm + fi) * 128;
-    const char* eb = (buf ? le1 : le0) + (wn + fi) * 128;
-#pragma unroll
-    for (int ks = 0; ks < TK / 16; ++ks) {
-      const int slot = 16 * ((2 * ks + fh) ^ fsw);
-      half8_t af[AM], bf[AN];
-#pragma unroll
-      for (int a = 0; a < AM; ++a) af[a] = *reinterpret_cast<const half8_t*>(xa + 32 * 128 * a + slot);
-#pragma unroll
-      for (int b = 0; b < AN; ++b) bf[b] = *reinterpret_cast<const half8_t*>(eb + 32 * 128 * b + slot);
-#pragma unroll
-      for (int a = 0; a < AM; ++a)
-#pragma unroll
-        for (int b = 0; b < AN; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
-      if constexpr (GROUPED) {
-        const int kend = step * TK + (ks + 1) * 16;  // channels done after this slice
-        if ((kend & ((1 << gshift) - 1)) == 0 && kend <= K) flush((kend >> gshift) - 1);
-      }
-    }
-  };
-
-  // Two steps per trip; the scheduling barriers keep each step's loads ahead
-  // of the multiplies that hide their latency.  Loads of a step past the end
-  // read zero (out-of-range lane offset) and land in a buffer no one reads
-  // again.
-  load(0, 0);
-  __syncthreads();
-  int step = 0;
-  for (; step + 1 < nsteps; step += 2) {
-    load(step + 1, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(0, step);
-    __syncthreads();
-    load(step + 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1, step + 1);
-    __syncthreads();
-  }
-  if (step < nsteps) compute(0, step);
-  if constexpr (GROUPED) return;
-
-  float ss = 0.0f;
-#pragma unroll
-  for (int a = 0; a < AM; ++a)
-#pragma unroll
-    for (int b = 0; b < AN; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ss += acc[a][b][r] * acc[a][b][r];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-  if (lane == 0) wsum[wave] = (double)ss;
-  __syncthreads();
-  if (t == 0) {
-    double v = wsum[0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) v += wsum[w];
-    partial[(size_t)cand * gridDim.x + tile] = v;
-  }
-}
-
 
 // ---------------------------------------------------------------------------
 // The loss product with the weight error built in place.
@@ -365,34 +196,73 @@ __device__ __forceinline__ half8_t scaled_error8(u32x4 raw, uint32_t p, float4_t
   return e;
 }
 
-// Sum of the squares of xs_c e_c^T for candidate c, e_c as in scaled_error8
-// with the group quantities of scale_group_params_kernel (= L(s_c)^2).  e
-// never goes to memory: every K step the workgroup builds the 128 x 64 tile
-// of e for the next step from weights already in registers and writes it to
-// LDS, where the matrix cores read it as the B operand while the scaled
-// activations stream in by buffer-to-LDS loads, as in sumsq_gemm_kernel.
-// Tile 512 tokens x 128 weight rows, so an element of e (about eight fp32
-// operations) is built once per 512 tokens, against 512 multiply-adds on the
-// matrix cores; 8 waves of 128 x 64 (4 x 2 v_mfma_f32_32x32x16_f16 tiles);
-// 160 KiB of LDS.  For the build, lane l of wave w takes channels
-// 8 (l % 8) .. + 7 of the step (LDS chunk l % 8) in rows 16 w + l / 8 and
-// 16 w + 8 + l / 8, so each wave load covers whole 128-byte lines of 8 rows.
-// Every load is an unconditional buffer load (out-of-range offsets return
-// zero): no branch separates a load from its use, and the waits count
-// exactly.  Tiles are ordered candidate-major: the workgroups on one XCD
-// share one candidate's scaled activations in its L2.  Output: per wave, the
-// fp64 value of its fp32 sum of squares, partial[(c * tiles + tile) * 8 + wave].
-constexpr int kLossM = 512, kLossN = 128, kLossWaves = 8;
+// Clipped errors of one row's 8 channels of one group for one ratio:
+//   e = fp16( (q - z) * s_g - w ),  q = clamp(rne(c / s_g) + z, 0, 15),  c = clamp(w, lo, hi)
+// with p = { s_g bits | z << 16, fp16(lo) bits | fp16(hi) bits << 16 }, the
+// group's clipped scale, zero point and fp32 bounds rounded to fp16.  For an
+// fp16 weight, clamping to the rounded bounds gives the fp16 rounding of the
+// clamp to the fp32 bounds (no fp16 value lies strictly between a bound and
+// its nearest fp16 value), which is what the quantizer sees.
+__device__ __forceinline__ half8_t clipped_error8(u32x4 raw, u32x2 p) {
+  const half8_t h = as_half8(raw);
+  const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[0] & 0xFFFFu));
+  const float zf = (float)(p[0] >> 16);
+  const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[1] & 0xFFFFu));
+  const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[1] >> 16));
+  float a[8], k[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) a[c] = __builtin_amdgcn_fmed3f((float)h[c], lo, hi);
+  rounded_quotients(a, s, k);
+  half8_t e;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    e[c] = (_Float16)__builtin_fmaf(__builtin_amdgcn_fmed3f(k[c], -zf, 15.0f - zf), s, -(float)h[c]);
+  return e;
+}
 
-template <bool KTAIL>
+// The loss products of the two searches, with the weight error built in
+// place:
+//  * scale search (CLIP false): the sum of the squares of xs_c e_c^T for
+//    candidate c, e_c as in scaled_error8 with the group quantities of
+//    scale_group_params_kernel (= L(s_c)^2);
+//  * clip search (CLIP true): for ratio c, the squares of x e_c^T summed per
+//    group of input channels (the output error of each weight group, e_c as
+//    in clipped_error8 with the quantities of clip_group_params_kernel).
+// e never goes to memory: every K step the workgroup builds the 128 x 64 tile
+// of e for the next step from weights already in registers and writes it to
+// LDS, where the matrix cores read it as the B operand while the activations
+// stream in by buffer-to-LDS loads.  Tile 512 tokens x 128 weight rows, so an
+// element of e (about eight fp32 operations) is built once per 512 tokens,
+// against 512 multiply-adds on the matrix cores; 8 waves of 128 x 64 (4 x 2
+// v_mfma_f32_32x32x16_f16 tiles), two per SIMD, so that one wave's loads,
+// build and LDS waits overlap the other's products (one wave per SIMD with
+// 128 x 128 tiles was 10% slower); 160 KiB of LDS.  Operands through LDS:
+// 16-byte chunk c of row r in slot c ^ ((r >> 1) & 7).  For the build, lane l
+// of wave w takes channels 8 (l % 8) .. + 7 of the step (LDS chunk l % 8) in
+// rows 16 w + l / 8 and 16 w + 8 + l / 8, so each wave load covers whole
+// 128-byte lines of 8 rows.  Every load is an unconditional buffer load
+// (out-of-range offsets return zero): no branch separates a load from its
+// use, and the waits count exactly.  Tiles are ordered candidate-major: the
+// workgroups on one XCD share one candidate's activations in its L2.
+// Output: scale search, per wave the fp64 value of its fp32 sum of squares,
+// partial[(c * tiles + tile) * 8 + wave]; clip search, at every group
+// boundary each wave adds the squares of its accumulators over its 128
+// tokens per column, writes them to gpart[c][tm][wave % 4][group][n] and
+// restarts its accumulators from zero.
+constexpr int kLossM = 512, kLossN = 128, kLossWaves = 8, kLossWM = 4;
+
+template <bool KTAIL, bool CLIP>
 __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Float16* __restrict__ XS,
                                                                    const _Float16* __restrict__ W,
                                                                    const float* __restrict__ s_all,
                                                                    const uint32_t* __restrict__ gp, int M, int N, int K,
                                                                    int gshift, int tiles_m, int tiles,
-                                                                   double* __restrict__ partial) {
-  constexpr int AM = 4, AN = 2, WM = 4;
+                                                                   double* __restrict__ partial,
+                                                                   float* __restrict__ gpart) {
+  constexpr int AM = 4, AN = 2, WM = kLossWM;
   constexpr int XOP = kLossM * TK * 2, EOP = kLossN * TK * 2;
+  constexpr int PE = CLIP ? 8 : 4;  // bytes of one group-parameter entry
+  typedef typename std::conditional<CLIP, u32x2, uint32_t>::type param_t;
   __shared__ __attribute__((aligned(1024))) char lx0[XOP], lx1[XOP], le0[EOP], le1[EOP];
   // (the wave index is uniform: readfirstlane keeps it, and the LDS addresses
   // derived from it, in scalar registers)
@@ -405,12 +275,14 @@ __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Floa
   const int nsteps = (K + TK - 1) / TK;
   const int G = K >> gshift;
 
-  // scaled activations: wave w fills rows 64 w .. 64 w + 63 of the X tile
+  // activations (each candidate's scaled copy for the scale search, the one
+  // X for the clip search): wave w fills rows 64 w .. 64 w + 63 of the X tile
   // with 8 loads of 8 rows x 128 B (lane l: row 64 w + 8 j + l / 8, slot
   // l % 8).  The swizzled chunk of a lane depends on j only through j's
   // parity, so two lane offsets serve all 8 loads; the row block 8 j and the
   // step go in the scalar offset.
-  const __amdgpu_buffer_rsrc_t rx = rsrc(XS + ((size_t)cand * M + m0) * K, (uint32_t)rows_m * K * 2);
+  const __amdgpu_buffer_rsrc_t rx =
+      rsrc(XS + ((CLIP ? 0 : (size_t)cand * M) + m0) * K, (uint32_t)rows_m * K * 2);
   const int xrow = 64 * wave + (lane >> 3);
   int xchunk[2];
   uint32_t xoff[2];
@@ -441,14 +313,15 @@ __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Floa
   const int ec = lane & 7, er0 = 16 * wave + (lane >> 3), er1 = er0 + 8;
   const bool ok0 = er0 < rows_n, ok1 = er1 < rows_n;
   const __amdgpu_buffer_rsrc_t rw = rsrc(W + (size_t)n0 * K, (uint32_t)rows_n * K * 2);
-  const __amdgpu_buffer_rsrc_t rsv = rsrc(s_all + (size_t)cand * K, (uint32_t)K * 4);
-  // group parameters of this candidate (G * N * 4 <= 2^31 bytes, checked by the caller)
-  const __amdgpu_buffer_rsrc_t rg = rsrc(gp + (size_t)cand * G * N, (uint32_t)G * N * 4);
+  const __amdgpu_buffer_rsrc_t rsv = rsrc(s_all + (CLIP ? 0 : (size_t)cand * K), CLIP ? 0u : (uint32_t)K * 4);
+  // group parameters of this candidate (G * N * PE <= 2^31 bytes, checked by the caller)
+  const __amdgpu_buffer_rsrc_t rg =
+      rsrc(reinterpret_cast<const char*>(gp) + (size_t)cand * G * N * PE, (uint32_t)G * N * PE);
   const uint32_t wo0 = (uint32_t)er0 * K * 2 + 16 * ec, wo1 = (uint32_t)er1 * K * 2 + 16 * ec;
-  const uint32_t go0 = (uint32_t)(n0 + er0) * 4, go1 = (uint32_t)(n0 + er1) * 4;
+  const uint32_t go0 = (uint32_t)(n0 + er0) * PE, go1 = (uint32_t)(n0 + er1) * PE;
   struct Rows {
     u32x4 w0, w1;
-    uint32_t p0, p1;
+    param_t p0, p1;
   };
   struct Scales {
     float4_t s0, s1;
@@ -460,23 +333,37 @@ __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Floa
   // the candidate's scales of the lane's 8 channels (the same for all rows:
   // L2-resident, loaded in the step that uses them)
   auto fetch_scales = [&](int step, Scales& c) {
-    const uint32_t so = (uint32_t)(step * TK + 8 * ec) * 4;
-    c.s0 = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rsv, so, 0, 0));
-    c.s1 = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rsv, so, 16, 0));
+    if constexpr (!CLIP) {
+      const uint32_t so = (uint32_t)(step * TK + 8 * ec) * 4;
+      c.s0 = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rsv, so, 0, 0));
+      c.s1 = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rsv, so, 16, 0));
+    }
   };
   auto fetch = [&](int step, Rows& f) {
     f.w0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo0 + step * TK * 2, 0, 0));
     f.w1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, wo1 + step * TK * 2, 0, 0));
-    const uint32_t go = (uint32_t)((step * TK + 8 * ec) >> gshift) * N * 4;
-    f.p0 = __builtin_amdgcn_raw_buffer_load_b32(rg, go + go0, 0, 0);
-    f.p1 = __builtin_amdgcn_raw_buffer_load_b32(rg, go + go1, 0, 0);
+    const uint32_t go = (uint32_t)((step * TK + 8 * ec) >> gshift) * N * PE;
+    if constexpr (CLIP) {
+      f.p0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, go + go0, 0, 0));
+      f.p1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, go + go1, 0, 0));
+    } else {
+      f.p0 = __builtin_amdgcn_raw_buffer_load_b32(rg, go + go0, 0, 0);
+      f.p1 = __builtin_amdgcn_raw_buffer_load_b32(rg, go + go1, 0, 0);
+    }
   };
   const int es0 = er0 * 128 + 16 * swz_chunk(er0, ec), es1 = er1 * 128 + 16 * swz_chunk(er1, ec);
   auto build = [&](int step, const Rows& f, const Scales& c, int buf) {
     const bool kin = !KTAIL || step * TK + 8 * ec < K;
     // rows past N and channels past K hold zeros (their parameters are zero
     // and would give NaN)
-    const half8_t e0 = scaled_error8(f.w0, f.p0, c.s0, c.s1), e1 = scaled_error8(f.w1, f.p1, c.s0, c.s1);
+    half8_t e0, e1;
+    if constexpr (CLIP) {
+      e0 = clipped_error8(f.w0, f.p0);
+      e1 = clipped_error8(f.w1, f.p1);
+    } else {
+      e0 = scaled_error8(f.w0, f.p0, c.s0, c.s1);
+      e1 = scaled_error8(f.w1, f.p1, c.s0, c.s1);
+    }
     char* de = buf ? le1 : le0;
     *reinterpret_cast<u32x4*>(de + es0) = kin && ok0 ? __builtin_bit_cast(u32x4, e0) : u32x4{0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4*>(de + es1) = kin && ok1 ? __builtin_bit_cast(u32x4, e1) : u32x4{0u, 0u, 0u, 0u};
@@ -493,7 +380,26 @@ __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Floa
   const int wm = (wave % WM) * (32 * AM), wn = (wave / WM) * (32 * AN);
   const int fi = lane & 31, fh = lane >> 5;  // fragment row and k-half of this lane
   const int fsw = (fi >> 1) & 7;             // swizzle of the fragment rows (bases are multiples of 32)
-  auto compute = [&](int buf) {
+  // clip search: squares per column over this wave's 128 tokens; lanes l and
+  // l + 32 hold the two halves of column l % 32 of each 32 x 32 tile
+  float* gout = CLIP ? gpart + (((size_t)cand * tiles_m + tm) * WM + (wave % WM)) * G * N : nullptr;
+  auto flush = [&](int grp) {
+#pragma unroll
+    for (int b = 0; b < AN; ++b) {
+      float v = 0.0f;
+#pragma unroll
+      for (int a = 0; a < AM; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          v += acc[a][b][r] * acc[a][b][r];
+          acc[a][b][r] = 0.0f;
+        }
+      v += __shfl_xor(v, 32);
+      const int n = n0 + wn + 32 * b + lane;
+      if (lane < 32 && n < N) gout[(size_t)grp * N + n] = v;
+    }
+  };
+  auto compute = [&](int buf, int step) {
     const char* xa = (buf ? lx1 : lx0) + (wm + fi) * 128;
     const char* eb = (buf ? le1 : le0) + (wn + fi) * 128;
 #pragma unroll
@@ -509,6 +415,10 @@ __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Floa
 #pragma unroll
         for (int b = 0; b < AN; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
+      if constexpr (CLIP) {
+        const int kend = step * TK + (ks + 1) * 16;  // channels done after this slice
+        if ((kend & ((1 << gshift) - 1)) == 0 && kend <= K) flush((kend >> gshift) - 1);
+      }
     }
   };
 
@@ -531,7 +441,7 @@ __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Floa
     fetch(step + 2, nxt);
     __builtin_amdgcn_sched_barrier(0);
     build(step + 1, cur, sc, 1);
-    compute(0);
+    compute(0, step);
     __syncthreads();
     cur = nxt;
     fetch_scales(step + 2, sc);
@@ -541,10 +451,11 @@ __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Floa
     // (past the last step this builds a tile that is never read: no branch
     // here, so the waits for the loads above stay exact)
     build(step + 2, cur, sc, 0);
-    compute(1);
+    compute(1, step + 1);
     __syncthreads();
   }
-  if (step < nsteps) compute(0);
+  if (step < nsteps) compute(0, step);
+  if constexpr (CLIP) return;
 
   float ss = 0.0f;
 #pragma unroll
@@ -557,9 +468,6 @@ __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Floa
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
   if (lane == 0) partial[((size_t)cand * tiles + tile) * kLossWaves + wave] = (double)ss;
 }
-
-// Tile edge of the loss product: 256 (8 waves) once M fills it, else 128.
-int loss_tile(int M) { return M > 128 ? 256 : 128; }
 
 // loss[c] = sqrt(sum of candidate c's tile partials), summed by one workgroup
 // in a fixed order.
@@ -608,31 +516,6 @@ hipError_t launch_scale_candidates(const void* x, int M, int K, const void* w, i
   return hipGetLastError();
 }
 
-// The loss product: whole-tile sums (scale search) or per-group sums (clip search).
-static hipError_t launch_sumsq(const _Float16* x, const _Float16* e, int M, int N, int K, int T, int tiles_m,
-                               dim3 grid, double* partial, int gshift, float* gpart, bool grouped,
-                               hipStream_t stream) {
-  const bool tail = K % TK != 0;
-#define AWQ_SUMSQ(WM_, WN_, TAIL_, GR_)                                                                          \
-  hipLaunchKernelGGL((sumsq_gemm_kernel<WM_, WN_, TAIL_, GR_>), grid, dim3(WM_ * WN_ * 64), 0, stream, x, e, M, N, \
-                     K, tiles_m, partial, gshift, gpart)
-  if (T == 256) {
-    if (grouped) {
-      if (tail) AWQ_SUMSQ(2, 4, true, true); else AWQ_SUMSQ(2, 4, false, true);
-    } else {
-      if (tail) AWQ_SUMSQ(2, 4, true, false); else AWQ_SUMSQ(2, 4, false, false);
-    }
-  } else {
-    if (grouped) {
-      if (tail) AWQ_SUMSQ(2, 2, true, true); else AWQ_SUMSQ(2, 2, false, true);
-    } else {
-      if (tail) AWQ_SUMSQ(2, 2, true, false); else AWQ_SUMSQ(2, 2, false, false);
-    }
-  }
-#undef AWQ_SUMSQ
-  return hipGetLastError();
-}
-
 // Workspace of the loss: the group parameters (4 bytes per candidate, row and
 // group, sized for the smallest group, 32 channels), the scaled activations
 // (count x M x K fp16) and the per-wave partial sums.
@@ -664,11 +547,11 @@ hipError_t launch_scale_loss(const void* x, const void* w, const float* s, int c
   const dim3 grid((unsigned)((size_t)tiles * count)), block(kLossWaves * 64);
   const _Float16* wh = static_cast<const _Float16*>(w);
   if (K % TK == 0)
-    hipLaunchKernelGGL((loss_fused_kernel<false>), grid, block, 0, stream, xs, wh, s, gp, M, N, K,
-                       log2_group(group_size), tiles_m, tiles, partial);
+    hipLaunchKernelGGL((loss_fused_kernel<false, false>), grid, block, 0, stream, xs, wh, s, gp, M, N, K,
+                       log2_group(group_size), tiles_m, tiles, partial, nullptr);
   else
-    hipLaunchKernelGGL((loss_fused_kernel<true>), grid, block, 0, stream, xs, wh, s, gp, M, N, K,
-                       log2_group(group_size), tiles_m, tiles, partial);
+    hipLaunchKernelGGL((loss_fused_kernel<true, false>), grid, block, 0, stream, xs, wh, s, gp, M, N, K,
+                       log2_group(group_size), tiles_m, tiles, partial, nullptr);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(loss_finalize_kernel, dim3(count), dim3(256), 0, stream, partial, tiles * kLossWaves, loss);
@@ -713,32 +596,42 @@ hipError_t launch_scale_columns(const void* src, int rows, int K, const float* s
   return hipGetLastError();
 }
 
-// Per-group partial errors: part[c][tm][h][j][n], h the two row halves of a tile.
+// Clip search workspace: the group parameters of every ratio (8 bytes per
+// ratio, row and group) and the per-group partial errors
+// part[c][tm][wave % 4][j][n] (4 token quarters of each 512-token tile).
 size_t clip_search_workspace_bytes(int count, int M, int N, int K, int group_size) {
-  const int T = loss_tile(M);
-  const size_t tiles_m = (M + T - 1) / T;
-  return align256((size_t)count * N * K * 2) + align256((size_t)count * tiles_m * 2 * (K / group_size) * N * 4);
+  const size_t tiles_m = (M + kLossM - 1) / kLossM, G = K / group_size;
+  return align256((size_t)count * G * N * 8) + align256((size_t)count * tiles_m * kLossWM * G * N * 4);
 }
 
 hipError_t launch_clip_search(const void* x, const void* w, int M, int N, int K, int group_size, bool zero_point,
                               const float* ratios, int count, void* w_out, int32_t* choice, void* workspace,
                               hipStream_t stream) {
-  const int T = loss_tile(M);
-  const int tiles_m = (M + T - 1) / T, tiles_n = (N + T - 1) / T;
+  const int tiles_m = (M + kLossM - 1) / kLossM, tiles_n = (N + kLossN - 1) / kLossN;
+  const int tiles = tiles_m * tiles_n;
+  const size_t G = K / group_size;
   char* ws = static_cast<char*>(workspace);
-  _Float16* e = reinterpret_cast<_Float16*>(ws);
-  float* gpart = reinterpret_cast<float*>(ws + align256((size_t)count * N * K * 2));
+  uint32_t* gp = reinterpret_cast<uint32_t*>(ws);
+  float* gpart = reinterpret_cast<float*>(ws + align256((size_t)count * G * N * 8));
   ClipRatios r;
   for (int c = 0; c < kMaxClipCandidates; ++c) r.v[c] = c < count ? ratios[c] : 1.0f;
-  hipError_t err = launch_clip_error(w, r, count, N, K, group_size, zero_point, e, stream);
+  hipError_t err = launch_clip_group_params(w, r, count, N, K, group_size, zero_point, gp, stream);
   if (err != hipSuccess) return err;
-  err = launch_sumsq(static_cast<const _Float16*>(x), e, M, N, K, T, tiles_m, dim3(tiles_m * tiles_n, count), nullptr,
-                     log2_group(group_size), gpart, true, stream);
+  const dim3 grid((unsigned)((size_t)tiles * count)), block(kLossWaves * 64);
+  const _Float16* xh = static_cast<const _Float16*>(x);
+  const _Float16* wh = static_cast<const _Float16*>(w);
+  if (K % TK == 0)
+    hipLaunchKernelGGL((loss_fused_kernel<false, true>), grid, block, 0, stream, xh, wh, nullptr, gp, M, N, K,
+                       log2_group(group_size), tiles_m, tiles, nullptr, gpart);
+  else
+    hipLaunchKernelGGL((loss_fused_kernel<true, true>), grid, block, 0, stream, xh, wh, nullptr, gp, M, N, K,
+                       log2_group(group_size), tiles_m, tiles, nullptr, gpart);
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
   // without a caller's choice buffer the choices go to the start of the
-  // workspace: the weight errors there are dead once the product has run
+  // workspace: the group parameters there are dead once the product has run
   int32_t* ch = choice ? choice : reinterpret_cast<int32_t*>(ws);
-  return launch_clip_apply(w, gpart, tiles_m * 2, r, count, N, K, group_size, zero_point, w_out, ch, stream);
+  return launch_clip_apply(w, gpart, tiles_m * kLossWM, r, count, N, K, group_size, zero_point, w_out, ch, stream);
 }
 
 }  // namespace awq

@@ -279,10 +279,14 @@ int awq_scale_columns(const void* src, int32_t rows, int32_t K, const float* s, 
  * w_clipped  out  fp16 [N][K].
  * choice     out  int32 [N][K/group_size]: index of the chosen ratio (may be NULL).
  * workspace: device scratch of awq_clip_search_workspace_bytes(count, M, N,
- * K, group_size) bytes, 16-byte aligned; contents not needed before or after.
- * The errors are evaluated with fp16 weight errors and fp32 accumulation
- * (relative error ~1e-3); a ratio whose error is within that of the best may
- * be chosen instead.  Deterministic.
+ * K, group_size) bytes (count * N * K / group_size * 8 for every ratio's
+ * group scales, zero points and bounds, plus the per-group partial errors),
+ * 16-byte aligned; contents not needed before or after.
+ * Shapes: as awq_pack, and K * N < 2^33.
+ * The weight errors are formed next to the matrix cores (never stored) and
+ * rounded to fp16, the products accumulate in fp32 (relative error ~1e-3);
+ * a ratio whose error is within that of the best may be chosen instead.
+ * Deterministic.
  */
 int awq_clip_search(const void* x, const void* w, int32_t M, int32_t N, int32_t K, int32_t group_size,
                     int32_t zero_point, const float* ratios, int32_t count, void* w_clipped, int32_t* choice,

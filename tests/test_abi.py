@@ -237,8 +237,11 @@ def test_clip_and_scale_columns_validation(lib):
     assert clip(4, 8, 128, 32, 3, choice=D + 2) == awq.AWQ_ERR_ALIGN
     assert clip(4, 8, 128, 32, 3, w=B + 8) == awq.AWQ_ERR_ALIGN
     need = awq.load_library().awq_clip_search_workspace_bytes(3, 4, 8, 128, 32)
-    assert need >= 3 * 8 * 128 * 2
+    # every ratio's group parameters (8 bytes per row and group) and the
+    # per-group partial errors of the 4 token quarters of one tile
+    assert need >= 3 * (128 // 32) * 8 * 8 + 3 * 4 * (128 // 32) * 8 * 4
     assert clip(4, 8, 128, 32, 3, wsb=need - 1) == awq.AWQ_ERR_WORKSPACE
+    assert clip(4, 1 << 16, 1 << 17, 128, 3) == awq.AWQ_ERR_SHAPE  # K * N < 2^33
     cols = lambda rows, K, **kw: lib.awq_scale_columns(  # noqa: E731
         kw.get("src", A) or None, rows, K, kw.get("s", B) or None, 0, kw.get("dst", C) or None, None)
     assert cols(0, 64) == awq.AWQ_ERR_SHAPE
