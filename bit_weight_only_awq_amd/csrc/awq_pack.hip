@@ -146,6 +146,7 @@ __global__ __launch_bounds__(kPackThreads) void scale_group_params_kernel(const 
   const int n = blockIdx.x * 8 + r;
   const int kw = K >> 3;
   const int G = kw / (WPL * GW);
+  __shared__ float4_t lsc[GW * kPass * 2];  // GW candidates x 512 channels of scales
   const int pos = l % GW;  // the lane's place in its group
   const int j_begin = blockIdx.y * chunk_words;
   const int j_end = min(kw, j_begin + chunk_words);  // multiples of WPL: no lane's words straddle j_end
@@ -167,16 +168,24 @@ __global__ __launch_bounds__(kPackThreads) void scale_group_params_kernel(const 
     }
     const int grp = j / (WPL * GW);
     for (int c0 = 0; c0 < count; c0 += GW) {
+      // the set's scales of this pass's 512 channels, staged in LDS once per
+      // block: the 8 rows of the block read the same ones (per-lane global
+      // loads of them kept the address units busy ~80% of the time)
+      __syncthreads();
+      for (int q = t; q < GW * kPass * 2; q += kPackThreads) {
+        const int i = q / (kPass * 2), f = q % (kPass * 2);  // candidate of the set, float4 of the pass
+        const int c = min(c0 + i, count - 1);                 // a short last set repeats the last candidate
+        const int k = 8 * w0 + 4 * f;
+        lsc[q] = k < K ? *reinterpret_cast<const float4_t*>(s_all + (size_t)c * K + k) : float4_t{1.f, 1.f, 1.f, 1.f};
+      }
+      __syncthreads();
       int mn[GW], mx[GW];  // order-preserving images of the lane's extremes
 #pragma unroll
       for (int i = 0; i < GW; ++i) {
-        const int c = min(c0 + i, count - 1);  // a short last set repeats the last candidate
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(s_all + (size_t)c * K), 0, K * 4, 0x00020000);
         float sv[8 * WPL];
 #pragma unroll
         for (int q4 = 0; q4 < 2 * WPL; ++q4) {
-          const float4_t v = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)j * 32, 16 * q4, 0));
+          const float4_t v = lsc[i * kPass * 2 + 2 * WPL * l + q4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) sv[4 * q4 + q] = v[q];
         }
