@@ -497,9 +497,10 @@ def leg_prefill(torch, awq, workloads, g=128, zp=True, iters=30, warm=20, dense=
 def leg_scale_search(torch, awq, workloads, g=128, zp=True, M=512, count=20, iters=5):
     """Activation-aware scale search: L(s) for `count` candidate scale vectors
     s = a^alpha over M calibration tokens, on the Llama-7B q (4096x4096) and
-    gate (4096->11008) shapes.  Per candidate: one scale-quantize-error pass
-    over W (read 2 B, write 2 B per weight) and one dense M x N x K product
-    with a sum-of-squares epilogue."""
+    gate (4096->11008) shapes.  One pass over W gives every candidate's group
+    scales and zero points; then per candidate one M x N x K product whose
+    weight operand, the quantization error of W diag(s), is built in LDS next
+    to the matrix cores, with a sum-of-squares epilogue."""
     out = {}
     alphas = [i / count for i in range(count)]
     for li, name in ((0, "q_proj"), (4, "gate_proj")):
@@ -529,10 +530,11 @@ def leg_scale_search(torch, awq, workloads, g=128, zp=True, M=512, count=20, ite
 
 def leg_clip_search(torch, awq, workloads, g=128, zp=True, M=512, iters=5):
     """Weight-clipping search (20 ratios, 1.0 down to 0.525) over M calibration
-    tokens on the Llama-7B q (4096x4096) and gate (4096->11008) shapes: per
-    ratio one clip-quantize-error pass over W and one M x N x K product whose
-    squares are summed per weight group, then the choice and the clipped
-    weights."""
+    tokens on the Llama-7B q (4096x4096) and gate (4096->11008) shapes: one
+    pass over W gives every ratio's clipped bounds, scales and zero points;
+    per ratio one M x N x K product whose weight operand, the
+    clipped-quantization error, is built in LDS, with squares summed per
+    weight group; then the choice and the clipped weights."""
     out = {}
     ratios = list(awq.DEFAULT_CLIP_RATIOS)
     for li, name in ((0, "q_proj"), (4, "gate_proj")):
