@@ -23,6 +23,7 @@ namespace {
 
 constexpr int kPackThreads = 256;  // 8 rows x 32 lanes
 constexpr int kPackWords = 2;      // packed words (8 channels each) per lane and pass of pack_kernel
+constexpr int kParamRows = 2;      // rows per lane of scale_group_params_kernel
 // One block quantizes one octet of rows (n0 .. n0+7) over one slice of K
 // (blockIdx.y: packed words [chunk_words * y, + chunk_words), a multiple of a
 // 512-channel pass, so slices end on group boundaries; several slices per row
@@ -132,8 +133,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const u32x4* __restr
 // group's two.  Candidates go in sets of GW (the lanes of a group): a
 // transposed reduction leaves lane p of the group with the extremes of
 // candidate p of the set, and each lane computes one scale and zero point
-// (two divisions) per set instead of one per candidate.  Same block shape
-// and K slices as pack_kernel.
+// (two divisions) per set instead of one per candidate; the set's scale
+// vectors are staged in LDS, and each lane holds the same 16 channels of two
+// rows, so that every scale it reads serves two products.  Blocks of 16 rows
+// x 512-channel passes, K sliced as in pack_kernel.
 template <int GW, bool ZP>
 __global__ __launch_bounds__(kPackThreads) void scale_group_params_kernel(const u32x4* __restrict__ w,
                                                                           const float* __restrict__ s_all, int count,
@@ -141,9 +144,11 @@ __global__ __launch_bounds__(kPackThreads) void scale_group_params_kernel(const 
                                                                           uint32_t* __restrict__ gp) {
   constexpr int WPL = kPackWords;
   constexpr int kPass = 32 * WPL;
+  constexpr int RPL = kParamRows;  // rows per lane: each scale read from LDS serves RPL products
   const int t = threadIdx.x;
   const int r = t >> 5, l = t & 31;
-  const int n = blockIdx.x * 8 + r;
+  const int nb = blockIdx.x * 8 * RPL;  // the block's first row
+  const int n0 = nb + RPL * r;          // this lane's rows n0 .. n0 + RPL - 1
   const int kw = K >> 3;
   const int G = kw / (WPL * GW);
   __shared__ float4_t lsc[GW * kPass * 2];  // GW candidates x 512 channels of scales
@@ -152,24 +157,26 @@ __global__ __launch_bounds__(kPackThreads) void scale_group_params_kernel(const 
   const int j_end = min(kw, j_begin + chunk_words);  // multiples of WPL: no lane's words straddle j_end
   // Unconditional buffer loads: a lane past the slice end reads other
   // weights or zeros and writes nothing, and its whole group is past the end
-  // with it (no branch around each load).
-  const __amdgpu_buffer_rsrc_t rw =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<u32x4*>(w + (size_t)blockIdx.x * 8 * kw), 0, 8 * kw * 16, 0x00020000);
+  // with it (no branch around each load); rows past N read zeros.
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4*>(w + (size_t)nb * kw), 0, min(8 * RPL, N - nb) * kw * 16, 0x00020000);
   for (int w0 = j_begin; w0 < j_end; w0 += kPass) {
     const int j = w0 + WPL * l;
     const bool active = j < j_end;
-    float hv[8 * WPL];
+    float hv[RPL][8 * WPL];
 #pragma unroll
-    for (int i = 0; i < WPL; ++i) {
-      const half8_t h = __builtin_bit_cast(
-          half8_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t)(r * kw + j + i) * 16, 0, 0));
+    for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) hv[8 * i + c] = (float)h[c];
-    }
+      for (int i = 0; i < WPL; ++i) {
+        const half8_t h = __builtin_bit_cast(
+            half8_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (uint32_t)((RPL * r + rr) * kw + j + i) * 16, 0, 0));
+#pragma unroll
+        for (int c = 0; c < 8; ++c) hv[rr][8 * i + c] = (float)h[c];
+      }
     const int grp = j / (WPL * GW);
     for (int c0 = 0; c0 < count; c0 += GW) {
       // the set's scales of this pass's 512 channels, staged in LDS once per
-      // block: the 8 rows of the block read the same ones (per-lane global
+      // block: the rows of the block read the same ones (per-lane global
       // loads of them kept the address units busy ~80% of the time)
       __syncthreads();
       for (int q = t; q < GW * kPass * 2; q += kPackThreads) {
@@ -179,9 +186,14 @@ __global__ __launch_bounds__(kPackThreads) void scale_group_params_kernel(const 
         lsc[q] = k < K ? *reinterpret_cast<const float4_t*>(s_all + (size_t)c * K + k) : float4_t{1.f, 1.f, 1.f, 1.f};
       }
       __syncthreads();
-      int mn[GW], mx[GW];  // order-preserving images of the lane's extremes
+      int mn[RPL][GW], mx[RPL][GW];  // order-preserving images of the lane's extremes
 #pragma unroll
       for (int i = 0; i < GW; ++i) {
+        if (c0 + i >= count) {  // a short last set: nothing to compute (uniform branch)
+#pragma unroll
+          for (int rr = 0; rr < RPL; ++rr) mn[rr][i] = mx[rr][i] = 0;
+          continue;
+        }
         float sv[8 * WPL];
 #pragma unroll
         for (int q4 = 0; q4 < 2 * WPL; ++q4) {
@@ -189,32 +201,39 @@ __global__ __launch_bounds__(kPackThreads) void scale_group_params_kernel(const 
 #pragma unroll
           for (int q = 0; q < 4; ++q) sv[4 * q4 + q] = v[q];
         }
-        if constexpr (ZP) {
-          float lo = fp32_product(hv[0], sv[0]), hi = lo;
 #pragma unroll
-          for (int q = 1; q < 8 * WPL; ++q) {
-            const float v = fp32_product(hv[q], sv[q]);
-            lo = fminf(lo, v);
-            hi = fmaxf(hi, v);
+        for (int rr = 0; rr < RPL; ++rr) {
+          if constexpr (ZP) {
+            float lo = fp32_product(hv[rr][0], sv[0]), hi = lo;
+#pragma unroll
+            for (int q = 1; q < 8 * WPL; ++q) {
+              const float v = fp32_product(hv[rr][q], sv[q]);
+              lo = fminf(lo, v);
+              hi = fmaxf(hi, v);
+            }
+            mn[rr][i] = ord_of(lo);
+            mx[rr][i] = ord_of(hi);
+          } else {
+            float hi = fabsf(fp32_product(hv[rr][0], sv[0]));
+#pragma unroll
+            for (int q = 1; q < 8 * WPL; ++q) hi = fmaxf(hi, fabsf(fp32_product(hv[rr][q], sv[q])));
+            mx[rr][i] = ord_of(hi);
           }
-          mn[i] = ord_of(lo);
-          mx[i] = ord_of(hi);
-        } else {
-          float hi = fabsf(fp32_product(hv[0], sv[0]));
-#pragma unroll
-          for (int q = 1; q < 8 * WPL; ++q) hi = fmaxf(hi, fabsf(fp32_product(hv[q], sv[q])));
-          mx[i] = ord_of(hi);
         }
       }
-      if constexpr (ZP) group_transpose<GW>(mn, MinOp());
-      group_transpose<GW>(mx, MaxOp());
       const int c = c0 + pos;
-      float s, zf;
-      _Float16 s16;
-      scale_zero_of_extremes<ZP>(ZP ? (float)(_Float16)float_of(mn[0]) : 0.0f, (float)(_Float16)float_of(mx[0]), s16,
-                                 s, zf);
-      if (active && c < count)
-        gp[((size_t)c * G + grp) * N + n] = (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)zf << 16);
+#pragma unroll
+      for (int rr = 0; rr < RPL; ++rr) {
+        if constexpr (ZP) group_transpose<GW>(mn[rr], MinOp());
+        group_transpose<GW>(mx[rr], MaxOp());
+        float s, zf;
+        _Float16 s16;
+        scale_zero_of_extremes<ZP>(ZP ? (float)(_Float16)float_of(mn[rr][0]) : 0.0f,
+                                   (float)(_Float16)float_of(mx[rr][0]), s16, s, zf);
+        const int n = n0 + rr;
+        if (active && c < count && n < N)
+          gp[((size_t)c * G + grp) * N + n] = (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)zf << 16);
+      }
     }
   }
 }
@@ -427,13 +446,13 @@ template <bool ZP>
 hipError_t launch_scale_group_params_zp(const void* w, const float* s, int count, int N, int K, int group_size,
                                         void* gp, hipStream_t stream) {
   constexpr int kTargetBlocks = 4096, kRingWords = 32 * kPackWords;
-  const int kw = K >> 3, octets = N / 8;
+  const int kw = K >> 3, bands = (N + 8 * kParamRows - 1) / (8 * kParamRows);
   const int rings = (kw + kRingWords - 1) / kRingWords;
-  int slices = (kTargetBlocks + octets - 1) / octets;
+  int slices = (kTargetBlocks + bands - 1) / bands;
   if (slices > rings) slices = rings;
   if (slices < 1) slices = 1;
   const int chunk = ((rings + slices - 1) / slices) * kRingWords;
-  const dim3 grid(octets, (kw + chunk - 1) / chunk), block(kPackThreads);
+  const dim3 grid(bands, (kw + chunk - 1) / chunk), block(kPackThreads);
   const u32x4* wv = static_cast<const u32x4*>(w);
   uint32_t* g = static_cast<uint32_t*>(gp);
   switch (group_size) {

@@ -165,30 +165,29 @@ __device__ __forceinline__ float fp32_product(float a, float b) {
   return p;
 }
 
-// rne(a / s) for NE weights of one group, as floats, where a and s
-// are fp16 values (a weight and its group's scale), computed without a
-// division and without a branch.  x = a * rcp(s) lies within 2 ulp of the
-// quotient; one correction step r = fma(-x, s, a), x' = fma(r, rcp(s), x)
-// makes it exact when the quotient is a half-integer j + 1/2 (then q - x is a
-// multiple of x's ulp of at most a few units, (q - x) * s has at most 13
-// significant bits, so r = a - x s is exact and x' rounds to q) and leaves it
-// within an ulp otherwise.  A quotient of two fp16 values that is not a
-// half-integer lies at least ~2^-13 from one (numerator and denominator have
-// 11-bit significands), far more than x' can be off while |x| < 16, so
-// rint(x') = rne(a / s) there; beyond, every code saturates (q = clamp(k + z,
-// 0, 15) with 0 <= z <= 15) and an off-by-one in k changes nothing.
-// (Half-integer quotients are common: fp16 weights are coarse against a
-// 16-level grid, about 1 in 250 weights.)
+// 768 + rne(a / s) for NE weights of one group, as floats, where a and s
+// are fp16 values (a weight and its group's scale) and rs = rcp(s), computed
+// without a division and without a branch: k = rint(fma(a, rs, 768)).
+// The fused multiply-add rounds a * rs + 768 once, to fp32's grid of 2^-14 on
+// [512, 1024), which snaps the quotient q = a / s to that grid: rcp's error
+// leaves |a * rs - q| <= |q| 2^-23 < 2^-19 while |q| < 16, so an exact
+// half-integer quotient j + 1/2 (a point of the grid) is recovered exactly
+// and rint's ties-to-even then rounds it as rne(q) does (768 is even).  A
+// quotient of two fp16 values that is not a half-integer lies at least about
+// 2^-12 from one (with a = A 2^e, s = S 2^f and 11-bit A, S, the gap
+// |2a - (2j + 1) s| / 2s is at least min(1 / 2S, |q| / A)), far more than
+// the snapped value can move it (2^-15 + 2^-19), so rint rounds it to the
+// same integer as q.  Beyond |q| = 16 every code saturates (the caller clamps
+// k - 768 to [-z, 15 - z] with 0 <= z <= 15), and the sum stays on the right
+// side of the clamp.  (Half-integer quotients are common: fp16 weights are
+// coarse against a 16-level grid, about 1 in 250 weights.)
+constexpr float kCodeBias = 768.0f;
+
 template <int NE>
-__device__ __forceinline__ void rounded_quotients(const float (&a)[NE], float s, float (&k)[NE]) {
+__device__ __forceinline__ void biased_quotients(const float (&a)[NE], float rs, float (&k)[NE]) {
 #pragma clang fp contract(off)
-  const float rs = __builtin_amdgcn_rcpf(s);
 #pragma unroll
-  for (int c = 0; c < NE; ++c) {
-    const float x = a[c] * rs;
-    const float r = __builtin_fmaf(-x, s, a[c]);
-    k[c] = rintf(__builtin_fmaf(r, rs, x));
-  }
+  for (int c = 0; c < NE; ++c) k[c] = rintf(__builtin_fmaf(a[c], rs, kCodeBias));
 }
 
 // Codes of a lane's 8 weights of one group, clamp(rne(a / s) + z, 0, 15) as
@@ -196,9 +195,10 @@ __device__ __forceinline__ void rounded_quotients(const float (&a)[NE], float s,
 __device__ __forceinline__ void codes_of(const float (&a)[8], float s, float zf, float (&q)[8]) {
 #pragma clang fp contract(off)
   float k[8];
-  rounded_quotients(a, s, k);
+  biased_quotients(a, __builtin_amdgcn_rcpf(s), k);
+  const float shift = zf - kCodeBias;  // exact: small integers
 #pragma unroll
-  for (int c = 0; c < 8; ++c) q[c] = fminf(fmaxf(k[c] + zf, 0.0f), 15.0f);
+  for (int c = 0; c < 8; ++c) q[c] = fminf(fmaxf(k[c] + shift, 0.0f), 15.0f);
 }
 
 // The packed word of 8 codes (small integers held as floats): two codes per

@@ -173,26 +173,60 @@ __global__ __launch_bounds__(256) void scaled_activations_kernel(const u32x4* __
   }
 }
 
+// fp16(fma(-h_lo, b0, c0)) | fp16(fma(-h_hi, b1, c1)) << 16 for the two fp16
+// halves of h2: each a single rounding of the exact fused multiply-add,
+// written straight into its half of the result (v_fma_mixlo/hi_f16 take the
+// fp16 operand as it is packed).
+__device__ __forceinline__ uint32_t neg_fma_pair(uint32_t h2, float b0, float c0, float b1, float c1) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, -%1, %2, %3 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, -%1, %4, %5 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(r)
+      : "v"(h2), "v"(b0), "v"(c0), "v"(b1), "v"(c1));
+  return r;
+}
+
+// fp16(c0 - h_lo) | fp16(c1 - h_hi) << 16, single roundings, as above.
+__device__ __forceinline__ uint32_t neg_add_pair(uint32_t h2, float c0, float c1) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, -%1, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(r)
+      : "v"(h2), "v"(c0), "v"(c1));
+  return r;
+}
+
 // Scaled errors of one row's 8 channels of one group for one candidate:
 //   e = fp16( (q - z) * s_g - w * s_c ),  q = clamp(rne(a / s_g) + z, 0, 15),  a = fp16(w * s_c)
-// (the difference formed by one fused multiply-add from the exact (q - z) s_g),
 // with the group's fp16 scale s_g and zero point z from p = s_g bits |
-// z << 16, and q by pack_kernel's rule (a is the
-// fp32 product rounded to fp16, as the quantizer sees it).  med3(k, -z,
-// 15 - z) is q - z exactly (small integers).
-__device__ __forceinline__ half8_t scaled_error8(u32x4 raw, uint32_t p, float4_t s0, float4_t s1) {
+// z << 16, and q by pack_kernel's rule (a is the fp32 product rounded to
+// fp16, as the quantizer sees it).  With k = 768 + rne(a / s_g) from
+// biased_quotients, med3(k, 768 - z, 783 - z) - 768 is q - z, and
+// fma(med3(..), s_g, -768 s_g) is (q - z) s_g exactly (small integers times
+// an fp16 value); the error is then one fused multiply-add rounded once to
+// fp16.  The product w * s_c is taken as fma(w, s_c, +0) so that the fp16
+// weight enters it without a conversion (the +0 changes only the sign of a
+// zero product, and the code of a zero is the zero point either way).
+__device__ __forceinline__ u32x4 scaled_error8(u32x4 raw, uint32_t p, float4_t s0, float4_t s1) {
+#pragma clang fp contract(off)
   const half8_t h = as_half8(raw);
   const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
   const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFFu));
   const float zf = (float)(p >> 16);
-  float a[8], k[8];
+  const float lob = kCodeBias - zf, hib = kCodeBias + 15.0f - zf, off = -kCodeBias * s;
+  float a[8], k[8], d[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) a[c] = (float)(_Float16)fp32_product((float)h[c], sv[c]);
-  rounded_quotients(a, s, k);
-  half8_t e;
+  for (int c = 0; c < 8; ++c) {
+    float prod = __builtin_fmaf((float)h[c], sv[c], 0.0f);
+    asm("" : "+v"(prod));  // keep the fp32 rounding of the product (see fp32_product)
+    a[c] = (float)(_Float16)prod;
+  }
+  biased_quotients(a, __builtin_amdgcn_rcpf(s), k);
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    e[c] = (_Float16)__builtin_fmaf(-(float)h[c], sv[c], __builtin_amdgcn_fmed3f(k[c], -zf, 15.0f - zf) * s);
+  for (int c = 0; c < 8; ++c) d[c] = __builtin_fmaf(__builtin_amdgcn_fmed3f(k[c], lob, hib), s, off);
+  u32x4 e;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) e[i] = neg_fma_pair(raw[i], sv[2 * i], d[2 * i], sv[2 * i + 1], d[2 * i + 1]);
   return e;
 }
 
@@ -202,22 +236,49 @@ __device__ __forceinline__ half8_t scaled_error8(u32x4 raw, uint32_t p, float4_t
 // group's clipped scale, zero point and fp32 bounds rounded to fp16.  For an
 // fp16 weight, clamping to the rounded bounds gives the fp16 rounding of the
 // clamp to the fp32 bounds (no fp16 value lies strictly between a bound and
-// its nearest fp16 value), which is what the quantizer sees.
-__device__ __forceinline__ half8_t clipped_error8(u32x4 raw, u32x2 p) {
+// its nearest fp16 value), which is what the quantizer sees.  Codes and
+// (q - z) s_g as in scaled_error8.
+__device__ __forceinline__ u32x4 clipped_error8(u32x4 raw, u32x2 p) {
+#pragma clang fp contract(off)
   const half8_t h = as_half8(raw);
   const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[0] & 0xFFFFu));
   const float zf = (float)(p[0] >> 16);
   const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[1] & 0xFFFFu));
   const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(p[1] >> 16));
-  float a[8], k[8];
+  const float lob = kCodeBias - zf, hib = kCodeBias + 15.0f - zf, off = -kCodeBias * s;
+  float a[8], k[8], d[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) a[c] = __builtin_amdgcn_fmed3f((float)h[c], lo, hi);
-  rounded_quotients(a, s, k);
-  half8_t e;
+  biased_quotients(a, __builtin_amdgcn_rcpf(s), k);
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    e[c] = (_Float16)__builtin_fmaf(__builtin_amdgcn_fmed3f(k[c], -zf, 15.0f - zf), s, -(float)h[c]);
+  for (int c = 0; c < 8; ++c) d[c] = __builtin_fmaf(__builtin_amdgcn_fmed3f(k[c], lob, hib), s, off);
+  u32x4 e;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) e[i] = neg_add_pair(raw[i], d[2 * i], d[2 * i + 1]);
   return e;
+}
+
+// Scheduling pattern of one step of the loss product: per 16-channel slice
+// the slice's fragment reads, then its 8 products each followed by 4 of the
+// error build's VALU instructions (the matrix cores take 32 cycles per
+// 32x32x16 product, in whose shadow a few independent VALU instructions
+// issue for free), then the rest of the build and its LDS writes.
+template <int N>
+__device__ __forceinline__ void products_with_valu() {
+  if constexpr (N > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+    products_with_valu<N - 1>();
+  }
+}
+
+template <int SLICES>
+__device__ __forceinline__ void interleave_step() {
+  if constexpr (SLICES > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // the slice's fragment reads
+    products_with_valu<8>();
+    interleave_step<SLICES - 1>();
+  }
 }
 
 // The loss products of the two searches, with the weight error built in
@@ -352,21 +413,40 @@ __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Floa
     }
   };
   const int es0 = er0 * 128 + 16 * swz_chunk(er0, ec), es1 = er1 * 128 + 16 * swz_chunk(er1, ec);
+  // Rows past N and channels past K must hold zeros.  A row past N loads
+  // zero weights (past its resource's range) but another row's group
+  // parameters; given the parameters { scale 1, zero point 0, clip bounds 0 }
+  // instead, its error is exactly zero (code 0, (q - z) s = 0, e = -0 * s_c + 0).
+  // Channels past K (the K-tail variant) read the next row's weights and are
+  // zeroed at the store.
   auto build = [&](int step, const Rows& f, const Scales& c, int buf) {
-    const bool kin = !KTAIL || step * TK + 8 * ec < K;
-    // rows past N and channels past K hold zeros (their parameters are zero
-    // and would give NaN)
-    half8_t e0, e1;
+    u32x4 e0, e1;
+    param_t p0 = f.p0, p1 = f.p1;
+    if constexpr (!KTAIL) {
+      if constexpr (CLIP) {
+        p0 = ok0 ? p0 : u32x2{0x3C00u, 0u};
+        p1 = ok1 ? p1 : u32x2{0x3C00u, 0u};
+      } else {
+        p0 = ok0 ? p0 : 0x3C00u;
+        p1 = ok1 ? p1 : 0x3C00u;
+      }
+    }
     if constexpr (CLIP) {
-      e0 = clipped_error8(f.w0, f.p0);
-      e1 = clipped_error8(f.w1, f.p1);
+      e0 = clipped_error8(f.w0, p0);
+      e1 = clipped_error8(f.w1, p1);
     } else {
-      e0 = scaled_error8(f.w0, f.p0, c.s0, c.s1);
-      e1 = scaled_error8(f.w1, f.p1, c.s0, c.s1);
+      e0 = scaled_error8(f.w0, p0, c.s0, c.s1);
+      e1 = scaled_error8(f.w1, p1, c.s0, c.s1);
     }
     char* de = buf ? le1 : le0;
-    *reinterpret_cast<u32x4*>(de + es0) = kin && ok0 ? __builtin_bit_cast(u32x4, e0) : u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(de + es1) = kin && ok1 ? __builtin_bit_cast(u32x4, e1) : u32x4{0u, 0u, 0u, 0u};
+    if constexpr (KTAIL) {
+      // (with the original parameters, a row past N may give NaN: masked here too)
+      const bool kin = step * TK + 8 * ec < K;
+      e0 = kin && ok0 ? e0 : u32x4{0u, 0u, 0u, 0u};
+      e1 = kin && ok1 ? e1 : u32x4{0u, 0u, 0u, 0u};
+    }
+    *reinterpret_cast<u32x4*>(de + es0) = e0;
+    *reinterpret_cast<u32x4*>(de + es1) = e1;
   };
 
   float16_t acc[AM][AN];
@@ -422,36 +502,53 @@ __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Floa
     }
   };
 
-  // Two steps per trip (constant buffer indices).  A step's activation loads
-  // and the weights two steps ahead are issued first; the error tile of the
-  // next step is built while the matrix cores work on this one.
+  // Two steps per trip (constant buffer indices).  A step's activation loads,
+  // then the candidate scales and the weights two steps ahead, are issued
+  // first; the error tile of the next step is then built while the matrix
+  // cores work on this one (products first in program order, so that the
+  // build's arithmetic fills the matrix cores' shadow).  The barrier at the
+  // end of a step waits for the activation loads only: the register loads
+  // issued after them stay in flight for a whole step.
   Rows cur, nxt;
-  Scales sc;
-  fetch_scales(0, sc);
+  Scales sc, scn;
   fetch(0, cur);
+  fetch_scales(0, sc);
   load_x(0, 0);
   fetch(1, nxt);
+  fetch_scales(1, scn);
   build(0, cur, sc, 0);
   __syncthreads();
   int step = 0;
   for (; step + 1 < nsteps; step += 2) {
     cur = nxt;
-    fetch_scales(step + 1, sc);
+    sc = scn;
     load_x(step + 1, 1);
+    fetch_scales(step + 2, scn);
     fetch(step + 2, nxt);
     __builtin_amdgcn_sched_barrier(0);
-    build(step + 1, cur, sc, 1);
     compute(0, step);
+    build(step + 1, cur, sc, 1);
+    if constexpr (!CLIP) {
+      interleave_step<TK / 16>();
+      __builtin_amdgcn_sched_group_barrier(0x002, 256, 0);  // the rest of the build
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);    // its LDS writes
+    }
     __syncthreads();
     cur = nxt;
-    fetch_scales(step + 2, sc);
+    sc = scn;
     load_x(step + 2, 0);
+    fetch_scales(step + 3, scn);
     fetch(step + 3, nxt);
     __builtin_amdgcn_sched_barrier(0);
+    compute(1, step + 1);
     // (past the last step this builds a tile that is never read: no branch
     // here, so the waits for the loads above stay exact)
     build(step + 2, cur, sc, 0);
-    compute(1, step + 1);
+    if constexpr (!CLIP) {
+      interleave_step<TK / 16>();
+      __builtin_amdgcn_sched_group_barrier(0x002, 256, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+    }
     __syncthreads();
   }
   if (step < nsteps) compute(0, step);

@@ -36,6 +36,46 @@ def check_choices(gpu_choice, gpu_wc, W, X, g, zp, ratios):
 
 
 @pytest.mark.parametrize("zp", [True, False])
+@pytest.mark.parametrize("N,K,g", [(264, 1024, 32), (40, 4096, 128), (8, 512, 256)])
+def test_clip_group_params_bit_exact(N, K, g, zp):
+    """Every ratio's group parameters as the loss product uses them, read from
+    the first region of the caller's workspace ([count][K/g][N] pairs of words
+    {fp16 scale bits | zero point << 16, fp16(lo) bits | fp16(hi) bits << 16}):
+    the scale and zero point are the oracle's group_params of clip_weight(W,
+    r) bit for bit, and clamping each fp16 weight of the group to [lo, hi]
+    reproduces clip_weight(W, r) bit for bit."""
+    awq = G.lib()
+    lib = awq.load_library()
+    M = 16
+    W = workloads.weight(N, K, cfg=7, layer=N + g, row_offset=True)
+    X = workloads.activations(M, K, cfg=7, layer=N + g)
+    ratios = [1.0, 0.9, 0.725, 0.525]
+    count, Gn = len(ratios), K // g
+    x, w = G.dev_f16(X), G.dev_f16(W)
+    out = torch.empty_like(w)
+    # (a caller's choice buffer: without one the choices overwrite the start of the workspace)
+    choice = torch.empty((N, Gn), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(int(lib.awq_clip_search_workspace_bytes(count, M, N, K, g)), dtype=torch.uint8, device="cuda")
+    import ctypes
+    arr = (ctypes.c_float * count)(*ratios)
+    st = lib.awq_clip_search(awq._ptr(x), awq._ptr(w), M, N, K, g, int(zp), ctypes.cast(arr, ctypes.c_void_p), count,
+                             awq._ptr(out), awq._ptr(choice), awq._ptr(ws), ws.numel(), awq._stream(x))
+    assert st == 0, awq.awq_strerror(st)
+    torch.cuda.synchronize()
+    gp = ws[: count * Gn * N * 8].cpu().numpy().view(np.uint32).reshape(count, Gn, N, 2)
+    for c, r in enumerate(ratios):
+        Wc = O.clip_weight(W, g, zp, r)
+        s16, z = O.group_params(Wc, g, zp)
+        want = s16.view(np.uint16).astype(np.uint32) | (z.astype(np.uint32) << 16)
+        assert np.array_equal(gp[c, :, :, 0].T, want), (r, int(np.count_nonzero(gp[c, :, :, 0].T != want)))
+        lo = (gp[c, :, :, 1].T & 0xFFFF).astype(np.uint16).view(np.float16)
+        hi = (gp[c, :, :, 1].T >> 16).astype(np.uint16).view(np.float16)
+        a = W.reshape(N, Gn, g)
+        clamped = np.minimum(np.maximum(a, lo[:, :, None]), hi[:, :, None]).reshape(N, K)
+        assert np.array_equal(clamped.view(np.uint16), Wc.view(np.uint16)), r
+
+
+@pytest.mark.parametrize("zp", [True, False])
 @pytest.mark.parametrize("M,N,K,g", [(64, 256, 512, 64), (37, 264, 2080, 32), (130, 520, 1024, 128),
                                      (300, 256, 2048, 256), (1, 8, 128, 128)])
 def test_clip_search_matches_oracle(M, N, K, g, zp):

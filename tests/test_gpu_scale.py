@@ -117,6 +117,37 @@ def test_search_scale_end_to_end(zp, duo):
 
 
 @pytest.mark.parametrize("zp", [True, False])
+@pytest.mark.parametrize("N,K,g", [(264, 1024, 32), (264, 4096, 128), (40, 11008, 64), (8, 512, 256)])
+def test_scale_loss_group_params_bit_exact(N, K, g, zp):
+    """The group scales and zero points the loss product quantizes with, read
+    from the first region of the caller's workspace ([count][K/g][N] words of
+    fp16 scale bits | zero point << 16), against the oracle's group_params of
+    scale_weights(W, s_c) for every candidate, bit for bit.  N = 264 and 40 end
+    in a partial band of rows, K = 4096 and 11008 span several K slices."""
+    awq = G.lib()
+    lib = awq.load_library()
+    M = 24
+    W = workloads.weight(N, K, cfg=6, layer=N + g, row_offset=True)
+    X = workloads.activations(M, K, cfg=6, layer=N + g)
+    S = np.stack([np.ones(K, np.float32)] + list(O.scale_candidates(X, [0.25, 0.5, 0.75])) +
+                 list(O.scale_candidates(X, [0.4], W)))
+    count = len(S)
+    x, w, s = G.dev_f16(X), G.dev_f16(W), torch.from_numpy(np.ascontiguousarray(S)).cuda()
+    ws = torch.zeros(int(lib.awq_scale_loss_workspace_bytes(count, M, N, K)), dtype=torch.uint8, device="cuda")
+    loss = torch.empty(count, dtype=torch.float64, device="cuda")
+    st = lib.awq_scale_loss(awq._ptr(x), awq._ptr(w), awq._ptr(s), count, M, N, K, g, int(zp), awq._ptr(ws),
+                            ws.numel(), awq._ptr(loss), awq._stream(x))
+    assert st == 0, awq.awq_strerror(st)
+    torch.cuda.synchronize()
+    G_ = K // g
+    gp = ws[: count * G_ * N * 4].cpu().numpy().view(np.uint32).reshape(count, G_, N)
+    for c in range(count):
+        s16, z = O.group_params(O.scale_weights(W, S[c]), g, zp)
+        want = s16.view(np.uint16).astype(np.uint32) | (z.astype(np.uint32) << 16)
+        assert np.array_equal(gp[c].T, want), (c, int(np.count_nonzero(gp[c].T != want)))
+
+
+@pytest.mark.parametrize("zp", [True, False])
 @pytest.mark.parametrize("g", [32, 128])
 def test_scaled_weight_codes_bit_exact(g, zp):
     """The quantizer on scaled weights: awq_scale_columns (fp16 of the fp32
