@@ -312,7 +312,7 @@ __device__ __forceinline__ void interleave_step() {
 // restarts its accumulators from zero.
 constexpr int kLossM = 512, kLossN = 128, kLossWaves = 8, kLossWM = 4;
 
-template <bool KTAIL, bool CLIP>
+template <bool KTAIL, bool CLIP, bool MIDFLUSH = false>
 __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Float16* __restrict__ XS,
                                                                    const _Float16* __restrict__ W,
                                                                    const float* __restrict__ s_all,
@@ -495,12 +495,22 @@ __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Floa
 #pragma unroll
         for (int b = 0; b < AN; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[a], bf[b], acc[a][b], 0, 0, 0);
-      if constexpr (CLIP) {
+      if constexpr (CLIP && MIDFLUSH) {
         const int kend = step * TK + (ks + 1) * 16;  // channels done after this slice
         if ((kend & ((1 << gshift) - 1)) == 0 && kend <= K) flush((kend >> gshift) - 1);
       }
     }
   };
+  // groups of 64 channels or more end at step boundaries (K is then a
+  // multiple of 64): their flush follows the step's products, outside the
+  // scheduled region
+  auto step_flush = [&](int step) {
+    if constexpr (CLIP && !MIDFLUSH) {
+      const int kend = (step + 1) * TK;
+      if ((kend & ((1 << gshift) - 1)) == 0) flush((kend >> gshift) - 1);
+    }
+  };
+  constexpr bool kInterleave = !(CLIP && MIDFLUSH);
 
   // Two steps per trip (constant buffer indices).  A step's activation loads,
   // then the candidate scales and the weights two steps ahead, are issued
@@ -528,11 +538,12 @@ __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Floa
     __builtin_amdgcn_sched_barrier(0);
     compute(0, step);
     build(step + 1, cur, sc, 1);
-    if constexpr (!CLIP) {
+    if constexpr (kInterleave) {
       interleave_step<TK / 16>();
       __builtin_amdgcn_sched_group_barrier(0x002, 256, 0);  // the rest of the build
       __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);    // its LDS writes
     }
+    step_flush(step);
     __syncthreads();
     cur = nxt;
     sc = scn;
@@ -544,14 +555,18 @@ __global__ __launch_bounds__(kLossWaves * 64) void loss_fused_kernel(const _Floa
     // (past the last step this builds a tile that is never read: no branch
     // here, so the waits for the loads above stay exact)
     build(step + 2, cur, sc, 0);
-    if constexpr (!CLIP) {
+    if constexpr (kInterleave) {
       interleave_step<TK / 16>();
       __builtin_amdgcn_sched_group_barrier(0x002, 256, 0);
       __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
     }
+    step_flush(step + 1);
     __syncthreads();
   }
-  if (step < nsteps) compute(0, step);
+  if (step < nsteps) {
+    compute(0, step);
+    step_flush(step);
+  }
   if constexpr (CLIP) return;
 
   float ss = 0.0f;
@@ -717,11 +732,15 @@ hipError_t launch_clip_search(const void* x, const void* w, int M, int N, int K,
   const dim3 grid((unsigned)((size_t)tiles * count)), block(kLossWaves * 64);
   const _Float16* xh = static_cast<const _Float16*>(x);
   const _Float16* wh = static_cast<const _Float16*>(w);
-  if (K % TK == 0)
-    hipLaunchKernelGGL((loss_fused_kernel<false, true>), grid, block, 0, stream, xh, wh, nullptr, gp, M, N, K,
+  // groups of 32 channels flush twice per step (K % 64 != 0 implies them)
+  if (K % TK != 0)
+    hipLaunchKernelGGL((loss_fused_kernel<true, true, true>), grid, block, 0, stream, xh, wh, nullptr, gp, M, N, K,
+                       log2_group(group_size), tiles_m, tiles, nullptr, gpart);
+  else if (group_size == 32)
+    hipLaunchKernelGGL((loss_fused_kernel<false, true, true>), grid, block, 0, stream, xh, wh, nullptr, gp, M, N, K,
                        log2_group(group_size), tiles_m, tiles, nullptr, gpart);
   else
-    hipLaunchKernelGGL((loss_fused_kernel<true, true>), grid, block, 0, stream, xh, wh, nullptr, gp, M, N, K,
+    hipLaunchKernelGGL((loss_fused_kernel<false, true, false>), grid, block, 0, stream, xh, wh, nullptr, gp, M, N, K,
                        log2_group(group_size), tiles_m, tiles, nullptr, gpart);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
