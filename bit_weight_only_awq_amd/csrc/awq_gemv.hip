@@ -39,8 +39,10 @@ __global__ __launch_bounds__(NW * QPW * 64) void gemv_kernel(const u32x4* __rest
   static_assert(ROWS == 4 || ROWS == 8, "row quads or octets");
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   __shared__ float red[QPW][NW][ROWS];
-  const int lane = threadIdx.x & 63, wave_all = threadIdx.x >> 6;
-  const int part = wave_all / NW, wave = wave_all - part * NW;  // row group of the wave, wave within it
+  // (the wave index is uniform: readfirstlane keeps it, the row group and
+  // the row addresses derived from it in scalar registers)
+  const int lane = threadIdx.x & 63, wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part = QPW == 1 ? 0 : wave_all / NW, wave = wave_all - part * NW;  // row group of the wave, wave within it
   const int t = wave * 64 + lane;                               // thread within the row group
   const int n0 = (blockIdx.x * QPW + part) * ROWS;
   const int chunks = K >> 5;                // 32-channel chunks per row
