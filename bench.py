@@ -494,7 +494,7 @@ def leg_prefill(torch, awq, workloads, g=128, zp=True, iters=30, warm=20, dense=
     return out
 
 
-def leg_scale_search(torch, awq, workloads, g=128, zp=True, M=512, count=20, iters=5):
+def leg_scale_search(torch, awq, workloads, g=128, zp=True, M=512, count=20, iters=20):
     """Activation-aware scale search: L(s) for `count` candidate scale vectors
     s = a^alpha over M calibration tokens, on the Llama-7B q (4096x4096) and
     gate (4096->11008) shapes.  One pass over W gives every candidate's group
@@ -508,10 +508,16 @@ def leg_scale_search(torch, awq, workloads, g=128, zp=True, M=512, count=20, ite
         W = torch.from_numpy(workloads.weight(N, K, cfg=6, layer=li)).cuda()
         X = torch.from_numpy(workloads.activations(M, K, cfg=6, layer=li)).cuda()
         S = awq.awq_scale_candidates(X, alphas)
-        for _ in range(2):
+        for _ in range(3):
             L = awq.awq_scale_loss(X, W, S, g, zp)
         torch.cuda.synchronize()
+        # one call after a synchronize, then the mean of back-to-back calls
+        # (the steady state of a quantization run, which searches layer after
+        # layer)
         tm = Timer(torch)
+        tm.start()
+        L = awq.awq_scale_loss(X, W, S, g, zp)
+        first = tm.stop_ms()
         tm.start()
         for _ in range(iters):
             L = awq.awq_scale_loss(X, W, S, g, zp)
@@ -520,6 +526,7 @@ def leg_scale_search(torch, awq, workloads, g=128, zp=True, M=512, count=20, ite
         best = min(range(count), key=lambda i: (losses[i], i))
         flops = 2.0 * M * N * K * count
         out[name] = {"M": M, "K": K, "N": N, "candidates": count, "us": round(ms * 1e3, 1),
+                     "calls": iters, "us_first_call": round(first * 1e3, 1),
                      "us_per_candidate": round(ms * 1e3 / count, 2),
                      "TFLOPS_product": round(flops / (ms * 1e-3) / 1e12, 1),
                      "best_alpha": alphas[best], "L_rtn": round(losses[0], 4), "L_best": round(losses[best], 4)}
@@ -528,7 +535,7 @@ def leg_scale_search(torch, awq, workloads, g=128, zp=True, M=512, count=20, ite
     return out
 
 
-def leg_clip_search(torch, awq, workloads, g=128, zp=True, M=512, iters=5):
+def leg_clip_search(torch, awq, workloads, g=128, zp=True, M=512, iters=20):
     """Weight-clipping search (20 ratios, 1.0 down to 0.525) over M calibration
     tokens on the Llama-7B q (4096x4096) and gate (4096->11008) shapes: one
     pass over W gives every ratio's clipped bounds, scales and zero points;
@@ -541,10 +548,13 @@ def leg_clip_search(torch, awq, workloads, g=128, zp=True, M=512, iters=5):
         _, K, N = workloads.LLAMA7B_BLOCK[li]
         W = torch.from_numpy(workloads.weight(N, K, cfg=7, layer=li)).cuda()
         X = torch.from_numpy(workloads.activations(M, K, cfg=7, layer=li)).cuda()
-        for _ in range(2):
+        for _ in range(3):
             wc, choice = awq.awq_clip_search(X, W, g, zp, ratios)
         torch.cuda.synchronize()
         tm = Timer(torch)
+        tm.start()
+        wc, choice = awq.awq_clip_search(X, W, g, zp, ratios)
+        first = tm.stop_ms()
         tm.start()
         for _ in range(iters):
             wc, choice = awq.awq_clip_search(X, W, g, zp, ratios)
@@ -552,6 +562,7 @@ def leg_clip_search(torch, awq, workloads, g=128, zp=True, M=512, iters=5):
         hist = torch.bincount(choice.flatten().long(), minlength=len(ratios)).cpu().tolist()
         flops = 2.0 * M * N * K * len(ratios)
         out[name] = {"M": M, "K": K, "N": N, "ratios": len(ratios), "us": round(ms * 1e3, 1),
+                     "calls": iters, "us_first_call": round(first * 1e3, 1),
                      "us_per_ratio": round(ms * 1e3 / len(ratios), 2),
                      "TFLOPS_product": round(flops / (ms * 1e-3) / 1e12, 1),
                      "groups_clipped": round(1.0 - hist[0] / sum(hist), 4)}
