@@ -240,7 +240,8 @@ size_t awq_scale_search_workspace_bytes(int32_t count, int32_t M, int32_t N, int
  * is formed next to the matrix cores (never stored) in fp32 from the exact
  * code times scale, rounded once to fp16 (relative 2^-11), the scaled
  * activations are rounded to fp16 (relative 2^-11), the product accumulates
- * in fp32 and the sum of squares in fp64: |loss - L| <= 1e-3 * L.  The codes
+ * in fp32, its squares are summed in fp32 per wave (128 x 64 outputs) and the
+ * waves' sums in fp64: |loss - L| <= 1e-3 * L.  The codes
  * are awq_pack's codes of fp16(W s) bit for bit.  Deterministic.
  */
 int awq_scale_loss(const void* x, const void* w, const float* s, int32_t count, int32_t M, int32_t N, int32_t K,
