@@ -325,25 +325,36 @@ __global__ __launch_bounds__(kPackThreads) void clip_group_params_kernel(const u
 
 // The clipping ratio of each weight group (n, j): the error of the group under
 // ratio c is the sum, in a fixed order (fp64), of the per-tile partials
-// part[c][tm][h][j][n] (tile rows tm, half h of a tile's rows), and the group
-// keeps the first ratio with the smallest error.  One thread per group,
-// consecutive threads on consecutive rows n, so the partial reads coalesce.
-__global__ __launch_bounds__(256) void clip_choose_kernel(const float* __restrict__ part, int parts, int G, int N,
+// part[c][tm][q][j][n] (tile rows tm, quarter q of a tile's rows), and the
+// group keeps the first ratio with the smallest error.  One thread per four
+// groups of consecutive rows n (N is a multiple of 8), so each partial read is
+// one 16-byte load and the reads of a wave coalesce; the parts of a ratio are
+// loaded together (the loop is unrolled) before their sum.
+__global__ __launch_bounds__(256) void clip_choose_kernel(const float4_t* __restrict__ part, int parts, int G, int N,
                                                           int count, int32_t* __restrict__ choice) {
+  const int N4 = N >> 2;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)G * N) return;
-  const int grp = (int)(idx / N), n = (int)(idx - (size_t)grp * N);
-  double best_v = __builtin_huge_val();
-  int best = 0;
+  if (idx >= (size_t)G * N4) return;
+  const int grp = (int)(idx / N4), n4 = (int)(idx - (size_t)grp * N4);
+  double best_v[4] = {__builtin_huge_val(), __builtin_huge_val(), __builtin_huge_val(), __builtin_huge_val()};
+  int best[4] = {0, 0, 0, 0};
   for (int c = 0; c < count; ++c) {
-    double v = 0.0;
-    for (int p = 0; p < parts; ++p) v += (double)part[(((size_t)c * parts + p) * G + grp) * N + n];
-    if (v < best_v) {
-      best_v = v;
-      best = c;
+    double v[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int p = 0; p < parts; ++p) {
+      const float4_t x = part[(((size_t)c * parts + p) * G + grp) * N4 + n4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += (double)x[i];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (v[i] < best_v[i]) {
+        best_v[i] = v[i];
+        best[i] = c;
+      }
   }
-  choice[(size_t)n * G + grp] = best;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) choice[(size_t)(4 * n4 + i) * G + grp] = best[i];
 }
 
 // Writes the clipped weights: every group clamped to its range shrunk by its
@@ -511,8 +522,8 @@ hipError_t launch_clip_apply(const void* w, const float* part, int parts, const 
                              int K, int group_size, bool zero_point, void* w_out, int32_t* choice, hipStream_t stream) {
   const int G = K / group_size;
   const size_t groups = (size_t)G * N;
-  hipLaunchKernelGGL(clip_choose_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream, part, parts, G,
-                     N, count, choice);
+  hipLaunchKernelGGL(clip_choose_kernel, dim3((unsigned)((groups / 4 + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const float4_t*>(part), parts, G, N, count, choice);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return zero_point ? launch_clip_zp<true>(w, ratios, count, N, K, group_size, nullptr, choice, w_out, true, stream)
