@@ -77,8 +77,11 @@ def test_clip_group_params_bit_exact(N, K, g, zp):
 
 @pytest.mark.parametrize("zp", [True, False])
 @pytest.mark.parametrize("M,N,K,g", [(64, 256, 512, 64), (37, 264, 2080, 32), (130, 520, 1024, 128),
-                                     (300, 256, 2048, 256), (1, 8, 128, 128)])
+                                     (300, 256, 2048, 256), (1, 8, 128, 128), (700, 264, 1024, 128),
+                                     (1030, 136, 544, 32)])
 def test_clip_search_matches_oracle(M, N, K, g, zp):
+    """(700 and 1030 tokens: two and three 512-token tiles, the last ragged;
+    their per-group partial errors are added by the choice kernel.)"""
     awq = G.lib()
     W = workloads.weight(N, K, cfg=7, layer=N, row_offset=True)
     X = workloads.activations(M, K, cfg=7, layer=N)

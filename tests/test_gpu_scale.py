@@ -43,8 +43,10 @@ def test_scale_candidates_match_oracle(M, K, duo):
 
 @pytest.mark.parametrize("zp", [True, False])
 @pytest.mark.parametrize("M,N,K,g", [(64, 256, 512, 64), (37, 264, 2080, 32), (1, 8, 256, 256),
-                                     (130, 1032, 1024, 128), (256, 512, 4096, 128)])
+                                     (130, 1032, 1024, 128), (256, 512, 4096, 128),
+                                     (600, 256, 512, 64), (1100, 136, 1056, 32)])
 def test_scale_loss_matches_oracle(M, N, K, g, zp):
+    """(600 and 1100 tokens: two and three 512-token tiles, the last ragged.)"""
     W = workloads.weight(N, K, cfg=6, layer=N, row_offset=True)
     X = workloads.activations(M, K, cfg=6, layer=N)
     rng = np.random.default_rng(N + K)
