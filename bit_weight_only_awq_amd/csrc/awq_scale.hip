@@ -297,7 +297,7 @@ __device__ __forceinline__ void interleave_step() {
 // against 512 multiply-adds on the matrix cores; 8 waves of 128 x 64 (4 x 2
 // v_mfma_f32_32x32x16_f16 tiles), two per SIMD, so that one wave's loads,
 // build and LDS waits overlap the other's products (one wave per SIMD with
-// 128 x 128 tiles was 10% slower); 160 KiB of LDS.  Operands through LDS:
+// 128 x 128 tiles was 5-10% slower); 160 KiB of LDS.  Operands through LDS:
 // 16-byte chunk c of row r in slot c ^ ((r >> 1) & 7).  For the build, lane l
 // of wave w takes channels 8 (l % 8) .. + 7 of the step (LDS chunk l % 8) in
 // rows 16 w + l / 8 and 16 w + 8 + l / 8, so each wave load covers whole
