@@ -250,3 +250,32 @@ def test_gemm_deterministic_and_stream():
     a = run_gemm(X[:16], packed, N, K, g, True)
     b = run_gemm(X[:16], packed, N, K, g, True, stream=torch.cuda.Stream())
     assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_gemm_repeat_bit_identical_many_tiles():
+    """Four waves of 256 x 256 tiles over the compute units (2048 x 28672 x
+    1024: 768 tiles and a half-width tail launch), so that most workgroups
+    start on a compute unit another one has just left: four calls give the
+    same bits in every output, and the oracle checks whole rows at the end of
+    a tile's last X load (rows 56-63 of the tile) and elsewhere.  (A build
+    whose register spill landed between that load and its barrier varied in
+    exactly those rows.)"""
+    awq = G.lib()
+    M, N, K, g = 2048, 28672, 1024, 128
+    W = workloads.weight(N, K, cfg=4, layer=7)
+    X = workloads.activations(M, K, cfg=4, layer=7)
+    w = G.dev_f16(W)
+    qw, sc, qz = awq.awq_pack(w, g, True)
+    del w
+    x = G.dev_f16(X)
+    y0 = awq.awq_gemm(x, qw, sc, qz, N, K, g, True)
+    for _ in range(3):
+        y = awq.awq_gemm(x, qw, sc, qz, N, K, g, True)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
+    rows = np.array([56, 63, 256 + 57, 1024 + 60, 2047 - 192, 1500])
+    yh = G.host_f16(y0)[rows]
+    # the oracle on all columns of these rows, from its own packing of W
+    packed = O.pack(W, g, True)
+    y_ref, d = O.matmul_ref(X[rows], O.dequant_packed(*packed, N, K, g, True))
+    G.assert_within_tolerance(yh, y_ref, d, "repeat many tiles")
