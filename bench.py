@@ -73,6 +73,7 @@ def parse():
     ap.add_argument("--summarize", nargs="+", metavar="DB",
                     help="print a per-kernel summary of rocprofv3 result databases and exit")
     ap.add_argument("--kernel-filter", default=None, help="with --summarize: only kernels whose name contains this")
+    ap.add_argument("--pool", action="store_true", help="with --summarize: one summary over all the databases")
     ap.add_argument("--kernel-hash", nargs="+", metavar="SRC",
                     help="print the hash of these kernel sources and the compile flags (for counter summaries)")
     ap.add_argument("--last", type=int, default=None,
@@ -793,28 +794,24 @@ def cpu_baseline(layers, g, zp, timed=None, min_seconds=8.0, max_passes=40, pack
     return out, check
 
 
-def summarize(db_paths, name_filter=None, last=None):
+def summarize(db_paths, name_filter=None, last=None, pool=False):
     """Per-kernel summary of rocprofv3 SQLite databases (kernel-trace and/or
     --pmc runs): dispatch count, duration statistics (mean, median, minimum,
     10th and 90th percentiles) and, when present, the per-dispatch average of
-    each collected counter.  Prints text."""
+    each collected counter.  With ``pool`` the selected dispatches of all the
+    databases (each one's last ``last``) are summarized as one set.  Prints
+    text."""
     import sqlite3
     import statistics
 
-    lines = []
-    for db in db_paths:
+    def select(db):
         con = sqlite3.connect(db)
-        lines.append(f"# {db}")
         rows = list(con.execute("select dispatch_id, name, duration, grid_x, workgroup_x from kernels "
                                 "order by dispatch_id"))
         if name_filter:
             rows = [r for r in rows if name_filter in r[1]]
         if last:
             rows = rows[-last:]  # e.g. only the timed replays at the end of the run
-            lines.append(f"# the last {len(rows)} matching dispatches")
-        by = {}
-        for kid, name, dur, grid, wg in rows:
-            by.setdefault((name, grid, wg), []).append((kid, dur))
         pmc = {}
         try:
             for kid, cname, val in con.execute("select dispatch_id, counter_name, counter_value from pmc_events"):
@@ -822,6 +819,26 @@ def summarize(db_paths, name_filter=None, last=None):
                 pmc[kid][cname] += val
         except sqlite3.Error:
             pass
+        return rows, pmc
+
+    groups = []
+    if pool:
+        rows, pmc = [], {}
+        for i, db in enumerate(db_paths):
+            r, p = select(db)
+            rows += [((i, kid), name, dur, grid, wg) for kid, name, dur, grid, wg in r]
+            pmc.update({(i, kid): v for kid, v in p.items()})
+        groups.append(("# pooled: " + " ".join(db_paths), rows, pmc))
+    else:
+        groups = [(f"# {db}",) + select(db) for db in db_paths]
+    lines = []
+    for head, rows, pmc in groups:
+        lines.append(head)
+        if last:
+            lines.append(f"# the last {last} matching dispatches of each run: {len(rows)}")
+        by = {}
+        for kid, name, dur, grid, wg in rows:
+            by.setdefault((name, grid, wg), []).append((kid, dur))
         for (name, grid, wg), ds in sorted(by.items(), key=lambda kv: -sum(d for _, d in kv[1])):
             durs = sorted(d for _, d in ds)
             p10 = durs[int(0.1 * (len(durs) - 1))]
@@ -842,7 +859,7 @@ def summarize(db_paths, name_filter=None, last=None):
 def main():
     args = parse()
     if args.summarize:
-        print(summarize(args.summarize, args.kernel_filter, args.last))
+        print(summarize(args.summarize, args.kernel_filter, args.last, args.pool))
         return 0
     if args.kernel_hash:
         print(kernel_hash(args.kernel_hash))

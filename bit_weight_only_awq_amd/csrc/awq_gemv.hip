@@ -22,7 +22,9 @@
 //     multiplies the fp32 chunk sum once, so no decoded weight is rounded;
 //   * row sums are reduced across the wave in registers (lane-swap exchanges
 //     that leave one row per 16- or 8-lane group, then DPP lane rotations),
-//     then across waves through LDS in a fixed order: bit-reproducible results.
+//     then across waves through LDS in a fixed order: bit-reproducible results;
+//   * quad workgroups are laid out in one contiguous band of rows per XCD, so
+//     each line of y is written from one XCD's L2.
 #include "awq_device.hpp"
 #include "awq_launch.hpp"
 
@@ -44,7 +46,12 @@ __global__ __launch_bounds__(NW * QPW * 64) void gemv_kernel(const u32x4* __rest
   const int lane = threadIdx.x & 63, wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int part = QPW == 1 ? 0 : wave_all / NW, wave = wave_all - part * NW;  // row group of the wave, wave within it
   const int t = wave * 64 + lane;                               // thread within the row group
-  const int n0 = (blockIdx.x * QPW + part) * ROWS;
+  // Quads: each XCD takes one contiguous band of row groups, so the 8 workgroups that write one
+  // 128-byte line of y sit on one XCD (the hardware deals workgroups to XCDs round robin, which
+  // would spread every line over all 8 L2s): the 7B decode step 2.0% faster.  Octets keep the
+  // dealt order (with the bands: 3-5% slower on the 70B MLP and fused gate_up layers).
+  const int bid = ROWS == 4 ? xcd_contiguous_tile(blockIdx.x, gridDim.x) : (int)blockIdx.x;
+  const int n0 = (bid * QPW + part) * ROWS;
   const int chunks = K >> 5;                // 32-channel chunks per row
   const int G = K >> gshift;
   const size_t row_u4 = (size_t)(K >> 5);   // a row is K/2 bytes = K/32 128-bit words
@@ -125,7 +132,7 @@ __global__ __launch_bounds__(NW * QPW * 64) void gemv_kernel(const u32x4* __rest
     float sum = red[p][0][r];
 #pragma unroll
     for (int w = 1; w < NW; ++w) sum += red[p][w][r];
-    y[(blockIdx.x * QPW + p) * ROWS + r] = (_Float16)sum;
+    y[(bid * QPW + p) * ROWS + r] = (_Float16)sum;
   }
 }
 
