@@ -151,7 +151,7 @@ int gemv_waves(int K) {
   return chunks > 8 * 64 ? 12 : (chunks + 63) / 64;
 }
 
-bool gemv_uses_octets(int N, int K) { return (long)(N / 8) * gemv_waves(K) >= 16 * 256; }
+bool gemv_uses_octets(int N, int K) { return (long)(N / 8) * gemv_waves(K) >= 32 * 256; }
 
 // Quads go two per workgroup while that fits 1024 threads (N is a multiple
 // of 8, so the quads always pair up); octets and 12-wave quads one.
@@ -193,9 +193,9 @@ hipError_t launch_zp(const void* x, const uint32_t* qweight, const void* scales,
   _Float16* yv = static_cast<_Float16*>(y);
   const int gs = log2_group(group_size);
   // row octets halve the activation loads per weight byte, but take half as
-  // many workgroups: they pay once the octets alone give ~16 waves per compute
-  // unit (the 70B MLP layers: 9% faster), quads stay faster below (the 7B
-  // layers: 2-15%)
+  // many workgroups: they pay once the octets alone give ~32 waves per compute
+  // unit (the 70B MLP layers, 48-56: 10-12% faster), quads stay faster below
+  // (the 7B layers: 2-15%; the fused 4096 -> 22016 gate_up layer at 21.5: 7%)
   if (gemv_uses_octets(N, K))
     return launch_rows<ZP, 8>(xv, wv, sc, qzeros, yv, N, K, gs, nw, stream);
   return launch_rows<ZP, 4>(xv, wv, sc, qzeros, yv, N, K, gs, nw, stream);

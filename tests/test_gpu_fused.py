@@ -50,3 +50,30 @@ def test_fused_pack_and_layers_match_separate(shapes, K, g, zp):
         y_ref, d = O.matmul_ref(X[rows], wdq)
         G.assert_within_tolerance(yf[rows], y_ref, d, f"fused M={M}")
         G.assert_within_tolerance(ys[rows], y_ref, d, f"separate M={M}")
+
+
+@pytest.mark.parametrize("zp", [True, False])
+def test_fused_octets_match_separate_quads(zp):
+    """A fused layer wide enough for the GEMV's row octets (4096 -> 2 x 16384:
+    4096 octets x 2 waves) against its two parts, which run on row quads: the
+    octet and quad reductions add every row in the same order, so the outputs
+    are bit-identical; sampled octets are checked against the oracle."""
+    awq = G.lib()
+    K, g, shapes = 4096, 128, (16384, 16384)
+    Ws = _parts(shapes, K, cfg=7)
+    dev = [G.dev_f16(W) for W in Ws]
+    fused = awq.pack_fused(dev, g, zp)
+    sep = [awq.pack(w, g, zp) for w in dev]
+    X = workloads.activations(1, K, cfg=7, layer=1)
+    x = G.dev_f16(X)
+    yf = G.host_f16(awq.linear(x, fused))
+    ys = np.concatenate([G.host_f16(awq.linear(x, p)) for p in sep], axis=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(yf.view(np.uint16), ys.view(np.uint16))
+    N = sum(shapes)
+    octets = np.sort(np.random.default_rng(7).choice(N // 8, size=16, replace=False))
+    rows = (octets[:, None] * 8 + np.arange(8)[None, :]).reshape(-1)
+    W = np.concatenate(Ws)[rows]
+    wdq = O.dequant_packed(*O.pack(W, g, zp), len(rows), K, g, zp)
+    y_ref, d = O.matmul_ref(X, wdq)
+    G.assert_within_tolerance(yf[:, rows], y_ref, d, f"fused octets zp={zp}")
